@@ -1,0 +1,269 @@
+"""Sparse-MLA decode throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--cpu-seconds 15] [--no-cpu-baseline]
+
+A step is one pass of the decode hot path over one batch of seeded synthetic input:
+slot resolution (logical top-k -> physical slots, page size 1 table), stage 1 (split
+gather + MFMA scores + online softmax + MFMA P*V) and stage 2 (LSE merge). The headline
+workload is the bf16 batch of 32 requests x 64 heads, latent 512 + rope 64, contexts
+U[8K, 32K] in a 2^20-slot pool of 64-slot pages, top-k 2048. The inputs are resident in
+HBM when a timed step starts: before every timed step a 1 GiB buffer is overwritten so
+that neither the L2 nor the 256 MB Infinity Cache holds the cache rows.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA decode queries/s + achieved HBM GB/s (% of peak) at top-k 2048"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(c, kv_dtype: str) -> dict:
+    """Bytes the method must move for one decode step of case `c` (every row, q element,
+    index and output read or written once). Split partials and repeated reads are not
+    counted: they are the implementation's overhead."""
+    T, H = c.q.shape[0], c.q.shape[1]
+    n_rows = int((c.idx >= 0).sum()) if len(c.dense_tokens) == 0 else None
+    row_bytes = 1152 if kv_dtype == "bf16" else 644        # fp8: 512 codes + 128 rope + 4 scale
+    kv = n_rows * row_bytes
+    q = T * H * 576 * 2
+    out = T * H * 512 * 2
+    lse = T * H * 4
+    idx = int(c.idx.size) * 4                               # logical indices read by resolve
+    slots = int(c.idx.size) * 4                             # resolved slots read by stage 1
+    pages = 0
+    for t in range(T):
+        row = c.idx[t][c.idx[t] >= 0]
+        pages += len(np.unique(row // c.layout.page_size)) * 4
+    return {"kv": kv, "q": q, "out": out, "lse": lse, "idx": idx, "page_table": pages,
+            "step": kv + q + out + lse + idx + pages,      # resolved slots stay on chip in an ideal fusion
+            "stage1": kv + q + slots}
+
+
+def setup_decode(c, smla, torch):
+    dev = "cuda"
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    lay = c.layout
+    code = {"bf16": smla.SMLA_BF16, "fp8": smla.SMLA_FP8_E4M3}[c.kv_dtype]
+    kv = smla.KvCache.empty(code, lay.num_slots, device=dev)
+    smap = smla.smla_resolve_slots(t(c.rows.pos[:, None]), None, t(c.rows.req), t(lay.page_table), t(lay.ctx),
+                                   lay.page_size)[:, 0].contiguous()
+    vals = c.rows.values
+    src = t(vals.view(np.int16)).view(torch.bfloat16) if vals.dtype == np.uint16 else t(vals)
+    smla.smla_kv_write(src, smap, kv)
+    T, H = c.q.shape[0], c.q.shape[1]
+    st = {
+        "q": t(c.q.view(np.int16)).view(torch.bfloat16), "kv": kv, "idx": t(c.idx), "valid": t(c.valid),
+        "req": t(c.tok_req), "pt": t(lay.page_table), "ctx": t(lay.ctx),
+        "slots": torch.empty(c.idx.shape, dtype=torch.int32, device=dev),
+        "out": torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev),
+        "lse": torch.empty((T, H), dtype=torch.float32, device=dev),
+    }
+    st["call"] = smla.DecodeCall(st["q"], kv, st["slots"], st["valid"], 1, c.scale, st["out"], st["lse"])
+    torch.cuda.synchronize()
+    return st
+
+
+def time_decode(c, smla, torch, steps, warmup, flush):
+    st = setup_decode(c, smla, torch)
+    lay = c.layout
+    call = st["call"]
+
+    def resolve():
+        smla.smla_resolve_slots(st["idx"], st["valid"], st["req"], st["pt"], st["ctx"], lay.page_size, slots=st["slots"])
+
+    def step():
+        resolve()
+        call()
+
+    for _ in range(warmup):
+        flush.zero_()
+        step()
+    torch.cuda.synchronize()
+
+    # cold steps: the flush runs between steps, outside the events
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(steps):
+        flush.zero_()
+        e = ev[k]
+        e[0].record()
+        resolve()
+        e[1].record()
+        call.stage1()
+        e[2].record()
+        call.stage2()
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    res_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    s1_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    s2_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    # warm steps: back to back, no flush
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / steps
+
+    # the same step captured in a HIP graph and replayed (warm)
+    graph_ms = None
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / steps
+    except Exception as ex:  # graph capture is a report-only extra
+        log(f"graph capture skipped: {ex}")
+    return {"step_ms": step_ms, "resolve_ms": res_ms, "stage1_ms": s1_ms, "stage2_ms": s2_ms,
+            "warm_ms": warm_ms, "graph_ms": graph_ms, "wall_s": wall, "splits": call.splits}
+
+
+def cpu_baseline(c, seconds: float) -> dict:
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    lay = c.layout
+    pool = oracle.Pool(lay.num_slots, c.kv_dtype)
+    osl = oracle.resolve_slots(c.rows.pos[:, None], None, c.rows.req, lay.page_table, lay.ctx, lay.page_size)[:, 0]
+    oracle.kv_write(pool, c.rows.values, "bf16" if c.rows.values.dtype == np.uint16 else "f32", osl)
+    T = c.q.shape[0]
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        t = done % T
+        sl = oracle.resolve_slots(c.idx[t:t + 1], c.valid[t:t + 1], c.tok_req[t:t + 1], lay.page_table, lay.ctx,
+                                  lay.page_size)
+        oracle.sparse_decode(c.q[t:t + 1], c.q_dtype, pool, sl, c.valid[t:t + 1], 1, c.scale)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} decode queries of the same workload (token t mod {T}, resolve + fp64 attention), "
+                      f"{el:.1f} s wall on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (decode shards by request with no "
+              "exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    import sparse_mla_attention_resolve_amd as smla
+
+    if not os.path.exists(smla.LIB_PATH):
+        raise SystemExit("libsmla.so is not built: run python -m sparse_mla_attention_resolve_amd.build")
+    torch.cuda.set_device(0)
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
+
+    log("generating the bf16 decode workload (batch 32, top-k 2048)")
+    c2 = wl.config2()
+    ab = algorithmic_bytes(c2, "bf16")
+    log("timing bf16 decode")
+    r = time_decode(c2, smla, torch, args.steps, args.warmup, flush)
+    T = c2.q.shape[0]
+    step_ms = float(r["step_ms"].mean())
+    s1_ms = float(r["stage1_ms"].mean())
+    value = T / (step_ms / 1e3)
+    s1_gbs = ab["stage1"] / (s1_ms / 1e3) / 1e9
+    step_gbs = ab["step"] / (step_ms / 1e3) / 1e9
+    log(f"step {step_ms*1e3:.1f} us (resolve {r['resolve_ms'].mean()*1e3:.1f}, stage1 {s1_ms*1e3:.1f}, "
+        f"stage2 {r['stage2_ms'].mean()*1e3:.1f}); warm {r['warm_ms']*1e3:.1f} us; graph "
+        f"{(r['graph_ms'] or 0)*1e3:.1f} us; stage1 {s1_gbs:.0f} GB/s")
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "sparse MLA decode, bf16 q and KV, batch 32, 64 heads, latent 512 + rope 64, "
+                               "contexts U[8K,32K], 2^20-slot pool of 64-slot pages, top-k 2048, step = resolve + "
+                               "split decode + LSE merge, inputs HBM-resident (1 GiB overwritten before each step)",
+                   "batch": T, "heads": 64, "topk": 2048, "splits": r["splits"], "parallelism": "none (1 GPU)"},
+        "hbm_gbs_step": step_gbs, "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_step": ab["step"],
+        "timing_us": {"step_median": float(np.median(r["step_ms"])) * 1e3,
+                      "step_p10": float(np.percentile(r["step_ms"], 10)) * 1e3,
+                      "step_p90": float(np.percentile(r["step_ms"], 90)) * 1e3,
+                      "resolve": float(r["resolve_ms"].mean()) * 1e3, "stage1": s1_ms * 1e3,
+                      "stage2": float(r["stage2_ms"].mean()) * 1e3,
+                      "warm_step": r["warm_ms"] * 1e3,
+                      "graph_replay_step": None if r["graph_ms"] is None else r["graph_ms"] * 1e3},
+        "roofline": {"bound": "hbm", "kernel": "decode_stage1_mfma<bf16>", "achieved": s1_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": s1_gbs / HBM_PEAK_GBS,
+                     "algorithmic_bytes_per_launch": ab["stage1"], "avg_launch_us": s1_ms * 1e3,
+                     "traffic": None},
+    }
+
+    if not args.no_fp8:
+        log("generating the fp8-KV decode workload (batch 64)")
+        c5 = wl.config5()
+        ab5 = algorithmic_bytes(c5, "fp8")
+        log("timing fp8-KV decode")
+        r5 = time_decode(c5, smla, torch, args.steps, args.warmup, flush)
+        ms5 = float(r5["step_ms"].mean())
+        s15 = float(r5["stage1_ms"].mean())
+        line["fp8_kv_decode"] = {
+            "workload": "batch 64, 64 heads, fp8 e4m3 latent + bf16 rope + fp32 scale per row, context 64K, top-k 2048",
+            "queries_per_s": c5.q.shape[0] / (ms5 / 1e3), "ms_per_step": ms5,
+            "hbm_gbs_step": ab5["step"] / (ms5 / 1e3) / 1e9,
+            "stage1_gbs": ab5["stage1"] / (s15 / 1e3) / 1e9, "stage1_us": s15 * 1e3,
+            "stage1_frac": ab5["stage1"] / (s15 / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "warm_step_us": r5["warm_ms"] * 1e3, "splits": r5["splits"]}
+        log(f"fp8: step {ms5*1e3:.1f} us, stage1 {s15*1e3:.1f} us")
+
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline(c2, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,45 @@
+// Host-side declarations shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/smla.h"
+
+namespace smla {
+
+// Rows of one stage-1 chunk (the unit of gather, MFMA and online-softmax update).
+constexpr int kChunk = 32;
+
+// Decode plan: everything the launches need, computed from scalar arguments only.
+struct DecodePlan {
+  int32_t T, H, S;           // tokens, heads, splits
+  int32_t rows_per_split;    // multiple of kChunk
+  int32_t max_len;           // table_width * page_size
+  size_t part_o_bytes;       // [T, S, H, 512] fp32
+  size_t part_lse_bytes;     // [T, S, H] fp32
+  size_t ws_bytes;
+};
+
+hipError_t launch_resolve(const int32_t* idx, int64_t idx_stride, const int32_t* valid,
+                          const int32_t* tok_req, int32_t R, const int32_t* page_table,
+                          int64_t pt_stride, int32_t pt_width, const int32_t* seq_lens,
+                          int32_t page_size, int32_t T, int32_t W, int32_t* slots,
+                          int64_t slots_stride, hipStream_t stream);
+
+hipError_t launch_kv_write(const void* src, int32_t src_dtype, int64_t src_stride,
+                           const int32_t* slot_mapping, int32_t T, const smla_kv& dst,
+                           hipStream_t stream);
+
+// stages: bit 0 = stage 1, bit 1 = stage 2
+hipError_t launch_decode(const smla_decode_args& a, const DecodePlan& plan, void* ws,
+                         hipStream_t stream, int stages = 3);
+
+hipError_t launch_union(const int32_t* slots, int64_t slots_stride, const int32_t* valid,
+                        int32_t Q, int32_t W, int32_t G, int64_t num_slots, uint32_t* enc,
+                        int64_t enc_stride, int32_t* lens, hipStream_t stream);
+
+hipError_t launch_prefill(const smla_prefill_args& a, hipStream_t stream);
+
+}  // namespace smla

@@ -1,0 +1,188 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point, its struct
+layouts match the binding's, and argument checks that precede any HIP call return the
+documented statuses (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+smla_pkg = pytest.importorskip("sparse_mla_attention_resolve_amd")
+from sparse_mla_attention_resolve_amd import smla as S  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUP, RANGE, WS = 0, 1, 2, 3, 4, 5, 6
+FAKE = 1 << 20          # a non-null, well-aligned address that no check dereferences
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(smla_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert len(names) >= 13
+    lib = S.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(S.EXPORTS) == set(names)
+
+
+def test_struct_sizes_and_version():
+    lib = S.lib()
+    assert lib.smla_abi_version() == 1
+    assert lib.smla_sizeof_kv() == ctypes.sizeof(S.smla_kv) == 80
+    assert lib.smla_sizeof_decode_args() == ctypes.sizeof(S.smla_decode_args)
+    assert lib.smla_sizeof_prefill_args() == ctypes.sizeof(S.smla_prefill_args)
+    assert lib.smla_status_str(6) == b"SMLA_ERR_WORKSPACE"
+
+
+def _resolve(**kw):
+    a = dict(idx=FAKE, idx_stride=8, valid=None, tok_req=FAKE, R=1, page_table=FAKE, pt_stride=4, pt_width=4,
+             seq_lens=FAKE, page_size=64, T=2, W=8, slots=FAKE, slots_stride=8)
+    a.update(kw)
+    return S.lib().smla_resolve_slots(*[a[k] for k in ("idx", "idx_stride", "valid", "tok_req", "R", "page_table",
+                                                         "pt_stride", "pt_width", "seq_lens", "page_size", "T", "W",
+                                                         "slots", "slots_stride")], None)
+
+
+def test_resolve_checks():
+    assert _resolve(T=0) == OK
+    assert _resolve(T=-1) == SHAPE
+    assert _resolve(idx=None) == NULL
+    assert _resolve(page_size=48) == UNSUP
+    assert _resolve(page_size=1 << 21) == UNSUP
+    assert _resolve(idx_stride=7) == SHAPE
+    assert _resolve(R=0) == SHAPE
+    assert _resolve(idx=FAKE + 2) == ALIGN
+    assert b"page_size" in S.lib().smla_last_error() or _resolve(page_size=3) == UNSUP
+
+
+def _decode_args(**kw):
+    a = S.smla_decode_args()
+    a.T, a.H, a.q_dtype, a.page_size = 4, 64, S.SMLA_BF16, 1
+    a.q, a.q_tok_stride, a.q_head_stride = FAKE, 64 * 576, 576
+    a.kv.dtype, a.kv.num_slots, a.kv.rows, a.kv.row_stride = S.SMLA_BF16, 1000, FAKE, 1152
+    a.table, a.table_stride, a.table_width = FAKE, 2048, 2048
+    a.lens, a.scale = FAKE, 0.0625
+    a.out, a.out_tok_stride, a.out_head_stride = FAKE, 64 * 512, 512
+    a.lse, a.lse_tok_stride = FAKE, 64
+    for k, v in kw.items():
+        if k.startswith("kv_"):
+            setattr(a.kv, k[3:], v)
+        else:
+            setattr(a, k, v)
+    return a
+
+
+def _ws(a):
+    n = ctypes.c_size_t(0)
+    st = S.lib().smla_sparse_decode_workspace(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_decode_checks_and_workspace():
+    st, n = _ws(_decode_args())
+    assert st == OK
+    splits = ctypes.c_int32(0)
+    assert S.lib().smla_sparse_decode_splits(ctypes.byref(_decode_args()), ctypes.byref(splits)) == OK
+    s = splits.value
+    assert 1 <= s <= 256
+    assert n >= 4 * s * 64 * 512 * 4 + 4 * s * 64 * 4
+    assert _ws(_decode_args(H=32))[0] == UNSUP
+    assert _ws(_decode_args(q_dtype=S.SMLA_F32))[0] == UNSUP          # fp32 q with a bf16 cache
+    assert _ws(_decode_args(q_dtype=S.SMLA_F32, H=16, kv_dtype=S.SMLA_F32, kv_row_stride=2304))[0] == OK
+    assert _ws(_decode_args(page_size=3))[0] == UNSUP
+    assert _ws(_decode_args(table_stride=100))[0] == SHAPE
+    assert _ws(_decode_args(num_splits=300))[0] == RANGE
+    assert _ws(_decode_args(kv_row_stride=1000))[0] == SHAPE
+    assert _ws(_decode_args(kv_row_stride=1160))[0] == ALIGN
+    assert _ws(_decode_args(kv_dtype=7))[0] == UNSUP
+    assert _ws(_decode_args(scale=float("nan")))[0] == SHAPE
+    assert _ws(_decode_args(table_width=1 << 20, table_stride=1 << 20, page_size=1 << 11))[0] == RANGE
+    # the workspace check precedes any launch
+    a = _decode_args()
+    assert S.lib().smla_sparse_decode(ctypes.byref(a), FAKE, 16, None) == WS
+    assert S.lib().smla_sparse_decode(ctypes.byref(a), None, 1 << 40, None) == WS
+    a = _decode_args(q=None)
+    assert S.lib().smla_sparse_decode(ctypes.byref(a), FAKE, 1 << 40, None) == NULL
+    a = _decode_args(q=FAKE + 8)
+    assert S.lib().smla_sparse_decode(ctypes.byref(a), FAKE, 1 << 40, None) == ALIGN
+    a = _decode_args(T=0)
+    assert S.lib().smla_sparse_decode(ctypes.byref(a), None, 0, None) == OK
+
+
+def test_decode_split_plan_follows_shapes():
+    lib = S.lib()
+
+    def splits(**kw):
+        v = ctypes.c_int32(0)
+        assert lib.smla_sparse_decode_splits(ctypes.byref(_decode_args(**kw)), ctypes.byref(v)) == OK
+        return v.value
+    assert splits(T=32) * 32 >= 256
+    assert splits(T=1, table_width=256, table_stride=256) <= 8
+    assert splits(num_splits=5) == 5
+    assert splits(num_splits=200, table_width=64, table_stride=64) == 2      # at most one split per 32 rows
+
+
+def test_union_checks():
+    lib = S.lib()
+
+    def u(**kw):
+        a = dict(slots=FAKE, stride=2048, valid=None, Q=4, W=2048, G=2, ns=1000, enc=FAKE, enc_stride=4096, lens=FAKE)
+        a.update(kw)
+        return lib.smla_build_group_union(a["slots"], a["stride"], a["valid"], a["Q"], a["W"], a["G"], a["ns"],
+                                          a["enc"], a["enc_stride"], a["lens"], None)
+    assert u(G=3) == UNSUP
+    assert u(G=16) == UNSUP
+    assert u(G=8, W=4096, stride=4096, enc_stride=32768) == RANGE
+    assert u(ns=(1 << 24) - 1) == RANGE
+    assert u(ns=0) == RANGE
+    assert u(Q=0) == OK
+    assert u(enc_stride=4095) == SHAPE
+    assert u(enc=None) == NULL
+
+
+def test_prefill_checks():
+    lib = S.lib()
+
+    def p(**kw):
+        a = S.smla_prefill_args()
+        a.Q, a.H, a.G, a.enc_width = 8, 64, 2, 4096
+        a.q, a.q_tok_stride, a.q_head_stride = FAKE, 64 * 576, 576
+        a.kv.dtype, a.kv.num_slots, a.kv.rows, a.kv.row_stride = S.SMLA_BF16, 1000, FAKE, 1152
+        a.enc, a.enc_stride, a.lens, a.scale = FAKE, 4096, FAKE, 0.0625
+        a.out, a.out_tok_stride, a.out_head_stride = FAKE, 64 * 512, 512
+        for k, v in kw.items():
+            if k.startswith("kv_"):
+                setattr(a.kv, k[3:], v)
+            else:
+                setattr(a, k, v)
+        return lib.smla_grouped_prefill(ctypes.byref(a), None)
+    assert p(H=32) == UNSUP                          # G * H != 128
+    assert p(G=3, H=43) == UNSUP
+    assert p(kv_dtype=S.SMLA_FP8_E4M3, kv_lat8=FAKE, kv_rope16=FAKE, kv_scale=FAKE, kv_lat8_stride=656,
+             kv_rope16_stride=656, kv_scale_stride=656) == UNSUP
+    assert p(enc_width=5000) == SHAPE
+    assert p(q=None) == NULL
+    assert p(Q=0) == OK
+
+
+def test_kv_write_checks():
+    lib = S.lib()
+    d = S.smla_kv()
+    d.dtype, d.num_slots, d.rows, d.row_stride = S.SMLA_BF16, 100, FAKE, 1152
+    assert lib.smla_kv_write(FAKE, 5, 576, FAKE, 3, ctypes.byref(d), None) == UNSUP
+    assert lib.smla_kv_write(FAKE, S.SMLA_F32, 500, FAKE, 3, ctypes.byref(d), None) == SHAPE
+    assert lib.smla_kv_write(FAKE + 4, S.SMLA_F32, 576, FAKE, 3, ctypes.byref(d), None) == ALIGN
+    assert lib.smla_kv_write(None, S.SMLA_F32, 576, FAKE, 3, ctypes.byref(d), None) == NULL
+    assert lib.smla_kv_write(FAKE, S.SMLA_F32, 576, FAKE, 0, ctypes.byref(d), None) == OK
+    d.dtype = S.SMLA_FP8_E4M3
+    d.lat8, d.lat8_stride, d.rope16, d.rope16_stride, d.scale, d.scale_stride = FAKE, 656, FAKE + 512, 656, FAKE + 640, 656
+    assert lib.smla_kv_write(FAKE, S.SMLA_F32, 576, FAKE, 0, ctypes.byref(d), None) == OK
+    d.rope16 = FAKE + 514
+    assert lib.smla_kv_write(FAKE, S.SMLA_F32, 576, FAKE, 0, ctypes.byref(d), None) == ALIGN

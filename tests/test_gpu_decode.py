@@ -1,0 +1,201 @@
+"""Split decode on the GPU against the fp64 oracle (tolerances: bf16 |d| <= 2e-2 + 1e-2|ref|,
+LSE |d| <= 1e-3, fp8 cache |d| <= 6e-2 + 1e-2|ref|; the fp32 path additionally 1e-4; every
+bf16 case also a norm-relative error <= 1e-2). Unused pool slots hold NaN, so a wrong gather
+cannot pass."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from . import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+smla = pytest.importorskip("sparse_mla_attention_resolve_amd")
+
+BF16_ATOL, BF16_RTOL, LSE_ATOL, FP8_ATOL = 2e-2, 1e-2, 1e-3, 6e-2
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _check(out, lse, o_ref, l_ref, atol, rtol, what, f32=False):
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    gc.assert_close(out, o_ref, atol, rtol, what + " out")
+    gc.assert_lse(lse, l_ref, LSE_ATOL, what + " lse")
+    if f32:
+        gc.assert_close(out, o_ref, 1e-4, 0, what + " out (fp32 path)")
+        gc.assert_lse(lse, l_ref, 1e-4, what + " lse (fp32 path)")
+    else:
+        assert gc.rel_l2(out, o_ref) <= 1e-2, (what, gc.rel_l2(out, o_ref))
+
+
+def _random_case(seed, T, W, lens, num_slots, P=1, kv_dtype="bf16"):
+    """Small decode case: T tokens, a NaN pool with rows only where tables point."""
+    rng = np.random.default_rng(seed)
+    H = 64
+    q = wl.f32_to_bf16_bits(rng.standard_normal((T, H, 576)).astype(np.float32) * 0.5)
+    if P == 1:
+        table = np.full((T, W), -1, np.int32)
+        for t in range(T):
+            n = min(lens[t], W)
+            table[t, :n] = rng.choice(num_slots, size=n, replace=False)
+            if n > 4:
+                table[t, rng.integers(0, n)] = -1      # a hole inside the valid prefix
+        live = np.unique(table[table >= 0])
+    else:
+        pages = num_slots // P
+        table = np.stack([rng.permutation(pages)[:W] for _ in range(T)]).astype(np.int32)
+        live = np.unique(np.concatenate([table[t, :(-(-lens[t] // P))] for t in range(T)] + [np.zeros(0, np.int32)]))
+        live = (live[:, None] * P + np.arange(P)[None, :]).reshape(-1)
+    vals = rng.standard_normal((len(live), 576)).astype(np.float32) * (1.0 if kv_dtype == "fp8" else 0.5)
+    return q, table, np.asarray(lens, np.int32), live.astype(np.int32), vals
+
+
+def _pools(live, vals, num_slots, kv_dtype):
+    kv = smla.KvCache.empty(gc.KV_CODE[kv_dtype], num_slots)
+    src = vals if kv_dtype != "bf16" else wl.f32_to_bf16_bits(vals)
+    st, sd = gc.src_tensor(src)
+    smla.smla_kv_write(st, _t(live), kv)
+    pool = oracle.Pool(num_slots, kv_dtype)
+    oracle.kv_write(pool, src, sd, live)
+    return kv, pool
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("splits", [0, 1, 3, 8])
+def test_decode_small_sparse(kv_dtype, splits):
+    lens = [0, 1, 17, 31, 32, 33, 300, 2048]
+    q, table, lens, live, vals = _random_case(11, len(lens), 2048, lens, 50000, kv_dtype=kv_dtype)
+    kv, pool = _pools(live, vals, 50000, kv_dtype)
+    out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(table), _t(lens), 1, 1 / 16, num_splits=splits)
+    o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, table, lens, 1, 1 / 16)
+    atol = FP8_ATOL if kv_dtype == "fp8" else BF16_ATOL
+    _check(out, lse, o_ref, l_ref, atol, BF16_RTOL, f"small {kv_dtype} splits={splits}")
+    empty = lens == 0
+    assert torch.all(out[torch.from_numpy(empty)] == 0)
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_decode_small_dense_paged(P):
+    lens = [1, 63, 64, 65, 1000, 4000]
+    q, table, lens, live, vals = _random_case(12 + P, len(lens), 4096 // P, lens, 8192, P=P)
+    kv, pool = _pools(live, vals, 8192, "bf16")
+    out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(table), _t(lens), P, 0.07)
+    o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, table, lens, P, 0.07)
+    _check(out, lse, o_ref, l_ref, BF16_ATOL, BF16_RTOL, f"dense P={P}")
+
+
+def test_virtual_table_equals_page_table():
+    """The same rows in the same order through resolved slots (page size 1) and through the
+    page table (page size 64) give bitwise equal outputs."""
+    P, T = 64, 4
+    lens = np.array([100, 700, 2048, 64], np.int32)
+    q, table, lens, live, vals = _random_case(13, T, 2048 // P, lens, 8192, P=P)
+    kv, _ = _pools(live, vals, 8192, "bf16")
+    qt = gc.q_tensor(q, "bf16")
+    a = smla.smla_sparse_decode(qt, kv, _t(table), _t(lens), P, 1 / 16, num_splits=4)
+    pos = np.tile(np.arange(2048, dtype=np.int32), (T, 1))
+    slots = smla.smla_resolve_slots(_t(pos), _t(lens), _t(np.arange(T, dtype=np.int32)), _t(table), _t(lens), P)
+    b = smla.smla_sparse_decode(qt, kv, slots, _t(lens), 1, 1 / 16, num_splits=4)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_deterministic():
+    lens = [2048, 1500, 7]
+    q, table, lens, live, vals = _random_case(14, 3, 2048, lens, 40000)
+    kv, _ = _pools(live, vals, 40000, "bf16")
+    qt = gc.q_tensor(q, "bf16")
+    a = smla.smla_sparse_decode(qt, kv, _t(table), _t(lens), 1, 1 / 16)
+    b = smla.smla_sparse_decode(qt, kv, _t(table), _t(lens), 1, 1 / 16)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def _run_config(c):
+    lay = c.layout
+    kv, smap = gc.gpu_pool(smla, lay, c.rows, c.kv_dtype)
+    pool, osl = gc.oracle_pool(lay, c.rows, c.kv_dtype)
+    assert np.array_equal(smap.cpu().numpy(), osl)
+    qt = gc.q_tensor(c.q, c.q_dtype)
+    slots = smla.smla_resolve_slots(_t(c.idx), _t(c.valid), _t(c.tok_req), _t(lay.page_table), _t(lay.ctx),
+                                    lay.page_size)
+    oslots = oracle.resolve_slots(c.idx, c.valid, c.tok_req, lay.page_table, lay.ctx, lay.page_size)
+    assert np.array_equal(slots.cpu().numpy(), oslots)
+    sparse = np.setdiff1d(np.arange(len(c.idx)), c.dense_tokens)
+    out, lse = smla.smla_sparse_decode(qt, kv, slots, _t(c.valid), 1, c.scale)
+    o_ref, l_ref = oracle.sparse_decode(c.q, c.q_dtype, pool, oslots, c.valid, 1, c.scale, tokens=sparse)
+    results = [(out[torch.from_numpy(sparse).cuda()], lse[torch.from_numpy(sparse).cuda()], o_ref, l_ref, "sparse rows")]
+    if len(c.dense_tokens):
+        d = c.dense_tokens
+        dt = torch.from_numpy(d).cuda()
+        pt_rows = lay.page_table[c.tok_req[d]]
+        ctx = lay.ctx[c.tok_req[d]]
+        out_d, lse_d = smla.smla_sparse_decode(qt[dt], kv, _t(pt_rows), _t(ctx), lay.page_size, c.scale)
+        od, ld = oracle.sparse_decode(c.q[d], c.q_dtype, pool, pt_rows, ctx, lay.page_size, c.scale)
+        results.append((out_d, lse_d, od, ld, "dense rows"))
+    return results
+
+
+def test_config1_tiny_fp32():
+    c = gc.config("config1")
+    for out, lse, o, l, what in _run_config(c):
+        _check(out, lse, o, l, BF16_ATOL, BF16_RTOL, "config1 " + what, f32=True)
+
+
+def test_config2_bf16():
+    c = gc.config("config2")
+    for out, lse, o, l, what in _run_config(c):
+        _check(out, lse, o, l, BF16_ATOL, BF16_RTOL, "config2 " + what)
+
+
+def test_config3_ragged():
+    c = gc.config("config3")
+    res = _run_config(c)
+    assert len(res) == 2
+    for out, lse, o, l, what in res:
+        _check(out, lse, o, l, BF16_ATOL, BF16_RTOL, "config3 " + what)
+
+
+def test_config5_fp8():
+    c = gc.config("config5")
+    for out, lse, o, l, what in _run_config(c):
+        _check(out, lse, o, l, FP8_ATOL, BF16_RTOL, "config5 " + what)
+
+
+def test_decode_graph_replay():
+    """resolve + decode captured in a HIP graph; every replay matches the eager result."""
+    c = wl.config2(T=8)
+    lay = c.layout
+    kv, _ = gc.gpu_pool(smla, lay, c.rows, "bf16")
+    qt = gc.q_tensor(c.q, "bf16")
+    idx, valid, req = _t(c.idx), _t(c.valid), _t(c.tok_req)
+    pt, ctx = _t(lay.page_table), _t(lay.ctx)
+    slots = torch.empty_like(idx)
+    out = torch.empty((8, 64, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((8, 64), dtype=torch.float32, device="cuda")
+    ws = torch.empty(smla.smla_sparse_decode_workspace(qt, kv, idx, valid, 1, c.scale), dtype=torch.uint8, device="cuda")
+
+    def step():
+        smla.smla_resolve_slots(idx, valid, req, pt, ctx, lay.page_size, slots=slots)
+        smla.smla_sparse_decode(qt, kv, slots, valid, 1, c.scale, out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)

@@ -1,0 +1,71 @@
+"""Cache writes on the GPU against the oracle's cache write: stored bits must be equal."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from . import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+smla = pytest.importorskip("sparse_mla_attention_resolve_amd")
+
+
+def _src(rng, n, src_dtype):
+    x = rng.standard_normal((n, 576)).astype(np.float32) * rng.choice([1e-3, 1.0, 40.0], size=(n, 1)).astype(np.float32)
+    x[0, :512] = 0.0                              # zero latent -> scale 0, codes 0
+    x[1, 7] = 3e4                                 # one huge element
+    x[2, :512] = 2.0 ** -20                       # tiny values
+    x[3, 100] = -x[3, :512].__abs__().max() * 3   # negative amax
+    if src_dtype == "bf16":
+        return wl.f32_to_bf16_bits(x)
+    return x
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("src_dtype", ["f32", "bf16"])
+def test_kv_write_bits(kv_dtype, src_dtype):
+    rng = np.random.default_rng(hash((kv_dtype, src_dtype)) % 1000)
+    n, ns = 300, 1000
+    src = _src(rng, n, src_dtype)
+    smap = rng.choice(ns, size=n, replace=False).astype(np.int32)
+    smap[5] = -1
+    smap[6] = ns + 10                             # past the pool: skipped
+    kv = smla.KvCache.empty(gc.KV_CODE[kv_dtype], ns)
+    st, _ = gc.src_tensor(src)
+    smla.smla_kv_write(st, torch.from_numpy(smap).cuda(), kv)
+    pool = oracle.Pool(ns, kv_dtype)
+    keep = (smap >= 0) & (smap < ns)
+    oracle.kv_write(pool, src[keep], src_dtype, smap[keep])
+    written = smap[keep]
+    want = pool.stored(written)
+    stor = kv.storage.cpu()
+    if kv_dtype == "f32":
+        got = stor.numpy()[written]
+        assert np.array_equal(got.view(np.uint32), want["rows"].view(np.uint32))
+    elif kv_dtype == "bf16":
+        got = stor.view(torch.int16).numpy().view(np.uint16)[written]
+        assert np.array_equal(got, want["rows"])
+    else:
+        s = stor.numpy()[written]
+        assert np.array_equal(s[:, :512], want["lat8"])
+        assert np.array_equal(s[:, 512:640].copy().view(np.uint16), want["rope16"])
+        assert np.array_equal(s[:, 640:644].copy().view(np.uint32)[:, 0], want["scale"].view(np.uint32))
+    # every other slot still holds the poison
+    others = np.setdiff1d(np.arange(ns), written)
+    if kv_dtype == "fp8":
+        assert np.all(stor.numpy()[others][:, :512] == 0x7F)
+    else:
+        assert torch.isnan(stor[torch.from_numpy(others)].float()).all()
+
+
+def test_kv_write_fp8_config5_codes():
+    c = wl.config5(T=8)
+    kv, smap = gc.gpu_pool(smla, c.layout, c.rows, "fp8")
+    pool, osl = gc.oracle_pool(c.layout, c.rows, "fp8")
+    assert np.array_equal(smap.cpu().numpy(), osl)
+    s = kv.storage[smap.long()].cpu().numpy()
+    want = pool.stored(osl)
+    assert np.array_equal(s[:, :512], want["lat8"])
+    assert np.array_equal(s[:, 512:640].copy().view(np.uint16), want["rope16"])
+    assert np.array_equal(s[:, 640:644].copy().view(np.float32)[:, 0], want["scale"])

@@ -1,0 +1,74 @@
+"""Grouped prefill on the GPU against the oracle (bf16 tolerances as decode)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from . import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+smla = pytest.importorskip("sparse_mla_attention_resolve_amd")
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _small(seed, Q, H, G, W=256, ns=3000):
+    rng = np.random.default_rng(seed)
+    slots, valid = wl.random_slot_lists(seed, Q, W, ns, overlap=0.7, G=G, pad_frac=0.3)
+    vals = wl.f32_to_bf16_bits(rng.standard_normal((ns, 576)).astype(np.float32) * 0.5)
+    live = np.unique(slots[slots >= 0]).astype(np.int32)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((Q, H, 576)).astype(np.float32) * 0.5)
+    kv = smla.KvCache.empty(smla.SMLA_BF16, ns)
+    smla.smla_kv_write(gc.bits_to_torch_bf16(vals[live]), _t(live), kv)
+    pool = oracle.Pool(ns, "bf16")
+    oracle.kv_write(pool, vals[live], "bf16", live)
+    return q, slots, valid, kv, pool, ns
+
+
+@pytest.mark.parametrize("Q,H,G", [(9, 64, 2), (2, 64, 2), (10, 32, 4), (13, 16, 8)])
+def test_prefill_small(Q, H, G):
+    q, slots, valid, kv, pool, ns = _small(20 + Q + G, Q, H, G)
+    enc, lens = smla.smla_build_group_union(_t(slots), _t(valid), G, ns)
+    out, lse = smla.smla_grouped_prefill(gc.q_tensor(q, "bf16"), kv, enc, lens, G, 0.0625)
+    enc_o, lens_o = oracle.group_union(slots, valid, G, ns)
+    o_ref, l_ref = oracle.grouped_prefill(q, pool, enc_o, lens_o, G, 0.0625)
+    # each query also equals decode over its own list
+    od, ld = oracle.sparse_decode(q, "bf16", pool, slots, valid, 1, 0.0625)
+    assert np.allclose(o_ref, od, atol=1e-12) and np.allclose(np.nan_to_num(l_ref, neginf=-1e300),
+                                                              np.nan_to_num(ld, neginf=-1e300), atol=1e-12)
+    o = out.float().cpu().numpy()
+    gc.assert_close(o, o_ref, 2e-2, 1e-2, f"prefill Q={Q} G={G}")
+    gc.assert_lse(lse.cpu().numpy(), l_ref, 1e-3, f"prefill Q={Q} G={G} lse")
+    assert gc.rel_l2(o, o_ref) <= 1e-2
+    # planted in the oracle, on the CPU: the second member's bit cleared, or the tail
+    # query dropped, gives an expectation the GPU result must NOT meet
+    if Q >= 2:
+        bad = enc_o.copy()
+        bad[:, :] &= ~np.uint32(1 << 25)
+        ob, _ = oracle.grouped_prefill(q, pool, bad, lens_o, G, 0.0625, queries=[1])
+        assert gc.rel_l2(o[1], ob[0]) > 0.05
+
+
+def test_prefill_config4_sampled():
+    c = gc.config("config4")
+    lay = c.layout
+    kv, smap = gc.gpu_pool(smla, lay, c.rows, "bf16")
+    pool, osl = gc.oracle_pool(lay, c.rows, "bf16")
+    req = np.zeros(len(c.idx), np.int32)
+    slots = smla.smla_resolve_slots(_t(c.idx), _t(c.valid), _t(req), _t(lay.page_table), _t(lay.ctx), lay.page_size)
+    oslots = oracle.resolve_slots(c.idx, c.valid, req, lay.page_table, lay.ctx, lay.page_size)
+    assert np.array_equal(slots.cpu().numpy(), oslots)
+    enc, lens = smla.smla_build_group_union(slots, _t(c.valid), c.G, lay.num_slots)
+    out, lse = smla.smla_grouped_prefill(gc.q_tensor(c.q, "bf16"), kv, enc, lens, c.G, c.scale)
+    rng = np.random.default_rng(44)
+    sample = np.sort(np.concatenate([rng.choice(len(c.idx), size=254, replace=False), [0, len(c.idx) - 1]]))
+    enc_o, lens_o = oracle.group_union(oslots, c.valid, c.G, lay.num_slots)
+    assert np.array_equal(lens.cpu().numpy(), lens_o)
+    o_ref, l_ref = oracle.grouped_prefill(c.q, pool, enc_o, lens_o, c.G, c.scale, queries=sample)
+    o = out[torch.from_numpy(sample).cuda()].float().cpu().numpy()
+    gc.assert_close(o, o_ref, 2e-2, 1e-2, "config4 out")
+    gc.assert_lse(lse[torch.from_numpy(sample).cuda()].cpu().numpy(), l_ref, 1e-3, "config4 lse")
+    assert gc.rel_l2(o, o_ref) <= 1e-2
