@@ -7,14 +7,16 @@ slot resolution (logical top-k -> physical slots, page size 1 table), stage 1 (s
 gather + MFMA scores + online softmax + MFMA P*V) and stage 2 (LSE merge). The headline
 workload is the bf16 batch of 32 requests x 64 heads, latent 512 + rope 64, contexts
 U[8K, 32K] in a 2^20-slot pool of 64-slot pages, top-k 2048. The inputs are resident in
-HBM when a timed step starts: before every timed step a 1 GiB buffer is overwritten so
-that neither the L2 nor the 256 MB Infinity Cache holds the cache rows.
+HBM when a timed step starts: before every timed step a 1 GiB buffer is read, so that
+neither the L2 nor the 256 MB Infinity Cache holds the cache rows (reading rather than
+writing it leaves no dirty lines whose write-back would compete with the step).
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -95,16 +97,18 @@ def time_decode(c, smla, torch, steps, warmup, flush):
         call()
 
     for _ in range(warmup):
-        flush.zero_()
+        flush.sum()
         step()
     torch.cuda.synchronize()
 
-    # cold steps: the flush runs between steps, outside the events
+    # cold steps: the flush runs between steps, outside the events. Python's collector is
+    # off meanwhile, so that a collection cannot stall the host between two launches.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
+    gc.disable()
     wall0 = time.perf_counter()
     for k in range(steps):
-        flush.zero_()
+        flush.sum()                       # reads 1 GiB: evicts the caches, leaves nothing dirty
         e = ev[k]
         e[0].record()
         resolve()
@@ -115,6 +119,7 @@ def time_decode(c, smla, torch, steps, warmup, flush):
         e[3].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
     res_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     s1_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
@@ -202,7 +207,7 @@ def main():
     if not os.path.exists(smla.LIB_PATH):
         raise SystemExit("libsmla.so is not built: run python -m sparse_mla_attention_resolve_amd.build")
     torch.cuda.set_device(0)
-    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device="cuda")
 
     log("generating the bf16 decode workload (batch 32, top-k 2048)")
     c2 = wl.config2()
@@ -225,7 +230,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "sparse MLA decode, bf16 q and KV, batch 32, 64 heads, latent 512 + rope 64, "
                                "contexts U[8K,32K], 2^20-slot pool of 64-slot pages, top-k 2048, step = resolve + "
-                               "split decode + LSE merge, inputs HBM-resident (1 GiB overwritten before each step)",
+                               "split decode + LSE merge, inputs HBM-resident (1 GiB read before each step)",
                    "batch": T, "heads": 64, "topk": 2048, "splits": r["splits"], "parallelism": "none (1 GPU)"},
         "hbm_gbs_step": step_gbs, "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_step": ab["step"],
@@ -255,9 +260,12 @@ def main():
             "queries_per_s": c5.q.shape[0] / (ms5 / 1e3), "ms_per_step": ms5,
             "hbm_gbs_step": ab5["step"] / (ms5 / 1e3) / 1e9,
             "stage1_gbs": ab5["stage1"] / (s15 / 1e3) / 1e9, "stage1_us": s15 * 1e3,
+            "resolve_us": float(r5["resolve_ms"].mean()) * 1e3, "stage2_us": float(r5["stage2_ms"].mean()) * 1e3,
+            "step_median_us": float(np.median(r5["step_ms"])) * 1e3,
             "stage1_frac": ab5["stage1"] / (s15 / 1e3) / 1e9 / HBM_PEAK_GBS,
             "warm_step_us": r5["warm_ms"] * 1e3, "splits": r5["splits"]}
-        log(f"fp8: step {ms5*1e3:.1f} us, stage1 {s15*1e3:.1f} us")
+        log(f"fp8: step {ms5*1e3:.1f} us (median {np.median(r5['step_ms'])*1e3:.1f}; resolve "
+            f"{r5['resolve_ms'].mean()*1e3:.1f}, stage1 {s15*1e3:.1f}, stage2 {r5['stage2_ms'].mean()*1e3:.1f})")
 
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")

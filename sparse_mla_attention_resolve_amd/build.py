@@ -38,9 +38,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libsmla")
 
 
+# Per-file code-generation options.
+#  -amdgpu-mfma-vgpr-form: the decode kernels hold their MFMA accumulators in VGPRs; left to
+#   its heuristics the compiler keeps them in AGPRs and copies them every loop iteration.
+#  -fno-honor-nans: the decode kernels never produce or test NaN (masked scores are -inf),
+#   so max needs no NaN-quieting instructions around it; infinities keep their semantics.
+FILE_FLAGS = {
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+}
+
+
 def _compile(src: str, extra: list[str], verbose: bool) -> tuple[str, str]:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -82,6 +82,7 @@ void plan_splits(int32_t T, int32_t max_len, int32_t requested, int32_t* S_out, 
   if (S < 1) S = 1;
   int32_t R = (max_len + S - 1) / S;
   R = (R + chunk - 1) / chunk * chunk;
+  if (R > smla::kMaxSplitRows) R = smla::kMaxSplitRows;   // a split's slot list lives in LDS
   S = (max_len + R - 1) / R;
   *S_out = S;
   *R_out = R;
@@ -108,7 +109,9 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   CHECK(a->table_width >= 1, SMLA_ERR_SHAPE, "%s: table_width must be >= 1", fn);
   CHECK(a->table_stride >= a->table_width, SMLA_ERR_SHAPE, "%s: table_stride < table_width", fn);
   const int64_t max_len = (int64_t)a->table_width * a->page_size;
-  CHECK(max_len <= (1 << 30), SMLA_ERR_RANGE, "%s: table_width * page_size exceeds 2^30", fn);
+  CHECK(max_len <= 256 * smla::kMaxSplitRows, SMLA_ERR_RANGE,
+        "%s: table_width * page_size exceeds %d (256 splits of %d rows)", fn, 256 * smla::kMaxSplitRows,
+        smla::kMaxSplitRows);
   CHECK(a->num_splits >= 0 && a->num_splits <= 256, SMLA_ERR_RANGE, "%s: num_splits must be in [0, 256]", fn);
   CHECK(isfinite(a->scale), SMLA_ERR_SHAPE, "%s: scale must be finite", fn);
   const int64_t qe = bf16 ? 8 : 1;   // q / out row loads are 16 bytes on the bf16 path
@@ -122,6 +125,9 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   if (a->lse) CHECK(a->lse_tok_stride >= a->H, SMLA_ERR_SHAPE, "%s: lse_tok_stride < H", fn);
   smla_status st = check_kv(a->kv, fn, false);
   if (st != SMLA_OK) return st;
+  CHECK(a->kv.row_stride < (1ll << 20) && a->kv.lat8_stride < (1ll << 20) && a->kv.rope16_stride < (1ll << 20) &&
+            a->kv.scale_stride < (1ll << 20),
+        SMLA_ERR_RANGE, "%s: kv row strides must be below 1 MiB", fn);
   if (need_ptrs && a->T > 0) {
     CHECK(a->q && a->table && a->lens && a->out, SMLA_ERR_NULL, "%s: q, table, lens and out are required", fn);
     CHECK(aligned(a->q, bf16 ? 16 : 4) && aligned(a->out, 16) && aligned(a->table, 4) && aligned(a->lens, 4) &&

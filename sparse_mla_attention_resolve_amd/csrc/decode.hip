@@ -24,10 +24,7 @@ namespace {
 
 constexpr int kHeads = 64;
 constexpr int kThreads = 256;
-constexpr int kRowBytesBf16 = 1152;
-constexpr int kLdsRowBf16 = 1168;     // 73 x 16 B: padded so 16 rows hit distinct banks
-constexpr int kLdsRowFp8 = 672;       // 42 x 16 B (656-byte packed row + pad)
-constexpr int kPStride = 40;          // bf16 per head row of the P tile (80 B)
+constexpr int kPStride = 40;          // bf16 per head row of the P tile (80 B: conflict-free reads)
 
 struct Stage1Args {
   const uint16_t* q;
@@ -42,6 +39,7 @@ struct Stage1Args {
   int32_t rows_per_split;
   int32_t S;
   int32_t H;
+  int32_t T;
   float* part_o;            // [T][S][H][512]
   float* part_lse;          // [T][S][H], natural log
 };
@@ -64,242 +62,347 @@ __device__ __forceinline__ int token_len(const Stage1Args& a, int t) {
   return n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
 }
 
+// Shared-memory layout of one gathered row: the row's 16-byte units, unit u stored at
+// position u ^ ((row >> 1) & 7). The XOR spreads the 16 rows that one MFMA operand read
+// touches over distinct banks without padding, so a 32-row chunk is a whole number of
+// 64-lane x 16-byte direct-to-LDS load instructions per wave.
 template <int KV>
-struct KvTraits;
+struct Lay;
 template <>
-struct KvTraits<SMLA_BF16> {
-  static constexpr int kUnits = 72;             // 16-byte units per row
-  static constexpr int kLdsRow = kLdsRowBf16;
-  static constexpr int kPerThread = (kChunk * kUnits + kThreads - 1) / kThreads;   // 9
-  __device__ static const char* unit_src(const smla_kv& kv, int64_t slot, int u) {
-    return (const char*)kv.rows + slot * kv.row_stride + u * 16;
-  }
+struct Lay<SMLA_BF16> {
+  static constexpr int kUnits = 72;      // 1152-byte row
+  static constexpr int kNBuf = 4;        // chunks in the LDS ring
 };
 template <>
-struct KvTraits<SMLA_FP8_E4M3> {
-  static constexpr int kUnits = 41;             // 32 latent + 8 rope + 1 scale
-  static constexpr int kLdsRow = kLdsRowFp8;
-  static constexpr int kPerThread = (kChunk * kUnits + kThreads - 1) / kThreads;   // 6
-  __device__ static const char* unit_src(const smla_kv& kv, int64_t slot, int u) {
-    if (u < 32) return (const char*)kv.lat8 + slot * kv.lat8_stride + u * 16;
-    if (u < 40) return (const char*)kv.rope16 + slot * kv.rope16_stride + (u - 32) * 16;
-    return (const char*)kv.scale + slot * kv.scale_stride;   // 4 useful bytes of 16 read
-  }
+struct Lay<SMLA_FP8_E4M3> {
+  static constexpr int kUnits = 40;      // 512 e4m3 codes + 64 bf16 rotary values; scales live apart
+  static constexpr int kNBuf = 6;
 };
 
-template <int KV>
-__global__ void __launch_bounds__(kThreads, 1) decode_stage1_mfma(Stage1Args a) {
-  using Tr = KvTraits<KV>;
-  constexpr int kBuf = kChunk * Tr::kLdsRow;
-  __shared__ __attribute__((aligned(16))) char kvbuf[2][kBuf];
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[kHeads * kPStride];
-  __shared__ float xch[2][kHeads];
+__device__ __forceinline__ int swz(int row, int unit) { return unit ^ ((row >> 1) & 7); }
 
-  const int t = blockIdx.x / a.S;
-  const int s = blockIdx.x % a.S;
+// Source of the gathers of masked rows (a row past the list's length, or a -1 entry):
+// the LDS tile then holds zeros there, so a zero softmax weight meets finite values.
+__device__ const uint4 kZeroRow[72] = {};
+
+// Workgroup barrier that waits for this wave's LDS operations only: the outstanding
+// direct-to-LDS gathers of later chunks stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+// 16-byte direct-to-LDS gather: lane l's 16 bytes at `src` land at lds_wave_base + 16 l.
+// Issued through inline assembly on purpose: the compiler does not see a pending LDS
+// write, so it adds no wait for it before the LDS reads of other ring slots; the kernel
+// orders the ring itself (wait_chunks, then a barrier). M0 is set right here and nothing
+// else in these kernels reads it.
+__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base);
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
+}
+
+// Wait until at most `chunks` chunks of `LOADS` gathers each are still in flight.
+template <int MAXC, int LOADS>
+__device__ __forceinline__ void wait_chunks(int chunks) {
+  if constexpr (MAXC > 0) {
+    if (chunks >= MAXC) { wait_vmcnt<MAXC * LOADS>(); return; }
+    wait_chunks<MAXC - 1, LOADS>(chunks);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+constexpr int kS1Threads = 512;   // 8 waves, two per SIMD: one waits on LDS while the other computes
+constexpr int kLoaders = 4;       // waves 0..3 issue the gathers
+
+// Workgroup id -> (token, split). Workgroups are dispatched to the 8 XCDs round robin;
+// when T is a multiple of 8 every split of a token runs on one XCD, so the token's partial
+// results stay in that XCD's L2 for stage 2, which uses the same token -> XCD rule.
+__device__ __forceinline__ void stage1_coords(int b, int T, int S, int& t, int& s) {
+  if ((T & 7) == 0) {
+    const int i = b >> 3;
+    t = (b & 7) + 8 * (i / S);
+    s = i % S;
+  } else {
+    t = b / S;
+    s = b % S;
+  }
+}
+
+template <int KV>
+__global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a) {
+  using L = Lay<KV>;
+  constexpr int kRowBytes = L::kUnits * 16;
+  constexpr int kChunkBytes = kChunk * kRowBytes;
+  constexpr int kLoads = kChunk * L::kUnits / (kLoaders * 64);   // per loader thread: 9 (bf16), 5 (fp8)
+  static_assert(kChunk * L::kUnits % (kLoaders * 64) == 0, "a chunk must tile the loaders' instructions");
+  constexpr int kNBuf = L::kNBuf;
+  __shared__ __attribute__((aligned(16))) char kvbuf[kNBuf][kChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[4][16 * kPStride];
+  __shared__ float xmax[2][kHeads];
+  __shared__ float xsum[2][kHeads];
+  __shared__ int32_t slot_s[kMaxSplitRows];
+  __shared__ float scale_s[KV == SMLA_FP8_E4M3 ? kMaxSplitRows : 1];
+
+  int t, s;
+  stage1_coords(blockIdx.x, a.T, a.S, t, s);
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int hh = w >> 1;      // head half: heads 32hh .. 32hh+31
-  const int x = w & 1;        // score phase: row half of the chunk; PV phase: column half
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform, kept in an SGPR
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int hq = w & 3;       // heads 16hq .. 16hq+15
+  const int x = w >> 2;       // scores: chunk rows 16x .. 16x+15; P V: columns 256x .. 256x+255
+  const int h0 = 16 * hq;
 
   const int len = token_len(a, t);
   const int r0 = s * a.rows_per_split;
-  if (r0 >= len) return;      // inactive split: stage 2 never reads it
+  if (r0 >= len) return;                      // inactive split: stage 2 never reads it
   const int r1 = min(r0 + a.rows_per_split, len);
-  const int nchunks = (r1 - r0 + kChunk - 1) / kChunk;
+  const int nrows = r1 - r0;
+  const int nchunks = (nrows + kChunk - 1) / kChunk;
 
-  // q fragments (A operand): head hh*32 + 16mt + c, dims 32ks + 8g .. +7
-  bf16x8 qf[2][18];
-  {
-    const uint16_t* qt = a.q + (int64_t)t * a.q_tok_stride;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const uint16_t* qh = qt + (int64_t)(hh * 32 + mt * 16 + c) * a.q_head_stride;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) qf[mt][ks] = as_bf16x8(*(const uint4*)(qh + ks * 32 + 8 * g));
-    }
+  // slots (and fp8 scales) of the split's rows; -1 marks a masked row
+  for (int i = tid; i < nchunks * kChunk; i += kS1Threads) {
+    const int64_t sl = i < nrows ? slot_of(a, t, r0 + i) : -1;
+    slot_s[i] = (int32_t)sl;
+    if constexpr (KV == SMLA_FP8_E4M3)
+      scale_s[i] = sl >= 0 ? *(const float*)((const char*)a.kv.scale + sl * a.kv.scale_stride) : 0.f;
   }
 
-  // stage the chunk that starts at position p0 into registers
-  uint4 stage[Tr::kPerThread];
-  auto gather = [&](int p0) {
+  // q fragments (A operand of the scores): head h0 + c, dims 32ks + 8g .. +7
+  bf16x8 qf[18];
+  {
+    const uint16_t* qh = a.q + (int64_t)t * a.q_tok_stride + (int64_t)(h0 + c) * a.q_head_stride;
 #pragma unroll
-    for (int k = 0; k < Tr::kPerThread; ++k) {
-      const int u = tid + kThreads * k;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (u < kChunk * Tr::kUnits) {
-        const int row = u / Tr::kUnits, col = u % Tr::kUnits;
-        const int p = p0 + row;
-        if (p < r1) {
-          const int64_t slot = slot_of(a, t, p);
-          if (slot >= 0) {
-            const char* src = Tr::unit_src(a.kv, slot, col);
-            if (KV == SMLA_FP8_E4M3 && col == 40)
-              v.x = *(const uint32_t*)src;
-            else
-              v = *(const uint4*)src;
-          }
-        }
-      }
-      stage[k] = v;
-    }
-  };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < Tr::kPerThread; ++k) {
-      const int u = tid + kThreads * k;
-      if (u < kChunk * Tr::kUnits) {
-        const int row = u / Tr::kUnits, col = u % Tr::kUnits;
-        *(uint4*)(kvbuf[buf] + row * Tr::kLdsRow + col * 16) = stage[k];
-      }
-    }
-  };
-
-  f32x4 oacc[2][16];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 16; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2][4], l_run[2][4];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) { m_run[mt][v] = -INFINITY; l_run[mt][v] = 0.f; }
-
-  gather(r0);
-  commit(0);
+    for (int ks = 0; ks < 18; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qh + ks * 32 + 8 * g));
+  }
+  // every plain load is done before the first gather is enqueued, so that the counter
+  // waits below count gathers only
+  wait_vmcnt<0>();
   __syncthreads();
 
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const int buf = ci & 1;
-    const int p0 = r0 + ci * kChunk;
-    if (ci + 1 < nchunks) gather(p0 + kChunk);
-    const char* kb = kvbuf[buf];
+  // plane bases and strides as scalars (a per-lane choice between two fields of the
+  // argument struct would otherwise become a memory load)
+  const char* const lat8 = (const char*)a.kv.lat8;
+  const char* const rope16_m32 = (const char*)a.kv.rope16 - 32 * 16;
+  // row strides fit 32 bits (a row is at most a few KB), so slot * stride is one 32x32->64 multiply
+  const uint32_t lat8_stride32 = (uint32_t)a.kv.lat8_stride, rope16_stride32 = (uint32_t)a.kv.rope16_stride;
+  const uint32_t row_stride32 = (uint32_t)a.kv.row_stride;
 
-    // ---- scores: heads hh*32 + 16mt + (4g+v), row x*16 + c of the chunk
-    const int myrow = x * 16 + c;
-    const char* krow = kb + myrow * Tr::kLdsRow;
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    float rowscale = 1.0f;
+  // gather chunk ci into ring slot ci % kNBuf: each loader thread owns the same kLoads
+  // 16-byte positions of every chunk, precomputed here as (row, byte offset in the row,
+  // plane); masked rows gather from the zero row
+  int32_t lpos[kLoads];
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) {
+    const int pos = (k * kLoaders + w) * 64 + lane;
+    const int row = pos / L::kUnits, unit = swz(row, pos % L::kUnits);   // the swizzle is an involution
+    lpos[k] = row | (unit << 8);
+  }
+  auto issue = [&](int ci) {
+    char* base = kvbuf[ci % kNBuf];
+    const int32_t* srow = slot_s + ci * kChunk;
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int32_t sl = srow[lpos[k] & 0xff];
+      const int unit = lpos[k] >> 8;
+      const bool live = sl >= 0;
+      const uint32_t slot = live ? (uint32_t)sl : 0u;
+      const char* src;
+      if constexpr (KV == SMLA_BF16) {
+        src = (live ? (const char*)a.kv.rows : (const char*)kZeroRow) + (uint64_t)slot * row_stride32 + unit * 16;
+      } else {
+        const bool lat = unit < 32;
+        const char* plane = live ? (lat ? lat8 : rope16_m32) : (const char*)kZeroRow;
+        src = plane + (uint64_t)slot * (lat ? lat8_stride32 : rope16_stride32) + unit * 16;
+      }
+      dma16(src, base + (k * kLoaders + w) * 64 * 16);
+    }
+  };
+
+  f32x4 oacc[16];
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }
+  uint16_t* pw = pbuf[hq];
+  const bool loader = w < kLoaders;
+
+  if (loader)
+    for (int ci = 0; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+
+  for (int ci = 0; ci < nchunks; ++ci) {
+    // chunk ci is in LDS once its loaders' gathers are done and every wave got here
+    if (loader) wait_chunks<kNBuf - 2, kLoads>(min(kNBuf - 2, nchunks - 1 - ci));
+    lds_barrier();
+    if (loader && ci + kNBuf - 1 < nchunks) issue(ci + kNBuf - 1);   // into the slot every wave is done with
+    const char* kb = kvbuf[ci % kNBuf];
+
+    // ---- scores: heads h0 + 4g + v against chunk row 16x + c
+    const int row = 16 * x + c;
+    const int key = (row >> 1) & 7;
+    const char* kr = kb + row * kRowBytes;
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float rs = 1.f;
     if constexpr (KV == SMLA_BF16) {
+      // unit 4ks + g sits at 4(ks ^ (key >> 2)) + (g ^ (key & 3)): one base for even and
+      // one for odd ks, plus the immediate 64 ks
+      const int kh = (key >> 2) * 64;
+      const char* b_even = kr + 16 * (g ^ (key & 3)) + kh;
+      const char* b_odd = kr + 16 * (g ^ (key & 3)) - kh;
+      // operand reads run three MFMAs ahead; the schedule barriers keep the compiler from
+      // hoisting every read (which would not fit the register file)
+      uint4 kq[4];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) kq[i] = *(const uint4*)(((i & 1) ? b_odd : b_even) + 64 * i);
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        const bf16x8 kf = as_bf16x8(*(const uint4*)(krow + (ks * 32 + 8 * g) * 2));
-        sacc[0] = mfma16x16x32(qf[0][ks], kf, sacc[0]);
-        sacc[1] = mfma16x16x32(qf[1][ks], kf, sacc[1]);
+        if (ks + 3 < 18) kq[(ks + 3) & 3] = *(const uint4*)((((ks + 3) & 1) ? b_odd : b_even) + 64 * (ks + 3));
+        sacc = mfma16x16x32(qf[ks], as_bf16x8(kq[ks & 3]), sacc);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      f32x4 racc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // unit 2ks + g/2 sits at 8(ks >> 2) + 2((ks & 3) ^ (key >> 1)) + ((g >> 1) ^ (key & 1))
+      const char* kb4[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) kb4[m] = kr + 32 * (m ^ (key >> 1)) + 16 * ((g >> 1) ^ (key & 1)) + 8 * (g & 1);
+      uint2 kq[4];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) kq[i] = *(const uint2*)(kb4[i & 3] + 128 * (i >> 2));
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
-        const uint2 codes = *(const uint2*)(krow + ks * 32 + 8 * g);
-        const bf16x8 kf = e4m3x8_to_bf16x8(codes.x, codes.y);
-        sacc[0] = mfma16x16x32(qf[0][ks], kf, sacc[0]);
-        sacc[1] = mfma16x16x32(qf[1][ks], kf, sacc[1]);
+        if (ks + 3 < 16) kq[(ks + 3) & 3] = *(const uint2*)(kb4[(ks + 3) & 3] + 128 * ((ks + 3) >> 2));
+        sacc = mfma16x16x32(qf[ks], e4m3x8_to_bf16x8(kq[ks & 3].x, kq[ks & 3].y), sacc);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      f32x4 racc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 16; ks < 18; ++ks) {
-        const bf16x8 kf = as_bf16x8(*(const uint4*)(krow + SMLA_FP8_ROPE_OFFSET + ((ks - 16) * 32 + 8 * g) * 2));
-        racc[0] = mfma16x16x32(qf[0][ks], kf, racc[0]);
-        racc[1] = mfma16x16x32(qf[1][ks], kf, racc[1]);
+        const bf16x8 kf = as_bf16x8(*(const uint4*)(kr + swz(row, 32 + (ks - 16) * 4 + g) * 16));
+        racc = mfma16x16x32(qf[ks], kf, racc);
       }
-      rowscale = *(const float*)(krow + SMLA_FP8_SCALE_OFFSET);
+      rs = scale_s[ci * kChunk + row];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sacc[mt][v] = sacc[mt][v] * rowscale + racc[mt][v];
+      for (int v = 0; v < 4; ++v) sacc[v] = sacc[v] * rs + racc[v];
     }
-    const int p = p0 + myrow;
-    const bool row_ok = p < r1 && slot_of(a, t, p) >= 0;
-    float sv[2][4], mloc[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        sv[mt][v] = row_ok ? sacc[mt][v] * a.scale_log2 : -INFINITY;
-        mloc[mt][v] = max16(sv[mt][v]);
-      }
-    if (c == 0) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) xch[x][hh * 32 + mt * 16 + 4 * g + v] = mloc[mt][v];
-    }
-    __syncthreads();
-    float alpha[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int h = hh * 32 + mt * 16 + 4 * g + v;
-        const float mc = fmaxf(mloc[mt][v], xch[x ^ 1][h]);
-        const float mn = fmaxf(m_run[mt][v], mc);
-        const bool none = mn == -INFINITY;
-        alpha[mt][v] = none ? 1.0f : exp2f(m_run[mt][v] - mn);
-        const float pv = none ? 0.0f : exp2f(sv[mt][v] - mn);
-        l_run[mt][v] = l_run[mt][v] * alpha[mt][v] + sum16(pv);
-        m_run[mt][v] = mn;
-        pbuf[h * kPStride + myrow] = (uint16_t)f32_to_bf16_rne(pv * rowscale);
-      }
-    __syncthreads();
 
-    // ---- P * V: heads hh*32 + 16mt + (4g+v), columns x*256 + 16nt + c
+    // ---- online softmax. The two waves of a head quarter hold rows 0..15 and 16..31 of
+    // the chunk and agree on the chunk maximum through LDS. The running max only moves when
+    // a score exceeds it by more than 2^8, so most chunks skip the rescale of O.
+    const bool ok = slot_s[ci * kChunk + row] >= 0;
+    float sv[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int v = 0; v < 4; ++v) {
+      sv[v] = ok ? sacc[v] * a.scale_log2 : -INFINITY;
+      const float mloc = max16(sv[v]);
+      if (c == 0) xmax[x][h0 + 4 * g + v] = mloc;
+    }
+    lds_barrier();
+    float alpha[4];
+    bool grow = false;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float mc = fmaxf(xmax[0][h0 + 4 * g + v], xmax[1][h0 + 4 * g + v]);
+      const bool up = mc > m_run[v] + 8.0f;
+      const float mn = up ? mc : m_run[v];
+      alpha[v] = up ? __builtin_amdgcn_exp2f(m_run[v] - mn) : 1.0f;
+      grow |= up;
+      const float pv = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] - mn);
+      pw[(4 * g + v) * kPStride + row] = __builtin_bit_cast(uint16_t, (__bf16)(pv * rs));
+      l_run[v] = l_run[v] * alpha[v] + sum16(pv);
+      m_run[v] = mn;
+    }
+    if (__any(grow)) {
 #pragma unroll
       for (int nt = 0; nt < 16; ++nt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) oacc[mt][nt][v] *= alpha[mt][v];
-    bf16x8 pf[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      pf[mt] = as_bf16x8(*(const uint4*)(pbuf + (hh * 32 + mt * 16 + c) * kPStride + 8 * g));
-#pragma unroll
-    for (int nt = 0; nt < 16; ++nt) {
-      const int col = x * 256 + nt * 16 + c;
-      bf16x8 vf;
-      if constexpr (KV == SMLA_BF16) {
-        uint32_t e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = *(const uint16_t*)(kb + (8 * g + i) * Tr::kLdsRow + col * 2);
-        vf = as_bf16x8(make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                                  e[6] | (e[7] << 16)));
-      } else {
-        uint32_t b[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) b[i] = *(const uint8_t*)(kb + (8 * g + i) * Tr::kLdsRow + col);
-        vf = e4m3x8_to_bf16x8(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                              b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
-      }
-      oacc[0][nt] = mfma16x16x32(pf[0], vf, oacc[0][nt]);
-      oacc[1][nt] = mfma16x16x32(pf[1], vf, oacc[1][nt]);
+        for (int v = 0; v < 4; ++v) oacc[nt][v] *= alpha[v];
     }
-    if (ci + 1 < nchunks) commit(buf ^ 1);
-    __syncthreads();
+    lds_barrier();
+
+    // ---- O += P V: A = P[head h0 + c][rows 8g .. 8g+7], B = V[rows 8g .. 8g+7][256x + 16nt + c]
+    if constexpr (KV == SMLA_BF16) {
+      // Two 16x16x16 MFMAs per 16-column tile, over chunk rows 0..15 and 16..31. A = P[head
+      // h0 + c][rows 16kh + 4g .. +3]; B = V[rows 16kh + 4g .. +3][256x + 16nt + c], which one
+      // transposed 16-bit read delivers when the group's lane c points at row 16kh + 4g + c/4,
+      // columns 256x + 16nt + 4(c%4) .. +3: unit 32x + 2nt + (c%4)/2 of that row, stored at
+      // 32x + 8(nt >> 2) + 2((nt & 3) ^ (key >> 1)) + (((c%4)/2) ^ (key & 1)).
+      const i16x4 pa0 = *(const i16x4*)(pw + c * kPStride + 4 * g);
+      const i16x4 pa1 = *(const i16x4*)(pw + c * kPStride + 16 + 4 * g);
+      const int b = (c & 3) >> 1;
+      const char* vb0[4];
+      const char* vb1[4];
+      {
+        const int r0 = 4 * g + (c >> 2), r1 = r0 + 16;
+        const int k0 = (r0 >> 1) & 7, k1 = (r1 >> 1) & 7;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          vb0[m] = kb + r0 * kRowBytes + 512 * x + 32 * (m ^ (k0 >> 1)) + 16 * (b ^ (k0 & 1)) + 8 * (c & 1);
+          vb1[m] = kb + r1 * kRowBytes + 512 * x + 32 * (m ^ (k1 >> 1)) + 16 * (b ^ (k1 & 1)) + 8 * (c & 1);
+        }
+      }
+      auto vread = [&](int i) {          // i = 2 nt + kh
+        const char* const* vb = (i & 1) ? vb1 : vb0;
+        const int nt = i >> 1;
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vb[nt & 3] + 128 * (nt >> 2)));
+      };
+      i16x4 vq[4];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) vq[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i + 3 < 32) vq[(i + 3) & 3] = vread(i + 3);
+        oacc[i >> 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k((i & 1) ? pa1 : pa0, vq[i & 3], oacc[i >> 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      const bf16x8 pf = as_bf16x8(*(const uint4*)(pw + c * kPStride + 8 * g));
+      // transposed 8-bit read: lane 16g + c receives V[8g + 0..7][256x + 16nt + c] when the
+      // group's lane c points at row 8g + c/2, columns 256x + 16nt + 8(c%2) .. +7: unit
+      // 16x + nt, stored at 16x + 8(nt >> 3) + ((nt & 7) ^ key): eight bases plus an immediate.
+      const int r = 8 * g + (c >> 1);
+      const int vkey = (r >> 1) & 7;
+      const char* vb[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) vb[m] = kb + r * kRowBytes + 256 * x + 16 * (m ^ vkey) + 8 * (c & 1);
+      auto vread = [&](int nt) {
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(vb[nt & 7] + 128 * (nt >> 3)));
+      };
+      i32x2 vq[4];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) vq[i] = vread(i);
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt) {
+        if (nt + 3 < 16) vq[(nt + 3) & 3] = vread(nt + 3);
+        oacc[nt] = mfma16x16x32(pf, e4m3x8_to_bf16x8((uint32_t)vq[nt & 3][0], (uint32_t)vq[nt & 3][1]), oacc[nt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
 
   // ---- combine the two row halves' sums, normalise, write the split's partials
   if (c == 0) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) xch[x][hh * 32 + mt * 16 + 4 * g + v] = l_run[mt][v];
+    for (int v = 0; v < 4; ++v) xsum[x][h0 + 4 * g + v] = l_run[v];
   }
-  __syncthreads();
+  lds_barrier();
   const int64_t part = (int64_t)t * a.S + s;
   float* po = a.part_o + part * a.H * kLatent;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int v = 0; v < 4; ++v) {
+    const int h = h0 + 4 * g + v;
+    const float l = xsum[0][h] + xsum[1][h];
+    const float inv = l > 0.f ? 1.0f / l : 0.0f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int h = hh * 32 + mt * 16 + 4 * g + v;
-      const float l = xch[0][h] + xch[1][h];
-      const float inv = l > 0.f ? 1.0f / l : 0.0f;
-#pragma unroll
-      for (int nt = 0; nt < 16; ++nt) po[h * kLatent + x * 256 + nt * 16 + c] = oacc[mt][nt][v] * inv;
-      if (x == 0 && c == 0)
-        a.part_lse[part * a.H + h] = l > 0.f ? (m_run[mt][v] + log2f(l)) * kLn2 : -INFINITY;
-    }
+    for (int nt = 0; nt < 16; ++nt) po[h * kLatent + 256 * x + nt * 16 + c] = oacc[nt][v] * inv;
+    if (x == 0 && c == 0) a.part_lse[part * a.H + h] = l > 0.f ? (m_run[v] + log2f(l)) * kLn2 : -INFINITY;
+  }
 }
 
 // fp32 q and fp32 cache: a plain VALU path, 16 heads per workgroup, rows in chunks of 16.
@@ -367,6 +470,7 @@ __global__ void __launch_bounds__(kThreads) decode_stage1_f32(Stage1Args a) {
 }
 
 struct Stage2Args {
+  int32_t T;
   const int32_t* lens;
   int32_t max_len;
   int32_t rows_per_split;
@@ -382,8 +486,18 @@ struct Stage2Args {
 
 // One workgroup per token and 8 heads; thread = (head, 16 consecutive columns).
 __global__ void __launch_bounds__(256) decode_stage2(Stage2Args a) {
-  const int t = blockIdx.x;
-  const int h = blockIdx.y * 8 + (threadIdx.x >> 5);
+  // same token -> XCD rule as stage 1, so that the partials come from this XCD's L2
+  const int hg_count = (a.H + 7) / 8;
+  int t, hg;
+  if ((a.T & 7) == 0) {
+    const int i = blockIdx.x >> 3;
+    t = (blockIdx.x & 7) + 8 * (i / hg_count);
+    hg = i % hg_count;
+  } else {
+    t = blockIdx.x / hg_count;
+    hg = blockIdx.x % hg_count;
+  }
+  const int h = hg * 8 + (threadIdx.x >> 5);
   const int c0 = (threadIdx.x & 31) * 16;
   if (h >= a.H) return;
   int len = a.lens[t];
@@ -456,6 +570,7 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   a.rows_per_split = plan.rows_per_split;
   a.S = plan.S;
   a.H = d.H;
+  a.T = d.T;
   a.part_o = (float*)ws;
   a.part_lse = (float*)((char*)ws + plan.part_o_bytes);
 
@@ -464,14 +579,15 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
     dim3 grid(plan.S * d.T, (d.H + 15) / 16);
     hipLaunchKernelGGL(decode_stage1_f32, grid, dim3(kThreads), 0, stream, a);
   } else if (d.kv.dtype == SMLA_BF16) {
-    hipLaunchKernelGGL(decode_stage1_mfma<SMLA_BF16>, dim3(plan.S * d.T), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_stage1_mfma<SMLA_BF16>, dim3(plan.S * d.T), dim3(kS1Threads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_stage1_mfma<SMLA_FP8_E4M3>, dim3(plan.S * d.T), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_stage1_mfma<SMLA_FP8_E4M3>, dim3(plan.S * d.T), dim3(kS1Threads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(stages & 2)) return e;
 
   Stage2Args b;
+  b.T = d.T;
   b.lens = d.lens;
   b.max_len = plan.max_len;
   b.rows_per_split = plan.rows_per_split;
@@ -485,7 +601,7 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   b.lse = d.lse;
   b.lse_tok_stride = d.lse_tok_stride;
   b.out_f32 = d.q_dtype == SMLA_F32;
-  hipLaunchKernelGGL(decode_stage2, dim3(d.T, (d.H + 7) / 8), dim3(256), 0, stream, b);
+  hipLaunchKernelGGL(decode_stage2, dim3(d.T * ((d.H + 7) / 8)), dim3(256), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -66,19 +66,30 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return as_bf16x8(v);
 }
 
-// Reductions over the 16 lanes that share lane / 16 (one column group of an MFMA tile).
+// Reductions over the 16 lanes that share lane / 16 (one column group of an MFMA tile),
+// with DPP lane moves: swap neighbours, swap pairs, mirror within 8, mirror within 16.
+// After the four steps every lane of the group holds the group's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadSwap1 = 0xb1;    // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadSwap2 = 0x4e;    // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
 __device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, 64));
-  v = fmaxf(v, __shfl_xor(v, 2, 64));
-  v = fmaxf(v, __shfl_xor(v, 4, 64));
-  v = fmaxf(v, __shfl_xor(v, 8, 64));
+  v = fmaxf(v, dpp<kDppQuadSwap1>(v));
+  v = fmaxf(v, dpp<kDppQuadSwap2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
   return v;
 }
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
+  v += dpp<kDppQuadSwap1>(v);
+  v += dpp<kDppQuadSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
   return v;
 }
 

@@ -115,6 +115,11 @@ def _stream(stream=None):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _rs(t: torch.Tensor) -> int:
+    """Row stride of a 2-D (or leading-dim) tensor; a single row may carry any stride."""
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t[0].numel())
+
+
 def _i32(t: torch.Tensor, name: str):
     if t.dtype != torch.int32:
         raise TypeError(f"{name} must be int32")
@@ -194,9 +199,9 @@ def smla_resolve_slots(idx, valid, tok_req, page_table, seq_lens, page_size: int
     if valid is not None:
         _i32(valid, "valid")
     R, ptw = page_table.shape
-    _check(_lib.smla_resolve_slots(_ptr(idx), idx.stride(0), _ptr(valid), _ptr(tok_req), R, _ptr(page_table),
-                                   page_table.stride(0), ptw, _ptr(seq_lens), page_size, T, W, _ptr(slots),
-                                   slots.stride(0), _stream(stream)))
+    _check(_lib.smla_resolve_slots(_ptr(idx), _rs(idx), _ptr(valid), _ptr(tok_req), R, _ptr(page_table),
+                                   _rs(page_table), ptw, _ptr(seq_lens), page_size, T, W, _ptr(slots),
+                                   _rs(slots), _stream(stream)))
     return slots
 
 
@@ -207,18 +212,18 @@ def _decode_args(q, kv: KvCache, table, lens, page_size, scale, out, lse, num_sp
     a.T, a.H = T, H
     a.q_dtype = SMLA_BF16 if q.dtype == torch.bfloat16 else SMLA_F32
     a.page_size = page_size
-    a.q, a.q_tok_stride, a.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
+    a.q, a.q_tok_stride, a.q_head_stride = q.data_ptr(), _rs(q), q.stride(1)
     a.kv = kv.desc()
     _i32(table, "table")
     _i32(lens, "lens")
-    a.table, a.table_stride, a.table_width = table.data_ptr(), table.stride(0), table.shape[1]
+    a.table, a.table_stride, a.table_width = table.data_ptr(), _rs(table), table.shape[1]
     a.num_splits = num_splits
     a.lens = lens.data_ptr()
     a.scale = scale
     if out is not None:
-        a.out, a.out_tok_stride, a.out_head_stride = out.data_ptr(), out.stride(0), out.stride(1)
+        a.out, a.out_tok_stride, a.out_head_stride = out.data_ptr(), _rs(out), out.stride(1)
     if lse is not None:
-        a.lse, a.lse_tok_stride = lse.data_ptr(), lse.stride(0)
+        a.lse, a.lse_tok_stride = lse.data_ptr(), _rs(lse)
     return a
 
 
@@ -296,8 +301,8 @@ def smla_build_group_union(slots, valid, G: int, num_slots: int, enc: Optional[t
         lens = torch.empty((ng,), dtype=torch.int32, device=slots.device)
     if valid is not None:
         _i32(valid, "valid")
-    _check(_lib.smla_build_group_union(_ptr(slots), slots.stride(0), _ptr(valid), Q, W, G, num_slots,
-                                       _ptr(enc), enc.stride(0), _ptr(lens), _stream(stream)))
+    _check(_lib.smla_build_group_union(_ptr(slots), _rs(slots), _ptr(valid), Q, W, G, num_slots,
+                                       _ptr(enc), _rs(enc), _ptr(lens), _stream(stream)))
     return enc, lens
 
 
@@ -312,15 +317,15 @@ def smla_grouped_prefill(q, kv: KvCache, enc, lens, G: int, scale: float,
         lse = torch.empty((Q, H), dtype=torch.float32, device=q.device)
     a = smla_prefill_args()
     a.Q, a.H, a.G, a.enc_width = Q, H, G, enc.shape[1]
-    a.q, a.q_tok_stride, a.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
+    a.q, a.q_tok_stride, a.q_head_stride = q.data_ptr(), _rs(q), q.stride(1)
     a.kv = kv.desc()
-    a.enc, a.enc_stride = enc.data_ptr(), enc.stride(0)
+    a.enc, a.enc_stride = enc.data_ptr(), _rs(enc)
     _i32(lens, "lens")
     a.lens = lens.data_ptr()
     a.scale = scale
-    a.out, a.out_tok_stride, a.out_head_stride = out.data_ptr(), out.stride(0), out.stride(1)
+    a.out, a.out_tok_stride, a.out_head_stride = out.data_ptr(), _rs(out), out.stride(1)
     if lse is not None:
-        a.lse, a.lse_tok_stride = lse.data_ptr(), lse.stride(0)
+        a.lse, a.lse_tok_stride = lse.data_ptr(), _rs(lse)
     _check(_lib.smla_grouped_prefill(ctypes.byref(a), _stream(stream)))
     return out, lse
 
@@ -331,6 +336,6 @@ def smla_kv_write(src: torch.Tensor, slot_mapping: torch.Tensor, kv: KvCache, st
     sd = SMLA_F32 if src.dtype == torch.float32 else SMLA_BF16
     _i32(slot_mapping, "slot_mapping")
     d = kv.desc()
-    _check(_lib.smla_kv_write(_ptr(src), sd, src.stride(0), _ptr(slot_mapping), T, ctypes.byref(d),
+    _check(_lib.smla_kv_write(_ptr(src), sd, _rs(src), _ptr(slot_mapping), T, ctypes.byref(d),
                               _stream(stream)))
     return kv
