@@ -210,7 +210,7 @@ def main():
     flush = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device="cuda")
 
     log("generating the bf16 decode workload (batch 32, top-k 2048)")
-    c2 = wl.config2()
+    c2 = wl.decode_bf16_b32()
     ab = algorithmic_bytes(c2, "bf16")
     log("timing bf16 decode")
     r = time_decode(c2, smla, torch, args.steps, args.warmup, flush)
@@ -249,7 +249,7 @@ def main():
 
     if not args.no_fp8:
         log("generating the fp8-KV decode workload (batch 64)")
-        c5 = wl.config5()
+        c5 = wl.decode_fp8_b64()
         ab5 = algorithmic_bytes(c5, "fp8")
         log("timing fp8-KV decode")
         r5 = time_decode(c5, smla, torch, args.steps, args.warmup, flush)

@@ -97,7 +97,7 @@ typedef struct {
 } smla_kv;
 
 /* ---------------------------------------------------------------------------------
- * a1. Slot resolution (the virtual block table).
+ * Slot resolution (the virtual block table).
  *
  * slots[t, j] = page_table[r, i / P] * P + i % P, with r = tok_req[t], i = idx[t, j],
  * P = page_size, when j < valid[t] (or valid == NULL), 0 <= r < R, 0 <= i < seq_lens[r],
@@ -124,7 +124,7 @@ smla_status smla_resolve_slots(const int32_t* idx, int64_t idx_stride, const int
                                int64_t slots_stride, void* stream);
 
 /* ---------------------------------------------------------------------------------
- * a2 + a3 (+ a4, a8). Split decode attention over a block table.
+ * Split decode attention over a block table.
  *
  * For every query token t and head h: softmax attention of q[t, h] over the rows its
  * table row names -- page_size 1: the first lens[t] entries of table[t] are slots
@@ -183,7 +183,7 @@ smla_status smla_sparse_decode_stage2(const smla_decode_args* args, void* worksp
                                       void* stream);
 
 /* ---------------------------------------------------------------------------------
- * a5. Group top-k union with per-query membership bits.
+ * Group top-k union with per-query membership bits.
  *
  * Queries are grouped G at a time in order (group g = queries gG .. min(gG+G, Q)-1; the
  * last group may be short and its missing members own no bits). For each group the
@@ -208,7 +208,7 @@ smla_status smla_build_group_union(const int32_t* slots, int64_t slots_stride, c
                                    uint32_t* enc, int64_t enc_stride, int32_t* lens, void* stream);
 
 /* ---------------------------------------------------------------------------------
- * a6. Grouped sparse prefill.
+ * Grouped sparse prefill.
  *
  * G consecutive queries with H heads each fill one 128-row tile (G * H == 128): the
  * tile gathers its group's union rows once and row i*H + h (member i, head h) attends,
@@ -240,7 +240,7 @@ typedef struct {
 smla_status smla_grouped_prefill(const smla_prefill_args* args, void* stream);
 
 /* ---------------------------------------------------------------------------------
- * a7. Cache write.
+ * Cache write.
  *
  * Writes row i of src into slot slot_mapping[i] of dst (rows with slot_mapping[i] < 0
  * or >= dst->num_slots are skipped), the write that precedes attention in a decode step

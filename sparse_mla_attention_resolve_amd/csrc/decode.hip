@@ -1,4 +1,4 @@
-// a2 + a3 (+ a4, a8): split decode attention over a block table.
+// Split decode attention over a block table.
 //
 // Stage 1 (one workgroup per token and split) walks the split's rows in chunks of 32:
 // it gathers the chunk's 576-wide rows from the pool into LDS, computes the scores of

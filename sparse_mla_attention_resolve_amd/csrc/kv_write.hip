@@ -1,4 +1,4 @@
-// a7: cache write, bf16 / fp32 / fp8 e4m3 with a per-token scale. The Assertion That
+// Cache write, bf16 / fp32 / fp8 e4m3 with a per-token scale. The Assertion That
 // Changed Everything, "The Message" (the write into the pool that precedes decode
 // attention, and the fp8 cache the Triton path refused) and "Why This Message Was
 // Written" (the fp8_e4m3 cache dtype).

@@ -1,4 +1,4 @@
-// a6: grouped sparse prefill. G consecutive queries with H heads fill one 128-row tile
+// Grouped sparse prefill. G consecutive queries with H heads fill one 128-row tile
 // (G * H = 128); the tile walks its group's union once and each row keeps only the
 // entries whose membership bit names its query (vLLM PR 63104, "Overview": 2, 4 or 8
 // queries share a 128-head row; "Details": the union is gathered once with a mask per

@@ -1,4 +1,4 @@
-// a1: logical top-k indices + page table -> physical slots (the virtual block table of
+// Logical top-k indices + page table -> physical slots (the virtual block table of
 // page size 1 that decode walks). The Virtual Block Table: Reusing Triton MLA for Sparse
 // Attention on Blackwell GPUs, "The Investigation" (slot formula) and "Assumptions and
 // Reasoning", Assumption 1 (page size 1).

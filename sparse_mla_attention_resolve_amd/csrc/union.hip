@@ -1,4 +1,4 @@
-// a5: per-group top-k union with membership bits (vLLM PR 63104, "Tests" for the edge
+// Per-group top-k union with membership bits (vLLM PR 63104, "Tests" for the edge
 // cases, "Changes" for unions of consecutive queries whose rows keep a bit per member,
 // "Details" for gathering the union once per 128-row tile).
 //

@@ -138,35 +138,35 @@ def _run_config(c):
     return results
 
 
-def test_config1_tiny_fp32():
-    c = gc.config("config1")
+def test_decode_tiny_f32_tiny_fp32():
+    c = gc.config("decode_tiny_f32")
     for out, lse, o, l, what in _run_config(c):
-        _check(out, lse, o, l, BF16_ATOL, BF16_RTOL, "config1 " + what, f32=True)
+        _check(out, lse, o, l, BF16_ATOL, BF16_RTOL, "decode_tiny_f32 " + what, f32=True)
 
 
-def test_config2_bf16():
-    c = gc.config("config2")
+def test_decode_bf16_b32_bf16():
+    c = gc.config("decode_bf16_b32")
     for out, lse, o, l, what in _run_config(c):
-        _check(out, lse, o, l, BF16_ATOL, BF16_RTOL, "config2 " + what)
+        _check(out, lse, o, l, BF16_ATOL, BF16_RTOL, "decode_bf16_b32 " + what)
 
 
-def test_config3_ragged():
-    c = gc.config("config3")
+def test_decode_ragged_b128_ragged():
+    c = gc.config("decode_ragged_b128")
     res = _run_config(c)
     assert len(res) == 2
     for out, lse, o, l, what in res:
-        _check(out, lse, o, l, BF16_ATOL, BF16_RTOL, "config3 " + what)
+        _check(out, lse, o, l, BF16_ATOL, BF16_RTOL, "decode_ragged_b128 " + what)
 
 
-def test_config5_fp8():
-    c = gc.config("config5")
+def test_decode_fp8_b64_fp8():
+    c = gc.config("decode_fp8_b64")
     for out, lse, o, l, what in _run_config(c):
-        _check(out, lse, o, l, FP8_ATOL, BF16_RTOL, "config5 " + what)
+        _check(out, lse, o, l, FP8_ATOL, BF16_RTOL, "decode_fp8_b64 " + what)
 
 
 def test_decode_graph_replay():
     """resolve + decode captured in a HIP graph; every replay matches the eager result."""
-    c = wl.config2(T=8)
+    c = wl.decode_bf16_b32(T=8)
     lay = c.layout
     kv, _ = gc.gpu_pool(smla, lay, c.rows, "bf16")
     qt = gc.q_tensor(c.q, "bf16")

@@ -59,8 +59,8 @@ def test_kv_write_bits(kv_dtype, src_dtype):
         assert torch.isnan(stor[torch.from_numpy(others)].float()).all()
 
 
-def test_kv_write_fp8_config5_codes():
-    c = wl.config5(T=8)
+def test_kv_write_fp8_b64_codes():
+    c = wl.decode_fp8_b64(T=8)
     kv, smap = gc.gpu_pool(smla, c.layout, c.rows, "fp8")
     pool, osl = gc.oracle_pool(c.layout, c.rows, "fp8")
     assert np.array_equal(smap.cpu().numpy(), osl)

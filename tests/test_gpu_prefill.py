@@ -52,8 +52,8 @@ def test_prefill_small(Q, H, G):
         assert gc.rel_l2(o[1], ob[0]) > 0.05
 
 
-def test_prefill_config4_sampled():
-    c = gc.config("config4")
+def test_prefill_grouped_q8192_sampled():
+    c = gc.config("prefill_grouped_q8192")
     lay = c.layout
     kv, smap = gc.gpu_pool(smla, lay, c.rows, "bf16")
     pool, osl = gc.oracle_pool(lay, c.rows, "bf16")
@@ -69,6 +69,6 @@ def test_prefill_config4_sampled():
     assert np.array_equal(lens.cpu().numpy(), lens_o)
     o_ref, l_ref = oracle.grouped_prefill(c.q, pool, enc_o, lens_o, c.G, c.scale, queries=sample)
     o = out[torch.from_numpy(sample).cuda()].float().cpu().numpy()
-    gc.assert_close(o, o_ref, 2e-2, 1e-2, "config4 out")
-    gc.assert_lse(lse[torch.from_numpy(sample).cuda()].cpu().numpy(), l_ref, 1e-3, "config4 lse")
+    gc.assert_close(o, o_ref, 2e-2, 1e-2, "prefill_grouped_q8192 out")
+    gc.assert_lse(lse[torch.from_numpy(sample).cuda()].cpu().numpy(), l_ref, 1e-3, "prefill_grouped_q8192 lse")
     assert gc.rel_l2(o, o_ref) <= 1e-2

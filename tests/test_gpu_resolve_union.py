@@ -62,13 +62,13 @@ def test_resolve_strided_rows():
     assert np.all(o[:, :8] == 12345) and np.all(o[:, 48:] == 12345)
 
 
-@pytest.mark.parametrize("cfg", ["config2", "config4"])
+@pytest.mark.parametrize("cfg", ["decode_bf16_b32", "prefill_grouped_q8192"])
 def test_resolve_config(cfg):
-    if cfg == "config2":
-        c = gc.config("config2")
+    if cfg == "decode_bf16_b32":
+        c = gc.config("decode_bf16_b32")
         idx, req, valid = c.idx, c.tok_req, c.valid
     else:
-        c = wl.config4(Q=2048, cached=16384)
+        c = wl.prefill_grouped_q8192(Q=2048, cached=16384)
         idx, req, valid = c.idx, np.zeros(c.idx.shape[0], np.int32), c.valid
     lay = c.layout
     got = smla.smla_resolve_slots(_t(idx), _t(valid), _t(req), _t(lay.page_table), _t(lay.ctx), lay.page_size)
@@ -136,8 +136,8 @@ def test_union_24bit_rows():
     _compare_union(enc_g, lens_g, enc_o, lens_o)
 
 
-def test_union_config4():
-    c = gc.config("config4")
+def test_union_prefill_grouped_q8192():
+    c = gc.config("prefill_grouped_q8192")
     lay = c.layout
     sl = oracle.resolve_slots(c.idx, c.valid, np.zeros(len(c.idx), np.int32), lay.page_table, lay.ctx, lay.page_size)
     enc_g, lens_g = _union_gpu(sl, c.valid, 2, lay.num_slots)

@@ -5,16 +5,16 @@ import workloads as wl
 import oracle
 
 
-def test_config1_shapes():
-    c = wl.config1()
+def test_decode_tiny_f32_shapes():
+    c = wl.decode_tiny_f32()
     assert c.q.shape == (1, 16, 576) and c.q.dtype == np.float32
     assert c.idx.shape == (1, 256) and len(np.unique(c.idx)) == 256
     assert c.idx.min() >= 0 and c.idx.max() < 1024
     assert c.rows.values.shape == (256, 576)
 
 
-def test_config2_structure():
-    c = wl.config2()
+def test_decode_bf16_b32_structure():
+    c = wl.decode_bf16_b32()
     assert c.q.shape == (32, 64, 576) and c.q.dtype == np.uint16
     assert np.all((c.layout.ctx >= 8192) & (c.layout.ctx <= 32768))
     assert c.layout.num_slots == 1 << 20
@@ -26,8 +26,8 @@ def test_config2_structure():
     assert len(c.rows.pos) == 32 * 2048
 
 
-def test_config3_structure():
-    c = wl.config3(T=24)
+def test_decode_ragged_b128_structure():
+    c = wl.decode_ragged_b128(T=24)
     assert np.array_equal(c.valid, np.minimum(c.layout.ctx, 2048))
     for t in range(24):
         v = c.valid[t]
@@ -36,8 +36,8 @@ def test_config3_structure():
     assert len(c.dense_tokens) == round(0.1 * 24)
 
 
-def test_config4_overlap():
-    c = wl.config4(Q=256, cached=4096)
+def test_prefill_grouped_q8192_overlap():
+    c = wl.prefill_grouped_q8192(Q=256, cached=4096)
     assert c.idx.shape == (256, 2048)
     for qi in range(256):
         assert len(np.unique(c.idx[qi])) == 2048
@@ -47,12 +47,12 @@ def test_config4_overlap():
     assert 1.2 < ratio < 1.3     # 1434 shared + 2 * 614 own, less own picks that collide
 
 
-def test_config5_structure():
-    c = wl.config5(T=4, ctx_len=65536)
+def test_decode_fp8_b64_structure():
+    c = wl.decode_fp8_b64(T=4, ctx_len=65536)
     assert c.kv_dtype == "fp8" and c.rows.values.dtype == np.float32
     assert c.layout.num_slots == 4 * 65536
 
 
 def test_seeded():
-    a, b = wl.config2(T=4), wl.config2(T=4)
+    a, b = wl.decode_bf16_b32(T=4), wl.decode_bf16_b32(T=4)
     assert np.array_equal(a.idx, b.idx) and np.array_equal(a.q, b.q)

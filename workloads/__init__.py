@@ -138,7 +138,7 @@ def _normal(rng, shape, scale):
     return x
 
 
-def config1(seed: int = 1) -> DecodeCase:
+def decode_tiny_f32(seed: int = 1) -> DecodeCase:
     """Tiny fp32 decode: 1 query token, 16 heads, a 4096-slot pool, context 1024,
     256 unique indices, identity page table."""
     rng = np.random.default_rng(seed)
@@ -157,7 +157,7 @@ def config1(seed: int = 1) -> DecodeCase:
                       rows, np.zeros(0, np.int32))
 
 
-def config2(seed: int = 2, T: int = 32) -> DecodeCase:
+def decode_bf16_b32(seed: int = 2, T: int = 32) -> DecodeCase:
     """bf16 decode: batch 32, 64 heads, contexts U[8K, 32K], 2^20-slot pool in
     64-slot pages dealt from a permutation, 2048 unique causal indices per query."""
     rng = np.random.default_rng(seed)
@@ -174,7 +174,7 @@ def config2(seed: int = 2, T: int = 32) -> DecodeCase:
                       np.zeros(0, np.int32))
 
 
-def config3(seed: int = 3, T: int = 128) -> DecodeCase:
+def decode_ragged_b128(seed: int = 3, T: int = 128) -> DecodeCase:
     """Ragged bf16 decode: batch 128, contexts U[128, 16K], lists of 2048 padded with -1
     (valid = min(ctx, 2048)); 10% of requests attend to their whole context through the
     page table instead."""
@@ -197,7 +197,7 @@ def config3(seed: int = 3, T: int = 128) -> DecodeCase:
                       q, layout, tok_req, idx, valid, rows, dense)
 
 
-def config5(seed: int = 5, T: int = 64, ctx_len: int = 65536) -> DecodeCase:
+def decode_fp8_b64(seed: int = 5, T: int = 64, ctx_len: int = 65536) -> DecodeCase:
     """fp8-KV decode: batch 64, 64 heads, context 64K each, 2048 unique indices;
     `rows.values` is the float32 cache write source (latent and rope ~ N(0,1))."""
     rng = np.random.default_rng(seed)
@@ -227,7 +227,7 @@ class PrefillCase:
     rows: LogicalRows       # bf16 bits, every position of the request
 
 
-def config4(seed: int = 4, Q: int = 8192, cached: int = 16384, H: int = 64, G: int = 2,
+def prefill_grouped_q8192(seed: int = 4, Q: int = 8192, cached: int = 16384, H: int = 64, G: int = 2,
             shared_frac: float = 0.7, W: int = TOPK) -> PrefillCase:
     """Grouped prefill: Q new query tokens at positions cached+i on `cached` cached
     tokens; each query has W causal indices, ~70% shared with its group partners
