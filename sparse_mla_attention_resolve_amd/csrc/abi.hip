@@ -62,7 +62,28 @@ smla_status check_kv(const smla_kv& kv, const char* fn, bool for_write) {
   return SMLA_OK;
 }
 
-// Split count and rows per split, from scalar arguments only.
+// Compute units of the current device (256 on MI355X); the fallback keeps host-only
+// callers (workspace queries without a GPU) deterministic.
+int32_t device_cus() {
+  static int32_t cached[64] = {};           // per device id; a racing first query writes the same value
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
+
+// Split count and rows per split, from the scalar arguments and the device's compute-unit
+// count. A stage-1 workgroup fills a compute unit (its LDS ring), so the default gives
+// every compute unit one (token, split) and no second round: floor(CUs / T) splits per
+// token, at least enough for the per-split row limit.
 void plan_splits(int32_t T, int32_t max_len, int32_t requested, int32_t* S_out, int32_t* R_out) {
   const int32_t chunk = smla::kChunk;
   const int32_t max_chunks = (max_len + chunk - 1) / chunk;
@@ -70,12 +91,10 @@ void plan_splits(int32_t T, int32_t max_len, int32_t requested, int32_t* S_out, 
   if (requested > 0) {
     S = requested;
   } else {
-    // about 256 rows per split; more splits when there are too few tokens to give every
-    // compute unit a workgroup
-    S = (max_len + 255) / 256;
-    const int32_t want_wgs = 256;
     const int32_t Tq = T > 0 ? T : 1;
-    if ((int64_t)Tq * S < want_wgs) S = (want_wgs + Tq - 1) / Tq;
+    S = device_cus() / Tq;
+    const int32_t need = (max_len + smla::kMaxSplitRows - 1) / smla::kMaxSplitRows;
+    if (S < need) S = need;
   }
   if (S > max_chunks) S = max_chunks;
   if (S > 256) S = 256;

@@ -33,7 +33,8 @@ struct Stage1Args {
   const int32_t* table;
   int64_t table_stride;
   const int32_t* lens;
-  int32_t max_len;
+  int32_t max_len;          // table_width * page size
+  int32_t table_width;
   int32_t log2_page;
   float scale_log2;         // softmax scale * log2(e): scores are kept in base 2
   int32_t rows_per_split;
@@ -76,7 +77,7 @@ struct Lay<SMLA_BF16> {
 template <>
 struct Lay<SMLA_FP8_E4M3> {
   static constexpr int kUnits = 40;      // 512 e4m3 codes + 64 bf16 rotary values; scales live apart
-  static constexpr int kNBuf = 6;
+  static constexpr int kNBuf = 7;
 };
 
 __device__ __forceinline__ int swz(int row, int unit) { return unit ^ ((row >> 1) & 7); }
@@ -106,6 +107,13 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
 }
 
+// 4-byte direct-to-LDS copy: lane l's word at `src` lands at lds_wave_base + 4 l.
+__device__ __forceinline__ void dma4(const void* src, char* lds_wave_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base);
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory");
+}
+
 // Wait until at most `chunks` chunks of `LOADS` gathers each are still in flight.
 template <int MAXC, int LOADS>
 __device__ __forceinline__ void wait_chunks(int chunks) {
@@ -119,6 +127,7 @@ __device__ __forceinline__ void wait_chunks(int chunks) {
 
 constexpr int kS1Threads = 512;   // 8 waves, two per SIMD: one waits on LDS while the other computes
 constexpr int kLoaders = 4;       // waves 0..3 issue the gathers
+constexpr int kQLoads = 64 * 72 / 64 / kLoaders;   // 16-byte q copies per loader lane (64 heads x 72 units)
 
 // Workgroup id -> (token, split). Workgroups are dispatched to the 8 XCDs round robin;
 // when T is a multiple of 8 every split of a token runs on one XCD, so the token's partial
@@ -147,6 +156,7 @@ __global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a
   __shared__ float xmax[2][kHeads];
   __shared__ float xsum[2][kHeads];
   __shared__ int32_t slot_s[kMaxSplitRows];
+  __shared__ int32_t page_s[kMaxSplitRows / 2 + 64];     // page ids of a split (page size >= 2)
   __shared__ float scale_s[KV == SMLA_FP8_E4M3 ? kMaxSplitRows : 1];
 
   int t, s;
@@ -158,32 +168,63 @@ __global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a
   const int x = w >> 2;       // scores: chunk rows 16x .. 16x+15; P V: columns 256x .. 256x+255
   const int h0 = 16 * hq;
 
-  const int len = token_len(a, t);
+  const int lp = a.log2_page;
   const int r0 = s * a.rows_per_split;
-  if (r0 >= len) return;                      // inactive split: stage 2 never reads it
+  const int len = token_len(a, t);             // a scalar load; used once the gathers below are issued
+  const bool loader = w < kLoaders;
+
+  // ---- prologue. The loader waves copy the split's table entries and the token's q rows
+  // straight into LDS, so that no register has to wait for memory before the first gathers
+  // go out: entries table[t][e0 .. e0 + n_ent) (slots when the page size is 1, page ids
+  // otherwise) into slot_s / page_s, and q[t] (64 x 576 bf16) into ring slots 2.. (free
+  // until the chunk gathers reach them).
+  const int32_t* trow = a.table + (int64_t)t * a.table_stride;
+  const int e0 = r0 >> lp;
+  const int n_ent = lp == 0 ? min(a.rows_per_split, a.max_len - r0)
+                            : min((r0 + a.rows_per_split - 1) >> lp, a.table_width - 1) - e0 + 1;
+  char* const qlds = kvbuf[2];
+  static_assert((kNBuf - 2) * kChunkBytes >= kHeads * kRow * 2, "q must fit the ring slots from 2 on");
+  if (loader) {
+    int32_t* ent = lp == 0 ? slot_s : page_s;
+    for (int k = w; k * 64 < n_ent; k += kLoaders) {
+      const int e = k * 64 + lane;
+      dma4(e < n_ent ? (const void*)(trow + e0 + e) : (const void*)kZeroRow, (char*)(ent + k * 64));
+    }
+    const uint16_t* qt = a.q + (int64_t)t * a.q_tok_stride;
+#pragma unroll
+    for (int m = 0; m < kQLoads; ++m) {
+      const int j = w + kLoaders * m;            // 16-byte units 64 j .. 64 j + 63 of the [64][72] tile
+      const int u = 64 * j + lane, h = u / 72, k = u % 72;
+      dma16(qt + (int64_t)h * a.q_head_stride + 8 * k, qlds + 1024 * j);
+    }
+    wait_vmcnt<kQLoads>();                      // the entries (issued first) are in LDS
+  }
+  if (r0 >= len) {                              // inactive split: stage 2 never reads it
+    wait_vmcnt<0>();                            // no gather may land after the workgroup is gone
+    return;
+  }
   const int r1 = min(r0 + a.rows_per_split, len);
   const int nrows = r1 - r0;
   const int nchunks = (nrows + kChunk - 1) / kChunk;
+  lds_barrier();
 
-  // slots (and fp8 scales) of the split's rows; -1 marks a masked row
+  // slots of the split's rows; -1 marks a masked row (past the length, a negative entry or
+  // page id, or a slot outside the pool)
   for (int i = tid; i < nchunks * kChunk; i += kS1Threads) {
-    const int64_t sl = i < nrows ? slot_of(a, t, r0 + i) : -1;
-    slot_s[i] = (int32_t)sl;
-    if constexpr (KV == SMLA_FP8_E4M3)
-      scale_s[i] = sl >= 0 ? *(const float*)((const char*)a.kv.scale + sl * a.kv.scale_stride) : 0.f;
+    int64_t sl = -1;
+    if (i < nrows) {
+      if (lp == 0) {
+        sl = slot_s[i];
+      } else {
+        const int p = r0 + i;
+        const int32_t page = page_s[(p >> lp) - e0];
+        sl = page < 0 ? -1 : ((int64_t)page << lp) + (p & ((1 << lp) - 1));
+      }
+      if (sl >= a.kv.num_slots) sl = -1;
+    }
+    slot_s[i] = sl < 0 ? -1 : (int32_t)sl;
   }
-
-  // q fragments (A operand of the scores): head h0 + c, dims 32ks + 8g .. +7
-  bf16x8 qf[18];
-  {
-    const uint16_t* qh = a.q + (int64_t)t * a.q_tok_stride + (int64_t)(h0 + c) * a.q_head_stride;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qh + ks * 32 + 8 * g));
-  }
-  // every plain load is done before the first gather is enqueued, so that the counter
-  // waits below count gathers only
-  wait_vmcnt<0>();
-  __syncthreads();
+  lds_barrier();
 
   // plane bases and strides as scalars (a per-lane choice between two fields of the
   // argument struct would otherwise become a memory load)
@@ -224,6 +265,29 @@ __global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a
     }
   };
 
+  // chunks 0 and 1 go out first (their ring slots hold no q); once q has landed every wave
+  // copies its fragments (A operand of the scores: head h0 + c, dims 32ks + 8g .. +7), and
+  // the slots q occupied take the next chunks
+  if (loader) {
+    for (int ci = 0; ci < 2 && ci < nchunks; ++ci) issue(ci);
+    wait_chunks<2, kLoads>(min(2, nchunks));    // q was issued before these chunks
+  }
+  lds_barrier();
+  bf16x8 qf[18];
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ((h0 + c) * 72 + 4 * ks + g) * 16));
+  lds_barrier();
+  if (loader) {
+    for (int ci = 2; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+  } else if constexpr (KV == SMLA_FP8_E4M3) {
+    // the other waves fetch the rows' scales meanwhile; the first barrier of the loop
+    // publishes them
+    for (int i = tid - kLoaders * 64; i < nchunks * kChunk; i += kS1Threads - kLoaders * 64) {
+      const int32_t sl = slot_s[i];
+      scale_s[i] = sl >= 0 ? *(const float*)((const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride) : 0.f;
+    }
+  }
+
   f32x4 oacc[16];
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -231,10 +295,6 @@ __global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a
 #pragma unroll
   for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }
   uint16_t* pw = pbuf[hq];
-  const bool loader = w < kLoaders;
-
-  if (loader)
-    for (int ci = 0; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
 
   for (int ci = 0; ci < nchunks; ++ci) {
     // chunk ci is in LDS once its loaders' gathers are done and every wave got here
@@ -484,68 +544,70 @@ struct Stage2Args {
   int32_t out_f32;
 };
 
-// One workgroup per token and 8 heads; thread = (head, 16 consecutive columns).
-__global__ void __launch_bounds__(256) decode_stage2(Stage2Args a) {
+// Thread = (token, head, 4 consecutive columns); a workgroup of 256 covers two heads. Every
+// split's LSE and 16-byte slice are loaded before any arithmetic, so a thread has all its
+// splits in flight at once (up to 8 per pass; more splits take further passes with a
+// running maximum).
+constexpr int kS2Threads = 256;
+constexpr int kS2Batch = 8;
+__global__ void __launch_bounds__(kS2Threads) decode_stage2(Stage2Args a) {
   // same token -> XCD rule as stage 1, so that the partials come from this XCD's L2
-  const int hg_count = (a.H + 7) / 8;
-  int t, hg;
+  const int hp_count = (a.H + 1) / 2;
+  int t, hp;
   if ((a.T & 7) == 0) {
     const int i = blockIdx.x >> 3;
-    t = (blockIdx.x & 7) + 8 * (i / hg_count);
-    hg = i % hg_count;
+    t = (blockIdx.x & 7) + 8 * (i / hp_count);
+    hp = i % hp_count;
   } else {
-    t = blockIdx.x / hg_count;
-    hg = blockIdx.x % hg_count;
+    t = blockIdx.x / hp_count;
+    hp = blockIdx.x % hp_count;
   }
-  const int h = hg * 8 + (threadIdx.x >> 5);
-  const int c0 = (threadIdx.x & 31) * 16;
+  const int h = hp * 2 + (threadIdx.x >> 7);
+  const int c0 = (threadIdx.x & 127) * 4;
   if (h >= a.H) return;
   int len = a.lens[t];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
   const int nact = min(a.S, (len + a.rows_per_split - 1) / a.rows_per_split);
   const int64_t base = (int64_t)t * a.S;
-  float mx = -INFINITY;
-  for (int s = 0; s < nact; ++s) mx = fmaxf(mx, a.part_lse[(base + s) * a.H + h]);
-  float acc[16];
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  float wsum = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < nact; ++s) {
-      const float l = a.part_lse[(base + s) * a.H + h];
-      if (l == -INFINITY) continue;
-      const float wgt = expf(l - mx);
-      wsum += wgt;
-      const float4* src = (const float4*)(a.part_o + ((base + s) * a.H + h) * kLatent + c0);
+  float mx = -INFINITY, wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < nact; s0 += kS2Batch) {
+    float l[kS2Batch];
+    float4 o[kS2Batch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 v = src[i];
-        acc[4 * i] += wgt * v.x;
-        acc[4 * i + 1] += wgt * v.y;
-        acc[4 * i + 2] += wgt * v.z;
-        acc[4 * i + 3] += wgt * v.w;
-      }
+    for (int j = 0; j < kS2Batch; ++j) {
+      const bool in = s0 + j < nact;
+      const int64_t ps = (base + s0 + (in ? j : 0)) * a.H + h;
+      l[j] = in ? a.part_lse[ps] : -INFINITY;
+      o[j] = in ? *(const float4*)(a.part_o + ps * kLatent + c0) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float bm = mx;
+#pragma unroll
+    for (int j = 0; j < kS2Batch; ++j) bm = fmaxf(bm, l[j]);
+    if (bm == -INFINITY) continue;                   // nothing but empty splits so far
+    const float r = expf(mx - bm);                   // 0 on the first non-empty pass
+    wsum *= r;
+    acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
+#pragma unroll
+    for (int j = 0; j < kS2Batch; ++j) {
+      const float wgt = l[j] == -INFINITY ? 0.f : expf(l[j] - bm);
+      wsum += wgt;
+      acc.x += wgt * o[j].x; acc.y += wgt * o[j].y; acc.z += wgt * o[j].z; acc.w += wgt * o[j].w;
+    }
+    mx = bm;
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   if (a.out_f32) {
     float* o = (float*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)h * a.out_head_stride + c0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(float4*)(o + 4 * i) = make_float4(acc[4 * i] * inv, acc[4 * i + 1] * inv, acc[4 * i + 2] * inv,
-                                          acc[4 * i + 3] * inv);
+    *(float4*)o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   } else {
     uint16_t* o = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)h * a.out_head_stride + c0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      uint4 v;
-      v.x = pack_bf16x2(acc[8 * i] * inv, acc[8 * i + 1] * inv);
-      v.y = pack_bf16x2(acc[8 * i + 2] * inv, acc[8 * i + 3] * inv);
-      v.z = pack_bf16x2(acc[8 * i + 4] * inv, acc[8 * i + 5] * inv);
-      v.w = pack_bf16x2(acc[8 * i + 6] * inv, acc[8 * i + 7] * inv);
-      *(uint4*)(o + 8 * i) = v;
-    }
+    uint2 v;
+    v.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    v.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    *(uint2*)o = v;
   }
-  if (a.lse && (threadIdx.x & 31) == 0)
+  if (a.lse && (threadIdx.x & 127) == 0)
     a.lse[(int64_t)t * a.lse_tok_stride + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
@@ -563,6 +625,7 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   a.table_stride = d.table_stride;
   a.lens = d.lens;
   a.max_len = plan.max_len;
+  a.table_width = d.table_width;
   int log2_page = 0;
   while ((1 << log2_page) < d.page_size) ++log2_page;
   a.log2_page = log2_page;
@@ -601,7 +664,7 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   b.lse = d.lse;
   b.lse_tok_stride = d.lse_tok_stride;
   b.out_f32 = d.q_dtype == SMLA_F32;
-  hipLaunchKernelGGL(decode_stage2, dim3(d.T * ((d.H + 7) / 8)), dim3(256), 0, stream, b);
+  hipLaunchKernelGGL(decode_stage2, dim3(d.T * ((d.H + 1) / 2)), dim3(kS2Threads), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ namespace smla {
 // Rows of one stage-1 chunk (the unit of gather, MFMA and online-softmax update).
 constexpr int kChunk = 32;
 // Most rows one stage-1 split may hold (its slot list is staged in LDS).
-constexpr int kMaxSplitRows = 512;
+constexpr int kMaxSplitRows = 1024;
 
 // Decode plan: everything the launches need, computed from scalar arguments only.
 struct DecodePlan {
