@@ -35,6 +35,36 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ["sparse_mla_attention_resolve_amd/csrc/decode.hip", "sparse_mla_attention_resolve_amd/csrc/smla_device.h",
+                  "sparse_mla_attention_resolve_amd/csrc/smla_internal.h"]
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernels_hbm_traffic.md")
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload`, as the committed rocprofv3 counter summary
+    records them (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel's reading), or None when
+    there is no such line or the decode kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read().split()
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    try:
+        recorded = text[text.index("source_sha256") + 1]
+    except (ValueError, IndexError):
+        return None
+    if recorded != h.hexdigest():
+        return None
+    for i, tok in enumerate(text):
+        if tok == "traffic_bytes_per_launch" and text[i + 1] == kernel and text[i + 2] == workload:
+            return int(text[i + 3])
+    return None
+
+
 def algorithmic_bytes(c, kv_dtype: str) -> dict:
     """Bytes the method must move for one decode step of case `c` (every row, q element,
     index and output read or written once). Split partials and repeated reads are not
@@ -194,6 +224,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with three plain 256 MiB fp32 copy kernels (y = x * 1), whose HBM counter "
+                         "readings give the scale for the decode kernels' FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (decode shards by request with no "
@@ -244,7 +277,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_stage1_mfma<bf16>", "achieved": s1_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": s1_gbs / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": ab["stage1"], "avg_launch_us": s1_ms * 1e3,
-                     "traffic": None},
+                     "traffic": measured_traffic("decode_stage1_mfma<bf16>", "bf16_batch_32")},
     }
 
     if not args.no_fp8:
@@ -270,6 +303,14 @@ def main():
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(c2, args.cpu_seconds)
+    if args.copy_calibration:
+        x = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            flush.sum()
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x (read 256 MiB, write 256 MiB)")
     print(json.dumps(line), flush=True)
 
 
