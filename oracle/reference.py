@@ -34,16 +34,19 @@ def resolve_slots(idx, valid, tok_req, page_table, seq_lens, page_size):
     slots before the decode kernel sees them.
 
     An entry resolves to -1 when it is padding or out of range: j >= valid[t] (the
-    per-token count of valid entries), a negative index, an index at or past the
-    request's context length, past the page-table row, or on a page whose id is < 0.
+    per-token count of valid entries), a token whose request is not a row of the page
+    table, a negative index, an index at or past the request's context length, past the
+    page-table row, or on a page whose id is < 0.
     """
     idx = np.asarray(idx, dtype=np.int64)
     T, W = idx.shape
     pt = np.asarray(page_table, dtype=np.int64)
-    req = np.asarray(tok_req, dtype=np.int64)[:, None]
+    req_raw = np.asarray(tok_req, dtype=np.int64)[:, None]
+    req_ok = (req_raw >= 0) & (req_raw < pt.shape[0])
+    req = np.where(req_ok, req_raw, 0)
     j = np.arange(W)[None, :]
     n = W if valid is None else np.asarray(valid, dtype=np.int64)[:, None]
-    ok = (j < n) & (idx >= 0) & (idx < np.asarray(seq_lens, dtype=np.int64)[req])
+    ok = req_ok & (j < n) & (idx >= 0) & (idx < np.asarray(seq_lens, dtype=np.int64)[req])
     page_no = np.where(ok, idx // page_size, 0)
     ok &= page_no < pt.shape[1]
     page = pt[req, np.minimum(page_no, pt.shape[1] - 1)]

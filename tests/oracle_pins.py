@@ -48,6 +48,7 @@ def check_resolve_bruteforce(ref, seed=0):
         pt = rng.integers(-1, 40, size=(R, maxp)).astype(np.int32)
         seq = rng.integers(0, maxp * P + 3, size=R).astype(np.int32)
         req = rng.integers(0, R, size=T).astype(np.int32)
+        req[1], req[3] = -1, R                      # tokens whose request is not in the table
         idx = rng.integers(-3, maxp * P + 5, size=(T, W)).astype(np.int32)
         valid = rng.integers(-1, W + 2, size=T).astype(np.int32)
         got = ref.resolve_slots(idx, valid, req, pt, seq, P)
@@ -55,7 +56,7 @@ def check_resolve_bruteforce(ref, seed=0):
             for j in range(W):
                 i, r = int(idx[t, j]), int(req[t])
                 want = -1
-                if j < valid[t] and 0 <= i < seq[r] and i // P < maxp and pt[r, i // P] >= 0:
+                if j < valid[t] and 0 <= r < R and 0 <= i < seq[r] and i // P < maxp and pt[r, i // P] >= 0:
                     want = int(pt[r, i // P]) * P + i % P
                 assert got[t, j] == want, (P, t, j, got[t, j], want)
         # no `valid` means every entry counts

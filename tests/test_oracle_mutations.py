@@ -19,7 +19,8 @@ MUTATIONS = [
     ("reference.py", "lse = m + np.log(z)", "lse = m - np.log(z)"),                         # sign of log
     ("reference.py", "p = np.exp(s - lse)", "p = np.exp(s - m)"),                           # unnormalised weights
     ("reference.py", "page * page_size + idx % page_size", "page * page_size + idx // page_size"),
-    ("reference.py", "ok = (j < n) &", "ok = (j <= n) &"),                                   # valid off by one
+    ("reference.py", "ok = req_ok & (j < n) &", "ok = req_ok & (j <= n) &"),                 # valid off by one
+    ("reference.py", "ok = req_ok & (j < n) &", "ok = (j < n) &"),                          # unknown request kept
     ("reference.py", "(idx < np.asarray(seq_lens, dtype=np.int64)[req])", "(idx <= np.asarray(seq_lens, dtype=np.int64)[req])"),
     ("reference.py", "page[keep] * page_size + p[keep] % page_size", "page[keep] * page_size + p[keep] % (page_size - 1)"),
     ("reference.py", "sel = row[:min(n, len(row))]", "sel = row[:len(row)]"),               # lens ignored
