@@ -3,8 +3,10 @@
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--cpu-seconds 15] [--no-cpu-baseline]
 
 A step is one pass of the decode hot path over one batch of seeded synthetic input:
-slot resolution (logical top-k -> physical slots, page size 1 table), stage 1 (split
+slot resolution (logical top-k -> physical slots through the page table), stage 1 (split
 gather + MFMA scores + online softmax + MFMA P*V) and stage 2 (LSE merge). The headline
+step runs the resolution inside stage 1 (smla_sparse_decode_topk); the two-kernel form
+(smla_resolve_slots, then decode over the slot table) is timed beside it. The headline
 workload is the bf16 batch of 32 requests x 64 heads, latent 512 + rope 64, contexts
 U[8K, 32K] in a 2^20-slot pool of 64-slot pages, top-k 2048. The inputs are resident in
 HBM when a timed step starts: before every timed step a 1 GiB buffer is read, so that
@@ -83,8 +85,9 @@ def algorithmic_bytes(c, kv_dtype: str) -> dict:
         row = c.idx[t][c.idx[t] >= 0]
         pages += len(np.unique(row // c.layout.page_size)) * 4
     return {"kv": kv, "q": q, "out": out, "lse": lse, "idx": idx, "page_table": pages,
-            "step": kv + q + out + lse + idx + pages,      # resolved slots stay on chip in an ideal fusion
-            "stage1": kv + q + slots}
+            "step": kv + q + out + lse + idx + pages,      # resolved slots stay on chip (fused stage 1)
+            "stage1": kv + q + idx + pages,                # stage 1 resolving the indices itself
+            "stage1_slots": kv + q + slots}                # stage 1 over resolved slots
 
 
 def setup_decode(c, smla, torch):
@@ -110,36 +113,56 @@ def setup_decode(c, smla, torch):
         "lse": torch.empty((T, H), dtype=torch.float32, device=dev),
     }
     st["call"] = smla.DecodeCall(st["q"], kv, st["slots"], st["valid"], 1, c.scale, st["out"], st["lse"])
+    # the fused form: stage 1 resolves the logical indices through the page table itself
+    st["fused"] = smla.DecodeCall(st["q"], kv, st["idx"], st["valid"], 1, c.scale, st["out"], st["lse"],
+                                  page_map=(st["req"], st["pt"], st["ctx"], lay.page_size))
     torch.cuda.synchronize()
     return st
 
 
 def time_decode(c, smla, torch, steps, warmup, flush):
+    """Cold steps (a 1 GiB read before each) of the fused step (stage 1 with in-kernel slot
+    resolution, then stage 2) with per-kernel events, the same for the two-kernel form
+    (smla_resolve_slots, then stage 1 over the resolved slots, then stage 2), and warm /
+    graph-replay figures of the fused step."""
     st = setup_decode(c, smla, torch)
     lay = c.layout
-    call = st["call"]
+    fused, call = st["fused"], st["call"]
 
     def resolve():
         smla.smla_resolve_slots(st["idx"], st["valid"], st["req"], st["pt"], st["ctx"], lay.page_size, slots=st["slots"])
 
     def step():
-        resolve()
-        call()
+        fused()
 
     for _ in range(warmup):
         flush.sum()
         step()
+        flush.sum()
+        resolve()
+        call()
     torch.cuda.synchronize()
 
     # cold steps: the flush runs between steps, outside the events. Python's collector is
     # off meanwhile, so that a collection cannot stall the host between two launches.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     gc.disable()
     wall0 = time.perf_counter()
     for k in range(steps):
         flush.sum()                       # reads 1 GiB: evicts the caches, leaves nothing dirty
         e = ev[k]
+        e[0].record()
+        fused.stage1()
+        e[1].record()
+        fused.stage2()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    for k in range(steps):
+        flush.sum()
+        e = ev2[k]
         e[0].record()
         resolve()
         e[1].record()
@@ -148,12 +171,14 @@ def time_decode(c, smla, torch, steps, warmup, flush):
         call.stage2()
         e[3].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     gc.enable()
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
-    res_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    s1_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    s2_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in ev])
+    s1_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    s2_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    two = {"step_ms": np.array([e[0].elapsed_time(e[3]) for e in ev2]),
+           "resolve_ms": np.array([e[0].elapsed_time(e[1]) for e in ev2]),
+           "stage1_ms": np.array([e[1].elapsed_time(e[2]) for e in ev2]),
+           "stage2_ms": np.array([e[2].elapsed_time(e[3]) for e in ev2])}
 
     # warm steps: back to back, no flush
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -185,8 +210,8 @@ def time_decode(c, smla, torch, steps, warmup, flush):
         graph_ms = e0.elapsed_time(e1) / steps
     except Exception as ex:  # graph capture is a report-only extra
         log(f"graph capture skipped: {ex}")
-    return {"step_ms": step_ms, "resolve_ms": res_ms, "stage1_ms": s1_ms, "stage2_ms": s2_ms,
-            "warm_ms": warm_ms, "graph_ms": graph_ms, "wall_s": wall, "splits": call.splits}
+    return {"step_ms": step_ms, "stage1_ms": s1_ms, "stage2_ms": s2_ms, "two_kernel": two,
+            "warm_ms": warm_ms, "graph_ms": graph_ms, "wall_s": wall, "splits": fused.splits}
 
 
 def cpu_baseline(c, seconds: float) -> dict:
@@ -253,27 +278,35 @@ def main():
     value = T / (step_ms / 1e3)
     s1_gbs = ab["stage1"] / (s1_ms / 1e3) / 1e9
     step_gbs = ab["step"] / (step_ms / 1e3) / 1e9
-    log(f"step {step_ms*1e3:.1f} us (resolve {r['resolve_ms'].mean()*1e3:.1f}, stage1 {s1_ms*1e3:.1f}, "
-        f"stage2 {r['stage2_ms'].mean()*1e3:.1f}); warm {r['warm_ms']*1e3:.1f} us; graph "
-        f"{(r['graph_ms'] or 0)*1e3:.1f} us; stage1 {s1_gbs:.0f} GB/s")
+    two = r["two_kernel"]
+    log(f"step {step_ms*1e3:.1f} us (stage1 with in-kernel resolution {s1_ms*1e3:.1f}, stage2 "
+        f"{r['stage2_ms'].mean()*1e3:.1f}); warm {r['warm_ms']*1e3:.1f} us; graph {(r['graph_ms'] or 0)*1e3:.1f} us; "
+        f"stage1 {s1_gbs:.0f} GB/s. Two-kernel form: {two['step_ms'].mean()*1e3:.1f} us (resolve "
+        f"{two['resolve_ms'].mean()*1e3:.1f}, stage1 {two['stage1_ms'].mean()*1e3:.1f}, stage2 "
+        f"{two['stage2_ms'].mean()*1e3:.1f})")
+
+    def us(a):
+        return float(np.mean(a)) * 1e3
 
     line = {
         "metric": METRIC, "value": value, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "sparse MLA decode, bf16 q and KV, batch 32, 64 heads, latent 512 + rope 64, "
-                               "contexts U[8K,32K], 2^20-slot pool of 64-slot pages, top-k 2048, step = resolve + "
-                               "split decode + LSE merge, inputs HBM-resident (1 GiB read before each step)",
+                               "contexts U[8K,32K], 2^20-slot pool of 64-slot pages, top-k 2048; step = slot "
+                               "resolution + split decode (stage 1, resolving in-kernel) + LSE merge (stage 2); "
+                               "inputs HBM-resident (1 GiB read before each step)",
                    "batch": T, "heads": 64, "topk": 2048, "splits": r["splits"], "parallelism": "none (1 GPU)"},
         "hbm_gbs_step": step_gbs, "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_step": ab["step"],
         "timing_us": {"step_median": float(np.median(r["step_ms"])) * 1e3,
                       "step_p10": float(np.percentile(r["step_ms"], 10)) * 1e3,
                       "step_p90": float(np.percentile(r["step_ms"], 90)) * 1e3,
-                      "resolve": float(r["resolve_ms"].mean()) * 1e3, "stage1": s1_ms * 1e3,
-                      "stage2": float(r["stage2_ms"].mean()) * 1e3,
+                      "stage1": s1_ms * 1e3, "stage2": us(r["stage2_ms"]),
                       "warm_step": r["warm_ms"] * 1e3,
-                      "graph_replay_step": None if r["graph_ms"] is None else r["graph_ms"] * 1e3},
+                      "graph_replay_step": None if r["graph_ms"] is None else r["graph_ms"] * 1e3,
+                      "two_kernel_form": {"step": us(two["step_ms"]), "resolve": us(two["resolve_ms"]),
+                                          "stage1": us(two["stage1_ms"]), "stage2": us(two["stage2_ms"])}},
         "roofline": {"bound": "hbm", "kernel": "decode_stage1_mfma<bf16>", "achieved": s1_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": s1_gbs / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": ab["stage1"], "avg_launch_us": s1_ms * 1e3,
@@ -288,17 +321,20 @@ def main():
         r5 = time_decode(c5, smla, torch, args.steps, args.warmup, flush)
         ms5 = float(r5["step_ms"].mean())
         s15 = float(r5["stage1_ms"].mean())
+        two5 = r5["two_kernel"]
         line["fp8_kv_decode"] = {
             "workload": "batch 64, 64 heads, fp8 e4m3 latent + bf16 rope + fp32 scale per row, context 64K, top-k 2048",
             "queries_per_s": c5.q.shape[0] / (ms5 / 1e3), "ms_per_step": ms5,
             "hbm_gbs_step": ab5["step"] / (ms5 / 1e3) / 1e9,
             "stage1_gbs": ab5["stage1"] / (s15 / 1e3) / 1e9, "stage1_us": s15 * 1e3,
-            "resolve_us": float(r5["resolve_ms"].mean()) * 1e3, "stage2_us": float(r5["stage2_ms"].mean()) * 1e3,
+            "stage2_us": us(r5["stage2_ms"]),
             "step_median_us": float(np.median(r5["step_ms"])) * 1e3,
             "stage1_frac": ab5["stage1"] / (s15 / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "warm_step_us": r5["warm_ms"] * 1e3, "splits": r5["splits"]}
-        log(f"fp8: step {ms5*1e3:.1f} us (median {np.median(r5['step_ms'])*1e3:.1f}; resolve "
-            f"{r5['resolve_ms'].mean()*1e3:.1f}, stage1 {s15*1e3:.1f}, stage2 {r5['stage2_ms'].mean()*1e3:.1f})")
+            "warm_step_us": r5["warm_ms"] * 1e3, "splits": r5["splits"],
+            "two_kernel_form_us": {"step": us(two5["step_ms"]), "resolve": us(two5["resolve_ms"]),
+                                   "stage1": us(two5["stage1_ms"]), "stage2": us(two5["stage2_ms"])}}
+        log(f"fp8: step {ms5*1e3:.1f} us (median {np.median(r5['step_ms'])*1e3:.1f}; stage1 {s15*1e3:.1f}, stage2 "
+            f"{r5['stage2_ms'].mean()*1e3:.1f}); two-kernel form {us(two5['step_ms']):.1f} us")
 
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 1
+#define SMLA_ABI_VERSION 2
 
 #define SMLA_LATENT 512          /* latent (value) columns of a cache row */
 #define SMLA_ROPE 64             /* rotary columns of a cache row */
@@ -183,6 +183,44 @@ smla_status smla_sparse_decode_stage2(const smla_decode_args* args, void* worksp
                                       void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Sparse decode straight from logical top-k indices: slot resolution fused into the
+ * decode.
+ *
+ * The indexer's top-k entries are request-relative positions; smla_resolve_slots turns
+ * them into the page size 1 table that smla_sparse_decode walks (The Virtual Block Table,
+ * "The Investigation" and "The Breakthrough"). Here stage 1 resolves each entry itself,
+ * through `map`, with exactly the rule of smla_resolve_slots, so the results are bitwise
+ * those of smla_resolve_slots followed by smla_sparse_decode with page_size 1, without
+ * the intermediate slot array or its kernel.
+ *
+ *   args       as for smla_sparse_decode, with page_size == 1, `table` = the logical
+ *              indices idx [T, table_width] (row stride table_stride) and `lens` = the
+ *              valid counts (entries j >= lens[t] are padding). bf16 q only.
+ *   map        tok_req [T] (request of each token), page_table [R, pt_width] (row stride
+ *              pt_stride, page ids), seq_lens [R], page_size P (power of two, 1 .. 2^20):
+ *              position i of request r is slot page_table[r, i / P] * P + i % P when
+ *              0 <= r < R, 0 <= i < seq_lens[r], i / P < pt_width and that page id >= 0;
+ *              otherwise the entry is masked.
+ * The workspace is the one smla_sparse_decode_workspace reports for `args`.
+ * smla_sparse_decode_topk_stage1 is stage 1 alone; smla_sparse_decode_stage2 with the
+ * same args and workspace finishes it.
+ * ------------------------------------------------------------------------------- */
+typedef struct {
+  const int32_t* tok_req;
+  const int32_t* page_table; int64_t pt_stride;   /* elements, >= pt_width */
+  const int32_t* seq_lens;
+  int32_t R;                 /* requests (>= 1) */
+  int32_t pt_width;          /* pages per page-table row (>= 1) */
+  int32_t page_size;         /* P */
+  int32_t reserved0;         /* must be 0 */
+} smla_page_map;
+
+smla_status smla_sparse_decode_topk(const smla_decode_args* args, const smla_page_map* map, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+smla_status smla_sparse_decode_topk_stage1(const smla_decode_args* args, const smla_page_map* map,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Group top-k union with per-query membership bits.
  *
  * Queries are grouped G at a time in order (group g = queries gG .. min(gG+G, Q)-1; the
@@ -270,6 +308,7 @@ int32_t smla_abi_version(void);
 int32_t smla_sizeof_kv(void);
 int32_t smla_sizeof_decode_args(void);
 int32_t smla_sizeof_prefill_args(void);
+int32_t smla_sizeof_page_map(void);
 
 #ifdef __cplusplus
 }

@@ -157,7 +157,8 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   plan->H = a->H;
   plan->max_len = (int32_t)max_len;
   plan_splits(a->T, (int32_t)max_len, a->num_splits, &plan->S, &plan->rows_per_split);
-  plan->part_o_bytes = (size_t)a->T * plan->S * a->H * SMLA_LATENT * sizeof(float);
+  // the bf16 path keeps its partial outputs in bf16, the fp32 path in fp32
+  plan->part_o_bytes = (size_t)a->T * plan->S * a->H * SMLA_LATENT * (bf16 ? 2 : 4);
   plan->part_lse_bytes = (size_t)a->T * plan->S * a->H * sizeof(float);
   plan->ws_bytes = (plan->part_o_bytes + plan->part_lse_bytes + 255) / 256 * 256;
   return SMLA_OK;
@@ -186,6 +187,7 @@ int32_t smla_abi_version(void) { return SMLA_ABI_VERSION; }
 int32_t smla_sizeof_kv(void) { return (int32_t)sizeof(smla_kv); }
 int32_t smla_sizeof_decode_args(void) { return (int32_t)sizeof(smla_decode_args); }
 int32_t smla_sizeof_prefill_args(void) { return (int32_t)sizeof(smla_prefill_args); }
+int32_t smla_sizeof_page_map(void) { return (int32_t)sizeof(smla_page_map); }
 
 smla_status smla_resolve_slots(const int32_t* idx, int64_t idx_stride, const int32_t* valid,
                                const int32_t* tok_req, int32_t R, const int32_t* page_table,
@@ -230,17 +232,40 @@ smla_status smla_sparse_decode_splits(const smla_decode_args* args, int32_t* num
   return ok();
 }
 
+static smla_status check_page_map(const smla_decode_args* args, const smla_page_map* m) {
+  const char* fn = "smla_sparse_decode_topk";
+  CHECK(m != nullptr, SMLA_ERR_NULL, "%s: map is NULL", fn);
+  CHECK(m->reserved0 == 0, SMLA_ERR_SHAPE, "%s: map->reserved0 must be 0", fn);
+  CHECK(args->page_size == 1, SMLA_ERR_UNSUPPORTED, "%s: args->page_size must be 1 (one row per entry)", fn);
+  CHECK(args->q_dtype == SMLA_BF16, SMLA_ERR_UNSUPPORTED, "%s: the fused path takes bf16 q", fn);
+  CHECK(m->R >= 1 && m->pt_width >= 1 && m->pt_stride >= m->pt_width, SMLA_ERR_SHAPE,
+        "%s: map needs R >= 1, pt_width >= 1 and pt_stride >= pt_width", fn);
+  CHECK(pow2(m->page_size) && m->page_size <= (1 << 20), SMLA_ERR_UNSUPPORTED,
+        "%s: map->page_size must be a power of two in [1, 2^20] (got %d)", fn, m->page_size);
+  if (args->T > 0) {
+    CHECK(m->tok_req && m->page_table && m->seq_lens, SMLA_ERR_NULL,
+          "%s: map->tok_req, page_table and seq_lens are required", fn);
+    CHECK(aligned(m->tok_req, 4) && aligned(m->page_table, 4) && aligned(m->seq_lens, 4), SMLA_ERR_ALIGN,
+          "%s: map arrays must be 4-byte aligned", fn);
+  }
+  return SMLA_OK;
+}
+
 static smla_status decode_stages(const smla_decode_args* args, void* workspace, size_t workspace_bytes,
-                                 void* stream, int stages) {
+                                 void* stream, int stages, const smla_page_map* map = nullptr) {
   smla::DecodePlan plan;
   smla_status st = check_decode(args, &plan, true);
   if (st != SMLA_OK) return st;
+  if (map) {
+    st = check_page_map(args, map);
+    if (st != SMLA_OK) return st;
+  }
   if (args->T == 0) return ok();
   CHECK(workspace != nullptr && workspace_bytes >= plan.ws_bytes, SMLA_ERR_WORKSPACE,
         "smla_sparse_decode: workspace needs %zu bytes (got %zu)", plan.ws_bytes, workspace_bytes);
   CHECK(aligned(workspace, 256), SMLA_ERR_ALIGN, "smla_sparse_decode: workspace must be 256-byte aligned");
   CHECK((int64_t)args->T * plan.S < (1ll << 31), SMLA_ERR_RANGE, "smla_sparse_decode: T * splits too large");
-  return device_status(smla::launch_decode(*args, plan, workspace, (hipStream_t)stream, stages),
+  return device_status(smla::launch_decode(*args, plan, workspace, (hipStream_t)stream, stages, map),
                        "smla_sparse_decode");
 }
 
@@ -257,6 +282,18 @@ smla_status smla_sparse_decode_stage1(const smla_decode_args* args, void* worksp
 smla_status smla_sparse_decode_stage2(const smla_decode_args* args, void* workspace, size_t workspace_bytes,
                                       void* stream) {
   return decode_stages(args, workspace, workspace_bytes, stream, 2);
+}
+
+smla_status smla_sparse_decode_topk(const smla_decode_args* args, const smla_page_map* map, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  CHECK(map != nullptr, SMLA_ERR_NULL, "smla_sparse_decode_topk: map is NULL");
+  return decode_stages(args, workspace, workspace_bytes, stream, 3, map);
+}
+
+smla_status smla_sparse_decode_topk_stage1(const smla_decode_args* args, const smla_page_map* map,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  CHECK(map != nullptr, SMLA_ERR_NULL, "smla_sparse_decode_topk_stage1: map is NULL");
+  return decode_stages(args, workspace, workspace_bytes, stream, 1, map);
 }
 
 smla_status smla_build_group_union(const int32_t* slots, int64_t slots_stride, const int32_t* valid,

@@ -41,8 +41,15 @@ struct Stage1Args {
   int32_t S;
   int32_t H;
   int32_t T;
-  float* part_o;            // [T][S][H][512]
+  float* part_o;            // fp32 path: [T][S][H][512]; bf16 path: bf16 in the packed order below
   float* part_lse;          // [T][S][H], natural log
+  // page map: when map_req is set, the (page size 1) table holds request-relative positions,
+  // which the kernel resolves through the request's page-table row
+  const int32_t* map_req;
+  const int32_t* map_pt;
+  int64_t map_pt_stride;
+  const int32_t* map_seq;
+  int32_t map_R, map_pt_width, map_log2_page;
 };
 
 // Physical slot of position p of token t's table row, or -1 when masked.
@@ -172,6 +179,14 @@ __global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a
   const int r0 = s * a.rows_per_split;
   const int len = token_len(a, t);             // a scalar load; used once the gathers below are issued
   const bool loader = w < kLoaders;
+  // page map (scalar loads, in flight with the copies below): the token's request, its
+  // context length and page-table row; an invalid request masks every entry
+  const bool mapped = a.map_req != nullptr;
+  int32_t req = -1, seq = 0;
+  if (mapped) {
+    req = a.map_req[t];
+    if (req >= 0 && req < a.map_R) seq = a.map_seq[req]; else req = -1;
+  }
 
   // ---- prologue. The loader waves copy the split's table entries and the token's q rows
   // straight into LDS, so that no register has to wait for memory before the first gathers
@@ -210,19 +225,45 @@ __global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a
 
   // slots of the split's rows; -1 marks a masked row (past the length, a negative entry or
   // page id, or a slot outside the pool)
-  for (int i = tid; i < nchunks * kChunk; i += kS1Threads) {
-    int64_t sl = -1;
-    if (i < nrows) {
-      if (lp == 0) {
-        sl = slot_s[i];
-      } else {
-        const int p = r0 + i;
-        const int32_t page = page_s[(p >> lp) - e0];
-        sl = page < 0 ? -1 : ((int64_t)page << lp) + (p & ((1 << lp) - 1));
-      }
-      if (sl >= a.kv.num_slots) sl = -1;
+  if (mapped) {
+    // positions -> slots exactly as smla_resolve_slots computes them: a position counts when
+    // 0 <= pos < the request's context and its page is inside the row with an id >= 0. Both
+    // of a thread's page-id loads are issued before either is used.
+    static_assert(kMaxSplitRows == 2 * kS1Threads, "two rows per thread");
+    const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
+    const int mlp = a.map_log2_page;
+    int32_t pos[2], page[2];
+    bool ok[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * kS1Threads;
+      pos[k] = i < nrows ? slot_s[i] : -1;
+      ok[k] = req >= 0 && pos[k] >= 0 && pos[k] < seq && (pos[k] >> mlp) < a.map_pt_width;
+      page[k] = ptrow[ok[k] ? (pos[k] >> mlp) : 0];
     }
-    slot_s[i] = sl < 0 ? -1 : (int32_t)sl;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * kS1Threads;
+      if (i >= nchunks * kChunk) continue;
+      int64_t sl = -1;
+      if (ok[k] && page[k] >= 0) sl = ((int64_t)page[k] << mlp) + (pos[k] & ((1 << mlp) - 1));
+      slot_s[i] = (sl < 0 || sl >= a.kv.num_slots) ? -1 : (int32_t)sl;
+    }
+  } else {
+    for (int i = tid; i < nchunks * kChunk; i += kS1Threads) {
+      int64_t sl = -1;
+      if (i < nrows) {
+        if (lp == 0) {
+          sl = slot_s[i];
+        } else {
+          const int p = r0 + i;
+          const int32_t pg = page_s[(p >> lp) - e0];
+          sl = pg < 0 ? -1 : ((int64_t)pg << lp) + (p & ((1 << lp) - 1));
+        }
+        if (sl >= a.kv.num_slots) sl = -1;
+      }
+      slot_s[i] = sl < 0 ? -1 : (int32_t)sl;
+    }
   }
   lds_barrier();
 
@@ -453,16 +494,22 @@ __global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a
   }
   lds_barrier();
   const int64_t part = (int64_t)t * a.S + s;
-  float* po = a.part_o + part * a.H * kLatent;
+  float inv[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int h = h0 + 4 * g + v;
     const float l = xsum[0][h] + xsum[1][h];
-    const float inv = l > 0.f ? 1.0f / l : 0.0f;
-#pragma unroll
-    for (int nt = 0; nt < 16; ++nt) po[h * kLatent + 256 * x + nt * 16 + c] = oacc[nt][v] * inv;
+    inv[v] = l > 0.f ? 1.0f / l : 0.0f;
     if (x == 0 && c == 0) a.part_lse[part * a.H + h] = l > 0.f ? (m_run[v] + log2f(l)) * kLn2 : -INFINITY;
   }
+  // bf16 partials in the accumulators' own order, so that one store instruction writes 512
+  // contiguous bytes: lane (g, c) of wave (hq, x) stores heads h0 + 4g .. +3 of column
+  // 256x + 16nt + c as 8 bytes at packed_index(...) below
+  uint2* po = (uint2*)((uint16_t*)a.part_o + part * (kHeads * kLatent)) + ((hq * 2 + x) * 16 * 64 + lane);
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt)
+    po[nt * 64] = make_uint2(pack_bf16x2(oacc[nt][0] * inv[0], oacc[nt][1] * inv[1]),
+                             pack_bf16x2(oacc[nt][2] * inv[2], oacc[nt][3] * inv[3]));
 }
 
 // fp32 q and fp32 cache: a plain VALU path, 16 heads per workgroup, rows in chunks of 16.
@@ -611,10 +658,95 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2(Stage2Args a) {
     a.lse[(int64_t)t * a.lse_tok_stride + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
+// Packed bf16 partials of the MFMA path: element (h, col) of one (token, split) sits at
+// ((((hq * 2 + x) * 16 + nt) * 4 + g) * 16 + c) * 4 + v with h = 16 hq + 4 g + v and
+// col = 256 x + 16 nt + c. Thread = (token, 4 heads 4q .. 4q+3, 4 columns): its 16 values
+// are 32 contiguous bytes of every split.
+__global__ void __launch_bounds__(kS2Threads) decode_stage2_packed(Stage2Args a) {
+  constexpr int kThreadsPerToken = 16 * 128;           // head quads x column quads
+  constexpr int kBlocksPerToken = kThreadsPerToken / kS2Threads;
+  int t, bi;
+  if ((a.T & 7) == 0) {
+    const int i = blockIdx.x >> 3;
+    t = (blockIdx.x & 7) + 8 * (i / kBlocksPerToken);
+    bi = i % kBlocksPerToken;
+  } else {
+    t = blockIdx.x / kBlocksPerToken;
+    bi = blockIdx.x % kBlocksPerToken;
+  }
+  const int j = bi * kS2Threads + threadIdx.x;          // 0 .. 2047
+  // consecutive threads take consecutive 32-byte pieces of the packed partial
+  const int cq = j & 3, q = (j >> 2) & 15, nt = (j >> 6) & 15, x = j >> 10;   // q = 4 hq + g
+  const int hq = q >> 2, g = q & 3;
+  const int col0 = 256 * x + 16 * nt + 4 * cq;
+  const int hbase = 4 * q;
+  int len = a.lens[t];
+  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+  const int nact = min(a.S, (len + a.rows_per_split - 1) / a.rows_per_split);
+  const int64_t base = (int64_t)t * a.S;
+  const int64_t off = ((((hq * 2 + x) * 16 + nt) * 4 + g) * 16 + 4 * cq) * 4;   // bf16 elements
+  const uint16_t* po = (const uint16_t*)a.part_o;
+  float mx[4], wsum[4], acc[4][4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    mx[v] = -INFINITY;
+    wsum[v] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[v][k] = 0.f;
+  }
+  for (int s0 = 0; s0 < nact; s0 += kS2Batch) {
+    float4 l[kS2Batch];
+    uint4 o[kS2Batch][2];
+#pragma unroll
+    for (int jj = 0; jj < kS2Batch; ++jj) {
+      const bool in = s0 + jj < nact;
+      const int64_t ps = base + s0 + (in ? jj : 0);
+      l[jj] = in ? *(const float4*)(a.part_lse + ps * a.H + hbase)
+                 : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      const uint4* src = (const uint4*)(po + ps * (kHeads * kLatent) + off);
+      o[jj][0] = in ? src[0] : make_uint4(0, 0, 0, 0);
+      o[jj][1] = in ? src[1] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float bm = mx[v];
+#pragma unroll
+      for (int jj = 0; jj < kS2Batch; ++jj) bm = fmaxf(bm, ((const float*)&l[jj])[v]);
+      if (bm == -INFINITY) continue;
+      const float r = expf(mx[v] - bm);
+      wsum[v] *= r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[v][k] *= r;
+#pragma unroll
+      for (int jj = 0; jj < kS2Batch; ++jj) {
+        const float lv = ((const float*)&l[jj])[v];
+        const float wgt = lv == -INFINITY ? 0.f : expf(lv - bm);
+        wsum[v] += wgt;
+        // column 4cq + k of head hbase + v is bf16 element 4k + v of the 16 loaded
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t word = ((const uint32_t*)&o[jj][0])[(4 * k + v) >> 1];
+          acc[v][k] += wgt * bf16_to_f32((v & 1) ? (word >> 16) : (word & 0xffffu));
+        }
+      }
+      mx[v] = bm;
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int h = hbase + v;
+    const float inv = wsum[v] > 0.f ? 1.0f / wsum[v] : 0.f;
+    uint16_t* o = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)h * a.out_head_stride + col0;
+    *(uint2*)o = make_uint2(pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv), pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv));
+    if (a.lse && nt == 0 && x == 0 && cq == 0)
+      a.lse[(int64_t)t * a.lse_tok_stride + h] = wsum[v] > 0.f ? mx[v] + logf(wsum[v]) : -INFINITY;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void* ws, hipStream_t stream,
-                         int stages) {
+                         int stages, const smla_page_map* map) {
   if (d.T == 0) return hipSuccess;
   Stage1Args a;
   a.q = (const uint16_t*)d.q;
@@ -636,6 +768,22 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   a.T = d.T;
   a.part_o = (float*)ws;
   a.part_lse = (float*)((char*)ws + plan.part_o_bytes);
+  a.map_req = nullptr;
+  a.map_pt = nullptr;
+  a.map_pt_stride = 0;
+  a.map_seq = nullptr;
+  a.map_R = a.map_pt_width = a.map_log2_page = 0;
+  if (map) {
+    a.map_req = map->tok_req;
+    a.map_pt = map->page_table;
+    a.map_pt_stride = map->pt_stride;
+    a.map_seq = map->seq_lens;
+    a.map_R = map->R;
+    a.map_pt_width = map->pt_width;
+    int l = 0;
+    while ((1 << l) < map->page_size) ++l;
+    a.map_log2_page = l;
+  }
 
   if (!(stages & 1)) {
   } else if (d.q_dtype == SMLA_F32) {
@@ -664,7 +812,10 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   b.lse = d.lse;
   b.lse_tok_stride = d.lse_tok_stride;
   b.out_f32 = d.q_dtype == SMLA_F32;
-  hipLaunchKernelGGL(decode_stage2, dim3(d.T * ((d.H + 1) / 2)), dim3(kS2Threads), 0, stream, b);
+  if (d.q_dtype == SMLA_F32)
+    hipLaunchKernelGGL(decode_stage2, dim3(d.T * ((d.H + 1) / 2)), dim3(kS2Threads), 0, stream, b);
+  else
+    hipLaunchKernelGGL(decode_stage2_packed, dim3(d.T * (16 * 128 / kS2Threads)), dim3(kS2Threads), 0, stream, b);
   return hipGetLastError();
 }
 

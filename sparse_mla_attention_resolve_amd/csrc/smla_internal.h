@@ -19,7 +19,7 @@ struct DecodePlan {
   int32_t T, H, S;           // tokens, heads, splits
   int32_t rows_per_split;    // multiple of kChunk
   int32_t max_len;           // table_width * page_size
-  size_t part_o_bytes;       // [T, S, H, 512] fp32
+  size_t part_o_bytes;       // [T, S, H, 512]: bf16 (packed order) on the bf16 path, fp32 on the fp32 path
   size_t part_lse_bytes;     // [T, S, H] fp32
   size_t ws_bytes;
 };
@@ -34,9 +34,10 @@ hipError_t launch_kv_write(const void* src, int32_t src_dtype, int64_t src_strid
                            const int32_t* slot_mapping, int32_t T, const smla_kv& dst,
                            hipStream_t stream);
 
-// stages: bit 0 = stage 1, bit 1 = stage 2
+// stages: bit 0 = stage 1, bit 1 = stage 2. `map` (nullable): the table holds positions that
+// stage 1 resolves through this page map.
 hipError_t launch_decode(const smla_decode_args& a, const DecodePlan& plan, void* ws,
-                         hipStream_t stream, int stages = 3);
+                         hipStream_t stream, int stages = 3, const smla_page_map* map = nullptr);
 
 hipError_t launch_union(const int32_t* slots, int64_t slots_stride, const int32_t* valid,
                         int32_t Q, int32_t W, int32_t G, int64_t num_slots, uint32_t* enc,

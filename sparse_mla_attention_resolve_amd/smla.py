@@ -23,11 +23,14 @@ UNION_MAX_SLOTS = (1 << 24) - 2
 
 STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_ALIGN",
           4: "SMLA_ERR_UNSUPPORTED", 5: "SMLA_ERR_RANGE", 6: "SMLA_ERR_WORKSPACE", 7: "SMLA_ERR_DEVICE"}
+STATUS_CODES = {v: k for k, v in STATUS.items()}
 
 EXPORTS = ["smla_resolve_slots", "smla_sparse_decode_workspace", "smla_sparse_decode_splits",
-           "smla_sparse_decode", "smla_sparse_decode_stage1", "smla_sparse_decode_stage2", "smla_build_group_union", "smla_grouped_prefill", "smla_kv_write",
+           "smla_sparse_decode", "smla_sparse_decode_stage1", "smla_sparse_decode_stage2",
+           "smla_sparse_decode_topk", "smla_sparse_decode_topk_stage1",
+           "smla_build_group_union", "smla_grouped_prefill", "smla_kv_write",
            "smla_status_str", "smla_last_error", "smla_abi_version", "smla_sizeof_kv",
-           "smla_sizeof_decode_args", "smla_sizeof_prefill_args"]
+           "smla_sizeof_decode_args", "smla_sizeof_prefill_args", "smla_sizeof_page_map"]
 
 
 class SmlaError(RuntimeError):
@@ -71,6 +74,11 @@ class smla_prefill_args(ctypes.Structure):
                 ("lse", c_p), ("lse_tok_stride", c_i64)]
 
 
+class smla_page_map(ctypes.Structure):
+    _fields_ = [("tok_req", c_p), ("page_table", c_p), ("pt_stride", c_i64), ("seq_lens", c_p),
+                ("R", c_i32), ("pt_width", c_i32), ("page_size", c_i32), ("reserved0", c_i32)]
+
+
 _sig = {
     "smla_resolve_slots": [c_p, c_i64, c_p, c_p, c_i32, c_p, c_i64, c_i32, c_p, c_i32, c_i32, c_i32, c_p, c_i64, c_p],
     "smla_sparse_decode_workspace": [ctypes.POINTER(smla_decode_args), ctypes.POINTER(c_sz)],
@@ -78,13 +86,16 @@ _sig = {
     "smla_sparse_decode": [ctypes.POINTER(smla_decode_args), c_p, c_sz, c_p],
     "smla_sparse_decode_stage1": [ctypes.POINTER(smla_decode_args), c_p, c_sz, c_p],
     "smla_sparse_decode_stage2": [ctypes.POINTER(smla_decode_args), c_p, c_sz, c_p],
+    "smla_sparse_decode_topk": [ctypes.POINTER(smla_decode_args), ctypes.POINTER(smla_page_map), c_p, c_sz, c_p],
+    "smla_sparse_decode_topk_stage1": [ctypes.POINTER(smla_decode_args), ctypes.POINTER(smla_page_map), c_p, c_sz,
+                                       c_p],
     "smla_build_group_union": [c_p, c_i64, c_p, c_i32, c_i32, c_i32, c_i64, c_p, c_i64, c_p, c_p],
     "smla_grouped_prefill": [ctypes.POINTER(smla_prefill_args), c_p],
     "smla_kv_write": [c_p, c_i32, c_i64, c_p, c_i32, ctypes.POINTER(smla_kv), c_p],
     "smla_status_str": [c_i32],
     "smla_last_error": [],
     "smla_abi_version": [],
-    "smla_sizeof_kv": [], "smla_sizeof_decode_args": [], "smla_sizeof_prefill_args": [],
+    "smla_sizeof_kv": [], "smla_sizeof_decode_args": [], "smla_sizeof_prefill_args": [], "smla_sizeof_page_map": [],
 }
 for _name, _args in _sig.items():
     _f = getattr(_lib, _name)
@@ -94,6 +105,7 @@ for _name, _args in _sig.items():
 assert _lib.smla_sizeof_kv() == ctypes.sizeof(smla_kv), "smla_kv layout mismatch"
 assert _lib.smla_sizeof_decode_args() == ctypes.sizeof(smla_decode_args), "smla_decode_args layout mismatch"
 assert _lib.smla_sizeof_prefill_args() == ctypes.sizeof(smla_prefill_args), "smla_prefill_args layout mismatch"
+assert _lib.smla_sizeof_page_map() == ctypes.sizeof(smla_page_map), "smla_page_map layout mismatch"
 
 
 def lib():
@@ -262,29 +274,75 @@ def smla_sparse_decode(q, kv: KvCache, table, lens, page_size: int, scale: float
     return out, lse
 
 
+def _page_map(tok_req, page_table, seq_lens, page_size: int) -> smla_page_map:
+    for t, n in ((tok_req, "tok_req"), (page_table, "page_table"), (seq_lens, "seq_lens")):
+        _i32(t, n)
+    m = smla_page_map()
+    m.tok_req, m.page_table, m.pt_stride = tok_req.data_ptr(), page_table.data_ptr(), _rs(page_table)
+    m.seq_lens = seq_lens.data_ptr()
+    m.R, m.pt_width = page_table.shape
+    m.page_size = page_size
+    return m
+
+
+def smla_sparse_decode_topk(q, kv: KvCache, idx, valid, tok_req, page_table, seq_lens, page_size: int,
+                            scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            want_lse: bool = True, num_splits: int = 0,
+                            workspace: Optional[torch.Tensor] = None, stream=None):
+    """Decode straight from logical top-k indices idx [T, W] (valid counts `valid` [T]),
+    resolved through the page table inside stage 1. Returns (out, lse)."""
+    T, H, _ = q.shape
+    if out is None:
+        out = torch.empty((T, H, LATENT), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    a = _decode_args(q, kv, idx, valid, 1, scale, out, lse, num_splits)
+    m = _page_map(tok_req, page_table, seq_lens, page_size)
+    need = c_sz(0)
+    _check(_lib.smla_sparse_decode_workspace(ctypes.byref(a), ctypes.byref(need)))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.smla_sparse_decode_topk(ctypes.byref(a), ctypes.byref(m), _ptr(workspace), workspace.numel(),
+                                        _stream(stream)))
+    return out, lse
+
+
 class DecodeCall:
     """Prepared arguments for repeated decode calls on fixed tensors (no per-call allocation);
-    `stage1()`, `stage2()` and `__call__()` enqueue on the current stream."""
+    `stage1()`, `stage2()` and `__call__()` enqueue on the current stream. With
+    `page_map=(tok_req, page_table, seq_lens, page_size)` the table holds logical top-k
+    indices and stage 1 resolves them (smla_sparse_decode_topk)."""
 
     def __init__(self, q, kv: KvCache, table, lens, page_size: int, scale: float, out, lse, num_splits: int = 0,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None, page_map=None):
         self.args = _decode_args(q, kv, table, lens, page_size, scale, out, lse, num_splits)
         need = c_sz(0)
         _check(_lib.smla_sparse_decode_workspace(ctypes.byref(self.args), ctypes.byref(need)))
         if workspace is None:
             workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=q.device)
         self.workspace = workspace
-        self.keep = (q, kv, table, lens, out, lse)
+        self.map = None if page_map is None else _page_map(*page_map)
+        self.keep = (q, kv, table, lens, out, lse, page_map)
         self.splits = smla_sparse_decode_splits(q, kv, table, lens, page_size, scale, num_splits)
 
     def _run(self, fn, stream):
         _check(fn(ctypes.byref(self.args), _ptr(self.workspace), self.workspace.numel(), _stream(stream)))
 
+    def _run_map(self, fn, stream):
+        _check(fn(ctypes.byref(self.args), ctypes.byref(self.map), _ptr(self.workspace), self.workspace.numel(),
+                  _stream(stream)))
+
     def __call__(self, stream=None):
-        self._run(_lib.smla_sparse_decode, stream)
+        if self.map is None:
+            self._run(_lib.smla_sparse_decode, stream)
+        else:
+            self._run_map(_lib.smla_sparse_decode_topk, stream)
 
     def stage1(self, stream=None):
-        self._run(_lib.smla_sparse_decode_stage1, stream)
+        if self.map is None:
+            self._run(_lib.smla_sparse_decode_stage1, stream)
+        else:
+            self._run_map(_lib.smla_sparse_decode_topk_stage1, stream)
 
     def stage2(self, stream=None):
         self._run(_lib.smla_sparse_decode_stage2, stream)

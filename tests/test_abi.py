@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol():
 
 def test_struct_sizes_and_version():
     lib = S.lib()
-    assert lib.smla_abi_version() == 1
+    assert lib.smla_abi_version() == 2
+    assert lib.smla_sizeof_page_map() == ctypes.sizeof(S.smla_page_map) == 48
     assert lib.smla_sizeof_kv() == ctypes.sizeof(S.smla_kv) == 80
     assert lib.smla_sizeof_decode_args() == ctypes.sizeof(S.smla_decode_args)
     assert lib.smla_sizeof_prefill_args() == ctypes.sizeof(S.smla_prefill_args)
@@ -92,7 +93,10 @@ def test_decode_checks_and_workspace():
     assert S.lib().smla_sparse_decode_splits(ctypes.byref(_decode_args()), ctypes.byref(splits)) == OK
     s = splits.value
     assert 1 <= s <= 256
-    assert n >= 4 * s * 64 * 512 * 4 + 4 * s * 64 * 4
+    assert n >= 4 * s * 64 * 512 * 2 + 4 * s * 64 * 4          # bf16 partial outputs + fp32 LSE
+    f32 = _decode_args(q_dtype=S.SMLA_F32, H=16, kv_dtype=S.SMLA_F32, kv_row_stride=2304)
+    assert S.lib().smla_sparse_decode_splits(ctypes.byref(f32), ctypes.byref(splits)) == OK
+    assert _ws(f32)[1] >= 4 * splits.value * 16 * 512 * 4 + 4 * splits.value * 16 * 4   # fp32 partials
     assert _ws(_decode_args(H=32))[0] == UNSUP
     assert _ws(_decode_args(q_dtype=S.SMLA_F32))[0] == UNSUP          # fp32 q with a bf16 cache
     assert _ws(_decode_args(q_dtype=S.SMLA_F32, H=16, kv_dtype=S.SMLA_F32, kv_row_stride=2304))[0] == OK
@@ -186,3 +190,29 @@ def test_kv_write_checks():
     assert lib.smla_kv_write(FAKE, S.SMLA_F32, 576, FAKE, 0, ctypes.byref(d), None) == OK
     d.rope16 = FAKE + 514
     assert lib.smla_kv_write(FAKE, S.SMLA_F32, 576, FAKE, 0, ctypes.byref(d), None) == ALIGN
+
+
+def _map(**kw):
+    m = S.smla_page_map()
+    m.tok_req, m.page_table, m.pt_stride, m.seq_lens = FAKE, FAKE, 512, FAKE
+    m.R, m.pt_width, m.page_size = 32, 512, 64
+    for k, v in kw.items():
+        setattr(m, k, v)
+    return m
+
+
+def test_decode_topk_checks():
+    """The fused path validates its page map on the host and stops before any launch."""
+    f = S.lib().smla_sparse_decode_topk
+    a = _decode_args()
+    assert f(ctypes.byref(a), None, None, 0, None) == NULL
+    assert f(ctypes.byref(a), ctypes.byref(_map(reserved0=1)), None, 0, None) == SHAPE
+    assert f(ctypes.byref(a), ctypes.byref(_map(page_size=3)), None, 0, None) == UNSUP
+    assert f(ctypes.byref(a), ctypes.byref(_map(R=0)), None, 0, None) == SHAPE
+    assert f(ctypes.byref(a), ctypes.byref(_map(pt_stride=10)), None, 0, None) == SHAPE
+    assert f(ctypes.byref(a), ctypes.byref(_map(tok_req=None)), None, 0, None) == NULL
+    assert f(ctypes.byref(a), ctypes.byref(_map(seq_lens=FAKE + 2)), None, 0, None) == ALIGN
+    assert f(ctypes.byref(_decode_args(page_size=64)), ctypes.byref(_map()), None, 0, None) == UNSUP
+    # a valid map reaches the workspace check, which precedes any launch
+    assert f(ctypes.byref(a), ctypes.byref(_map()), None, 0, None) == S.STATUS_CODES["SMLA_ERR_WORKSPACE"]
+    assert S.lib().smla_sparse_decode_topk_stage1(ctypes.byref(a), None, None, 0, None) == NULL

@@ -199,3 +199,50 @@ def test_decode_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+
+
+@pytest.mark.parametrize("name", ["decode_bf16_b32", "decode_ragged_b128", "decode_fp8_b64"])
+def test_topk_fused_equals_resolve_then_decode(name):
+    """smla_sparse_decode_topk (resolution inside stage 1) is bitwise smla_resolve_slots followed
+    by the page size 1 decode, on the workloads' own index lists and page tables."""
+    c = gc.config(name)
+    lay = c.layout
+    kv, _ = gc.gpu_pool(smla, lay, c.rows, c.kv_dtype)
+    qt = gc.q_tensor(c.q, c.q_dtype)
+    idx, valid, req, pt, ctx = _t(c.idx), _t(c.valid), _t(c.tok_req), _t(lay.page_table), _t(lay.ctx)
+    slots = smla.smla_resolve_slots(idx, valid, req, pt, ctx, lay.page_size)
+    a = smla.smla_sparse_decode(qt, kv, slots, valid, 1, c.scale)
+    b = smla.smla_sparse_decode_topk(qt, kv, idx, valid, req, pt, ctx, lay.page_size, c.scale)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_topk_fused_masks(splits):
+    """Every masking rule of slot resolution inside the fused path: invalid requests, negative
+    positions, positions at or past the context, pages past the table row, page ids < 0,
+    padding past the valid count, and an empty context."""
+    rng = np.random.default_rng(21)
+    T, W, R, P, ptw, pages = 6, 300, 4, 16, 20, 160
+    num_slots = pages * P
+    page_table = np.stack([rng.permutation(pages)[:ptw] for _ in range(R)]).astype(np.int32)
+    page_table[1, 3] = -1
+    page_table[3, [0, 7]] = -1
+    seq_lens = np.array([320, 100, 0, 250], np.int32)
+    tok_req = np.array([0, 1, 2, 3, 7, -1], np.int32)
+    idx = np.stack([rng.choice(np.arange(-5, 340), size=W, replace=False) for _ in range(T)]).astype(np.int32)
+    valid = np.array([300, 150, 300, 0, 300, 280], np.int32)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((T, 64, 576)).astype(np.float32) * 0.5)
+    live = np.arange(num_slots, dtype=np.int32)
+    vals = rng.standard_normal((num_slots, 576)).astype(np.float32) * 0.5
+    kv, pool = _pools(live, vals, num_slots, "bf16")
+    qt = gc.q_tensor(q, "bf16")
+    args = (_t(idx), _t(valid), _t(tok_req), _t(page_table), _t(seq_lens))
+    slots = smla.smla_resolve_slots(*args, P)
+    a = smla.smla_sparse_decode(qt, kv, slots, _t(valid), 1, 1 / 16, num_splits=splits)
+    b = smla.smla_sparse_decode_topk(qt, kv, *args, P, 1 / 16, num_splits=splits)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    oslots = oracle.resolve_slots(idx, valid, tok_req, page_table, seq_lens, P)
+    assert np.array_equal(slots.cpu().numpy(), oslots)
+    o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, oslots, valid, 1, 1 / 16)
+    _check(b[0], b[1], o_ref, l_ref, BF16_ATOL, BF16_RTOL, f"fused masks splits={splits}")
+    assert int((oslots >= 0).sum(axis=1).min()) == 0 and int((oslots >= 0).sum(axis=1).max()) > 100
