@@ -24,7 +24,6 @@ namespace {
 
 constexpr int kHeads = 64;
 constexpr int kThreads = 256;
-constexpr int kPStride = 40;          // bf16 per head row of the P tile (80 B: conflict-free reads)
 
 struct Stage1Args {
   const uint16_t* q;
@@ -71,9 +70,16 @@ __device__ __forceinline__ int token_len(const Stage1Args& a, int t) {
 }
 
 // Shared-memory layout of one gathered row: the row's 16-byte units, unit u stored at
-// position u ^ ((row >> 1) & 7). The XOR spreads the 16 rows that one MFMA operand read
-// touches over distinct banks without padding, so a 32-row chunk is a whole number of
-// 64-lane x 16-byte direct-to-LDS load instructions per wave.
+// position u ^ key(row), a permutation inside each aligned block of 8 units. The key spreads
+// the rows that one operand read touches over the 64 LDS banks without padding, so a 32-row
+// chunk is a whole number of 64-lane x 16-byte direct-to-LDS load instructions. Its form
+// depends on the row size; both were chosen with the LDS bank-conflict counter on gfx950:
+//   bf16 (1152-byte rows): key = row & 7, conflict-free for the 16-byte score reads (16
+//     consecutive rows at one unit) and the transposing value reads (rows 4g .. 4g+3 and
+//     16 + 4g .. +3 at two units);
+//   fp8 (640-byte rows): key = 2 ((row >> 1) & 3) + (((row >> 3) ^ (row >> 4)) & 1),
+//     conflict-free for the 8-byte latent score reads and the transposing value reads; the
+//     two 16-byte rotary reads per chunk meet a two-way conflict.
 template <int KV>
 struct Lay;
 template <>
@@ -87,7 +93,13 @@ struct Lay<SMLA_FP8_E4M3> {
   static constexpr int kNBuf = 7;
 };
 
-__device__ __forceinline__ int swz(int row, int unit) { return unit ^ ((row >> 1) & 7); }
+template <int KV>
+__device__ __forceinline__ int swz_key(int row) {
+  if constexpr (KV == SMLA_BF16) return row & 7;
+  else return 2 * ((row >> 1) & 3) + (((row >> 3) ^ (row >> 4)) & 1);
+}
+template <int KV>
+__device__ __forceinline__ int swz(int row, int unit) { return unit ^ swz_key<KV>(row); }
 
 // Source of the gathers of masked rows (a row past the list's length, or a -1 entry):
 // the LDS tile then holds zeros there, so a zero softmax weight meets finite values.
@@ -132,9 +144,13 @@ __device__ __forceinline__ void wait_chunks(int chunks) {
   }
 }
 
-constexpr int kS1Threads = 512;   // 8 waves, two per SIMD: one waits on LDS while the other computes
-constexpr int kLoaders = 4;       // waves 0..3 issue the gathers
-constexpr int kQLoads = 64 * 72 / 64 / kLoaders;   // 16-byte q copies per loader lane (64 heads x 72 units)
+// Stage 1 workgroup: 8 waves, two per SIMD. Wave w = (hq, x) with hq = w & 3, x = w >> 2
+// owns heads 16hq .. 16hq+15; for the scores it takes rows 16x .. 16x+15 of each chunk, for
+// the output it takes latent columns 256x .. 256x+255. Its partner w ^ 4 holds the other half.
+constexpr int kS1Waves = 8;
+constexpr int kS1Threads = 64 * kS1Waves;
+constexpr int kQLoads = 18;                 // 16-byte q pieces per lane: 16 heads x 72 units / 64 lanes
+constexpr int kAhead = 4;                   // LDS operand reads kept in flight ahead of the MFMAs
 
 // Workgroup id -> (token, split). Workgroups are dispatched to the 8 XCDs round robin;
 // when T is a multiple of 8 every split of a token runs on one XCD, so the token's partial
@@ -150,72 +166,225 @@ __device__ __forceinline__ void stage1_coords(int b, int T, int S, int& t, int& 
   }
 }
 
+// Max and sum over the four lanes c, 16 + c, 32 + c, 48 + c (the four 16-lane rows of the
+// wave): v_permlane16_swap exchanges rows 0 <-> 1 and 2 <-> 3 between its two operands,
+// v_permlane32_swap the two halves, so each returned pair holds both partners' values.
+__device__ __forceinline__ float max_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Wait until at most `chunks` chunks are in flight for this wave, which issues `hi` or `lo`
+// copies per chunk (a compile-time count either way; the choice is wave-uniform).
+template <int MAXC, int HI, int LO>
+__device__ __forceinline__ void wait_chunks_w(bool hi, int chunks) {
+  if (hi) wait_chunks<MAXC, HI>(chunks); else wait_chunks<MAXC, LO>(chunks);
+}
+
+
+// Per-lane LDS byte offsets of wave (hq, x)'s operand reads (the same for every chunk).
+//   ka[m]: score operand A = K[chunk row 16x + c][dims 32ks + 8g .. +7]
+//     bf16: unit 4ks + g sits at 4(ks ^ (key >> 2)) + (g ^ (key & 3)): base m = ks & 1, plus 64 ks
+//     fp8:  8 bytes at unit 2ks + g/2, stored at 8(ks >> 2) + 2((ks & 3) ^ (key >> 1)) +
+//           ((g >> 1) ^ (key & 1)), + 8(g & 1): base m = ks & 3, plus 128 (ks >> 2)
+//   vo[m]: P V operand B = V[rows 4g .. 4g+3, then 16 + 4g .. +3][column c of tile 16x + nt]
+//     bf16: two transposed 16-bit reads (j = 0, 1); the group's lane c points at row
+//           16j + 4g + c/4, columns 16(16x + nt) + 4(c%4) .. +3: unit 32x + 2nt + (c%4)/2,
+//           stored at 32x + 8(nt >> 2) + 2((nt & 3) ^ (key >> 1)) + (((c%4)/2) ^ (key & 1)):
+//           base vo[4j + (nt & 3)], plus 128 (nt >> 2)
+//     fp8:  one transposed 8-bit read; lane c of the group points at row R(c/2), columns
+//           16(16x + nt) + 8(c%2) .. +7, with R(i) = 4g + i for i < 4 and 16 + 4g + i - 4
+//           after: unit 16x + nt, stored at 16x + 8(nt >> 3) + ((nt & 7) ^ key): base
+//           vo[nt & 7], plus 128 (nt >> 3)
 template <int KV>
-__global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a) {
+struct Offsets {
+  int ka[4];
+  int vo[8];
+  __device__ __forceinline__ Offsets(int x, int g, int c) {
+    constexpr int kRowBytes = Lay<KV>::kUnits * 16;
+    const int row = 16 * x + c, key = swz_key<KV>(row);
+    if constexpr (KV == SMLA_BF16) {
+      const int kh = (key >> 2) * 64;
+      ka[0] = row * kRowBytes + 16 * (g ^ (key & 3)) + kh;
+      ka[1] = row * kRowBytes + 16 * (g ^ (key & 3)) - kh;
+      ka[2] = ka[3] = 0;
+      const int b = (c & 3) >> 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 16 * j + 4 * g + (c >> 2), k2 = swz_key<KV>(r);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          vo[4 * j + m] = r * kRowBytes + 512 * x + 32 * (m ^ (k2 >> 1)) + 16 * (b ^ (k2 & 1)) + 8 * (c & 1);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) ka[m] = row * kRowBytes + 32 * (m ^ (key >> 1)) + 16 * ((g >> 1) ^ (key & 1)) + 8 * (g & 1);
+      const int i = c >> 1;
+      const int r = i < 4 ? 4 * g + i : 16 + 4 * g + i - 4, k2 = swz_key<KV>(r);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) vo[m] = r * kRowBytes + 256 * x + 16 * (m ^ k2) + 8 * (c & 1);
+    }
+  }
+};
+
+// One step of wave (hq, x): the scores of one chunk's rows 16x .. 16x+15 (S^T tile: lane
+// (g, c) gets rows 16x + 4g + v of head 16hq + c; 18 MFMAs on two accumulator chains)
+// and / or O += P V over another chunk's columns 256x .. 256x+255 (16 MFMAs, one per
+// 16-column tile), interleaved so that the matrix unit always has independent work while
+// the operand reads run kAhead steps ahead. sl receives the latent part of the scores, sr
+// the rotary part (fp8 only; bf16 sums both into sl).
+template <int KV, bool DO_S, bool DO_PV>
+__device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, const Offsets<KV>& off, int x, int g,
+                                           int c, const bf16x8 (&qf)[kQLoads], f32x4& sl, f32x4& sr,
+                                           const bf16x8& pa, f32x4 (&oacc)[16]) {
+  constexpr bool kFp8 = KV == SMLA_FP8_E4M3;
+  constexpr int kRowBytes = Lay<KV>::kUnits * 16;
+  constexpr int kSteps = DO_S ? 18 : 16;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 racc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // score step ks: bf16 k steps 0 .. 17; fp8 latent k steps 0 .. 15, then rotary 16, 17
+  auto kread = [&](int ks) -> uint4 {
+    if constexpr (!kFp8) {
+      return *(const uint4*)(kbS + off.ka[ks & 1] + 64 * ks);
+    } else if (ks < 16) {
+      const uint2 v = *(const uint2*)(kbS + off.ka[ks & 3] + 128 * (ks >> 2));
+      return make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+      const int row = 16 * x + c;
+      return *(const uint4*)(kbS + row * kRowBytes + swz<KV>(row, 32 + (ks - 16) * 4 + g) * 16);
+    }
+  };
+  auto vread = [&](int nt) -> uint4 {
+    if constexpr (!kFp8) {
+      const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(kbV + off.vo[nt & 3] + 128 * (nt >> 2)));
+      const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(kbV + off.vo[4 + (nt & 3)] + 128 * (nt >> 2)));
+      return __builtin_bit_cast(uint4, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      const i32x2 a = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) i32x2*)(kbV + off.vo[nt & 7] + 128 * (nt >> 3)));
+      return make_uint4((uint32_t)a[0], (uint32_t)a[1], 0u, 0u);
+    }
+  };
+  uint4 kq[kAhead + 1], vq[kAhead + 1];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) {
+    if constexpr (DO_S) kq[i] = kread(i);
+    if constexpr (DO_PV) vq[i] = vread(i);
+  }
+#pragma unroll
+  for (int k = 0; k < kSteps; ++k) {
+    if constexpr (DO_S) {
+      if (k + kAhead < 18) kq[(k + kAhead) % (kAhead + 1)] = kread(k + kAhead);
+      const uint4 kv = kq[k % (kAhead + 1)];
+      if constexpr (!kFp8) {
+        acc[k & 1] = mfma16x16x32(as_bf16x8(kv), qf[k], acc[k & 1]);
+      } else if (k < 16) {
+        acc[k & 1] = mfma16x16x32(e4m3x8_to_bf16x8(kv.x, kv.y), qf[k], acc[k & 1]);
+      } else {
+        racc = mfma16x16x32(as_bf16x8(kv), qf[k], racc);
+      }
+    }
+    if constexpr (DO_PV) {
+      if (k < 16) {
+        if (k + kAhead < 16) vq[(k + kAhead) % (kAhead + 1)] = vread(k + kAhead);
+        const uint4 vv = vq[k % (kAhead + 1)];
+        const bf16x8 b = kFp8 ? e4m3x8_to_bf16x8(vv.x, vv.y) : as_bf16x8(vv);
+        oacc[k] = mfma16x16x32(pa, b, oacc[k]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (DO_S) {
+    sl = acc[0] + acc[1];
+    sr = racc;
+  }
+}
+
+// Stage 1. The scores are computed transposed, S^T = K Q^T (chunk rows are the M dimension
+// of a 16x16x32 MFMA tile, heads the N dimension, K = 576), so that lane (g, c) holds head
+// c's scores for rows 4g .. 4g+3 of its half. The two partners swap their tiles through LDS,
+// after which each lane holds head c's eight scores for rows 4g + v and 16 + 4g + v: the
+// softmax statistics need only cross-lane moves inside the wave, and the eight weights are
+// the A operand of the P V product (16x16x32, K = the chunk's 32 rows taken in that order),
+// whose B operand the transposing LDS reads fetch in the same row order. The loop is
+// software pipelined: while it accumulates P V for chunk ci it computes the scores of
+// chunk ci + 1.
+
+template <int KV>
+__global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a) {
   using L = Lay<KV>;
   constexpr int kRowBytes = L::kUnits * 16;
   constexpr int kChunkBytes = kChunk * kRowBytes;
-  constexpr int kLoads = kChunk * L::kUnits / (kLoaders * 64);   // per loader thread: 9 (bf16), 5 (fp8)
-  static_assert(kChunk * L::kUnits % (kLoaders * 64) == 0, "a chunk must tile the loaders' instructions");
+  constexpr int kInstr = kChunk * L::kUnits / 64;           // 16-byte x 64-lane copies per chunk: 36 / 20
+  static_assert(kChunk * L::kUnits % 64 == 0, "a chunk must be whole copy instructions");
+  constexpr int kLoadsHi = kInstr / kS1Waves + 1, kLoadsLo = kInstr / kS1Waves;
+  constexpr int kHiWaves = kInstr % kS1Waves;               // waves 0 .. kHiWaves-1 issue one more copy
   constexpr int kNBuf = L::kNBuf;
+  constexpr bool kFp8 = KV == SMLA_FP8_E4M3;
   __shared__ __attribute__((aligned(16))) char kvbuf[kNBuf][kChunkBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[4][16 * kPStride];
-  __shared__ float xmax[2][kHeads];
-  __shared__ float xsum[2][kHeads];
-  __shared__ int32_t slot_s[kMaxSplitRows];
+  __shared__ __attribute__((aligned(16))) int32_t slot_s[kMaxSplitRows];
   __shared__ int32_t page_s[kMaxSplitRows / 2 + 64];     // page ids of a split (page size >= 2)
-  __shared__ float scale_s[KV == SMLA_FP8_E4M3 ? kMaxSplitRows : 1];
+  __shared__ __attribute__((aligned(16))) float scale_s[kFp8 ? kMaxSplitRows : 4];
+  __shared__ float sx[kS1Waves][4][64];                    // score tiles swapped between partners
 
   int t, s;
   stage1_coords(blockIdx.x, a.T, a.S, t, s);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform, kept in an SGPR
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int hq = w & 3;       // heads 16hq .. 16hq+15
-  const int x = w >> 2;       // scores: chunk rows 16x .. 16x+15; P V: columns 256x .. 256x+255
+  const int hq = w & 3, x = w >> 2;
   const int h0 = 16 * hq;
+  const bool hi = w < kHiWaves;
 
+  // the scalar loads the prologue depends on go out together
   const int lp = a.log2_page;
   const int r0 = s * a.rows_per_split;
-  const int len = token_len(a, t);             // a scalar load; used once the gathers below are issued
-  const bool loader = w < kLoaders;
-  // page map (scalar loads, in flight with the copies below): the token's request, its
-  // context length and page-table row; an invalid request masks every entry
+  const int len = token_len(a, t);
   const bool mapped = a.map_req != nullptr;
-  int32_t req = -1, seq = 0;
+  int32_t req = mapped ? a.map_req[t] : -1;
+  int32_t seq = 0;
   if (mapped) {
-    req = a.map_req[t];
     if (req >= 0 && req < a.map_R) seq = a.map_seq[req]; else req = -1;
   }
 
-  // ---- prologue. The loader waves copy the split's table entries and the token's q rows
-  // straight into LDS, so that no register has to wait for memory before the first gathers
-  // go out: entries table[t][e0 .. e0 + n_ent) (slots when the page size is 1, page ids
-  // otherwise) into slot_s / page_s, and q[t] (64 x 576 bf16) into ring slots 2.. (free
-  // until the chunk gathers reach them).
+  // ---- prologue. The waves copy the split's table entries and the token's q straight into
+  // LDS, so that no register waits for memory before the first gathers go out: entries
+  // table[t][e0 .. e0 + n_ent) (slots when the page size is 1, page ids otherwise) into
+  // slot_s / page_s, and q, in the order the lanes read it back (head quarter hq: piece ks
+  // of lane (g, c) = head 16hq + c, dims 32ks + 8g .. +7), into ring slots 2.. (free until
+  // the chunk gathers reach them). Wave (hq, x) copies pieces 9x .. 9x+8 of quarter hq.
   const int32_t* trow = a.table + (int64_t)t * a.table_stride;
   const int e0 = r0 >> lp;
   const int n_ent = lp == 0 ? min(a.rows_per_split, a.max_len - r0)
                             : min((r0 + a.rows_per_split - 1) >> lp, a.table_width - 1) - e0 + 1;
-  char* const qlds = kvbuf[2];
-  static_assert((kNBuf - 2) * kChunkBytes >= kHeads * kRow * 2, "q must fit the ring slots from 2 on");
-  if (loader) {
+  static_assert((kNBuf - 2) * kChunkBytes >= 4 * kQLoads * 1024, "q must fit the ring slots from 2 on");
+  char* const qlds = kvbuf[2] + hq * (kQLoads * 1024);
+  {
     int32_t* ent = lp == 0 ? slot_s : page_s;
-    for (int k = w; k * 64 < n_ent; k += kLoaders) {
+    for (int k = w; k * 64 < n_ent; k += kS1Waves) {
       const int e = k * 64 + lane;
       dma4(e < n_ent ? (const void*)(trow + e0 + e) : (const void*)kZeroRow, (char*)(ent + k * 64));
     }
-    const uint16_t* qt = a.q + (int64_t)t * a.q_tok_stride;
+    const uint16_t* qh = a.q + (int64_t)t * a.q_tok_stride + (int64_t)(h0 + c) * a.q_head_stride + 8 * g;
 #pragma unroll
-    for (int m = 0; m < kQLoads; ++m) {
-      const int j = w + kLoaders * m;            // 16-byte units 64 j .. 64 j + 63 of the [64][72] tile
-      const int u = 64 * j + lane, h = u / 72, k = u % 72;
-      dma16(qt + (int64_t)h * a.q_head_stride + 8 * k, qlds + 1024 * j);
+    for (int k = 0; k < kQLoads / 2; ++k) {
+      const int ks = 9 * x + k;
+      dma16(qh + 32 * ks, qlds + ks * 1024);
     }
-    wait_vmcnt<kQLoads>();                      // the entries (issued first) are in LDS
+    wait_vmcnt<kQLoads / 2>();                  // this wave's entries (issued first) are in LDS
   }
   if (r0 >= len) {                              // inactive split: stage 2 never reads it
-    wait_vmcnt<0>();                            // no gather may land after the workgroup is gone
+    wait_vmcnt<0>();                            // no copy may land after the workgroup is gone
     return;
   }
   const int r1 = min(r0 + a.rows_per_split, len);
@@ -229,20 +398,21 @@ __global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a
     // positions -> slots exactly as smla_resolve_slots computes them: a position counts when
     // 0 <= pos < the request's context and its page is inside the row with an id >= 0. Both
     // of a thread's page-id loads are issued before either is used.
-    static_assert(kMaxSplitRows == 2 * kS1Threads, "two rows per thread");
+    constexpr int kPer = kMaxSplitRows / kS1Threads;
+    static_assert(kMaxSplitRows % kS1Threads == 0, "rows per thread");
     const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
     const int mlp = a.map_log2_page;
-    int32_t pos[2], page[2];
-    bool ok[2];
+    int32_t pos[kPer], page[kPer];
+    bool ok[kPer];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kPer; ++k) {
       const int i = tid + k * kS1Threads;
       pos[k] = i < nrows ? slot_s[i] : -1;
       ok[k] = req >= 0 && pos[k] >= 0 && pos[k] < seq && (pos[k] >> mlp) < a.map_pt_width;
       page[k] = ptrow[ok[k] ? (pos[k] >> mlp) : 0];
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kPer; ++k) {
       const int i = tid + k * kS1Threads;
       if (i >= nchunks * kChunk) continue;
       int64_t sl = -1;
@@ -275,242 +445,181 @@ __global__ void __launch_bounds__(kS1Threads, 2) decode_stage1_mfma(Stage1Args a
   const uint32_t lat8_stride32 = (uint32_t)a.kv.lat8_stride, rope16_stride32 = (uint32_t)a.kv.rope16_stride;
   const uint32_t row_stride32 = (uint32_t)a.kv.row_stride;
 
-  // gather chunk ci into ring slot ci % kNBuf: each loader thread owns the same kLoads
-  // 16-byte positions of every chunk, precomputed here as (row, byte offset in the row,
-  // plane); masked rows gather from the zero row
-  int32_t lpos[kLoads];
+  // fp8: the rows' scales go to LDS ahead of the first chunk (masked rows, and the entries
+  // past the split's last chunk, which hold no slot, read a zero)
+  if constexpr (kFp8) {
+    for (int k = 0; k * kS1Threads < nchunks * kChunk; ++k) {
+      const int i = k * kS1Threads + tid;
+      const int32_t sl = i < nchunks * kChunk ? slot_s[i] : -1;
+      const char* src = sl >= 0 ? (const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride : (const char*)kZeroRow;
+      dma4(src, (char*)(scale_s + k * kS1Threads + w * 64));
+    }
+  }
+
+  // gather chunk ci into ring slot ci % kNBuf: copy instruction i = 8k + w of a chunk puts
+  // the chunk's 16-byte units 64i .. 64i+63 (row-major, unit positions swizzled) at bytes
+  // 1024i of the slot. Each lane's (row, stored unit) pairs are the same for every chunk;
+  // masked rows gather from the zero row.
+  int32_t lpos[kLoadsHi];
 #pragma unroll
-  for (int k = 0; k < kLoads; ++k) {
-    const int pos = (k * kLoaders + w) * 64 + lane;
-    const int row = pos / L::kUnits, unit = swz(row, pos % L::kUnits);   // the swizzle is an involution
+  for (int k = 0; k < kLoadsHi; ++k) {
+    const int pos = (k * kS1Waves + w) * 64 + lane;
+    const int row = pos / L::kUnits, unit = swz<KV>(row, pos % L::kUnits);   // the swizzle is an involution
     lpos[k] = row | (unit << 8);
   }
   auto issue = [&](int ci) {
     char* base = kvbuf[ci % kNBuf];
     const int32_t* srow = slot_s + ci * kChunk;
+    // every slot is read before the first copy goes out: a copy's asm statement is a memory
+    // barrier for the compiler, so a read placed after one would wait for LDS on its own
+    int32_t sls[kLoadsHi];
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const int32_t sl = srow[lpos[k] & 0xff];
+    for (int k = 0; k < kLoadsHi; ++k) sls[k] = (k < kLoadsLo || hi) ? srow[lpos[k] & 0xff] : -1;
+#pragma unroll
+    for (int k = 0; k < kLoadsHi; ++k) {
+      if (k == kLoadsLo && !hi) break;
+      const int32_t sl = sls[k];
       const int unit = lpos[k] >> 8;
       const bool live = sl >= 0;
       const uint32_t slot = live ? (uint32_t)sl : 0u;
       const char* src;
-      if constexpr (KV == SMLA_BF16) {
+      if constexpr (!kFp8) {
         src = (live ? (const char*)a.kv.rows : (const char*)kZeroRow) + (uint64_t)slot * row_stride32 + unit * 16;
       } else {
         const bool lat = unit < 32;
         const char* plane = live ? (lat ? lat8 : rope16_m32) : (const char*)kZeroRow;
         src = plane + (uint64_t)slot * (lat ? lat8_stride32 : rope16_stride32) + unit * 16;
       }
-      dma16(src, base + (k * kLoaders + w) * 64 * 16);
+      dma16(src, base + (k * kS1Waves + w) * 1024);
     }
   };
 
   // chunks 0 and 1 go out first (their ring slots hold no q); once q has landed every wave
-  // copies its fragments (A operand of the scores: head h0 + c, dims 32ks + 8g .. +7), and
-  // the slots q occupied take the next chunks
-  if (loader) {
-    for (int ci = 0; ci < 2 && ci < nchunks; ++ci) issue(ci);
-    wait_chunks<2, kLoads>(min(2, nchunks));    // q was issued before these chunks
-  }
+  // moves its quarter to registers, and after every wave has done so the slots q occupied
+  // take the next chunks
+  for (int ci = 0; ci < 2 && ci < nchunks; ++ci) issue(ci);
+  wait_chunks_w<2, kLoadsHi, kLoadsLo>(hi, min(2, nchunks));   // q was issued before these chunks
   lds_barrier();
-  bf16x8 qf[18];
+  bf16x8 qf[kQLoads];
 #pragma unroll
-  for (int ks = 0; ks < 18; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ((h0 + c) * 72 + 4 * ks + g) * 16));
+  for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
   lds_barrier();
-  if (loader) {
-    for (int ci = 2; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
-  } else if constexpr (KV == SMLA_FP8_E4M3) {
-    // the other waves fetch the rows' scales meanwhile; the first barrier of the loop
-    // publishes them
-    for (int i = tid - kLoaders * 64; i < nchunks * kChunk; i += kS1Threads - kLoaders * 64) {
-      const int32_t sl = slot_s[i];
-      scale_s[i] = sl >= 0 ? *(const float*)((const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride) : 0.f;
-    }
-  }
+  for (int ci = 2; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
 
+  const Offsets<KV> off(x, g, c);
   f32x4 oacc[16];
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }
-  uint16_t* pw = pbuf[hq];
+  float m_run = -INFINITY, l_part = 0.f;        // head h0 + c; l_part: this lane's rows only
+  bf16x8 pa;                                    // softmax weights of the chunk being multiplied
+  f32x4 sl, sr;
 
-  for (int ci = 0; ci < nchunks; ++ci) {
-    // chunk ci is in LDS once its loaders' gathers are done and every wave got here
-    if (loader) wait_chunks<kNBuf - 2, kLoads>(min(kNBuf - 2, nchunks - 1 - ci));
-    lds_barrier();
-    if (loader && ci + kNBuf - 1 < nchunks) issue(ci + kNBuf - 1);   // into the slot every wave is done with
-    const char* kb = kvbuf[ci % kNBuf];
-
-    // ---- scores: heads h0 + 4g + v against chunk row 16x + c
-    const int row = 16 * x + c;
-    const int key = (row >> 1) & 7;
-    const char* kr = kb + row * kRowBytes;
-    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rs = 1.f;
-    if constexpr (KV == SMLA_BF16) {
-      // unit 4ks + g sits at 4(ks ^ (key >> 2)) + (g ^ (key & 3)): one base for even and
-      // one for odd ks, plus the immediate 64 ks
-      const int kh = (key >> 2) * 64;
-      const char* b_even = kr + 16 * (g ^ (key & 3)) + kh;
-      const char* b_odd = kr + 16 * (g ^ (key & 3)) - kh;
-      // operand reads run three MFMAs ahead; the schedule barriers keep the compiler from
-      // hoisting every read (which would not fit the register file)
-      uint4 kq[4];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) kq[i] = *(const uint4*)(((i & 1) ? b_odd : b_even) + 64 * i);
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        if (ks + 3 < 18) kq[(ks + 3) & 3] = *(const uint4*)((((ks + 3) & 1) ? b_odd : b_even) + 64 * (ks + 3));
-        sacc = mfma16x16x32(qf[ks], as_bf16x8(kq[ks & 3]), sacc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      // unit 2ks + g/2 sits at 8(ks >> 2) + 2((ks & 3) ^ (key >> 1)) + ((g >> 1) ^ (key & 1))
-      const char* kb4[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) kb4[m] = kr + 32 * (m ^ (key >> 1)) + 16 * ((g >> 1) ^ (key & 1)) + 8 * (g & 1);
-      uint2 kq[4];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) kq[i] = *(const uint2*)(kb4[i & 3] + 128 * (i >> 2));
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        if (ks + 3 < 16) kq[(ks + 3) & 3] = *(const uint2*)(kb4[(ks + 3) & 3] + 128 * ((ks + 3) >> 2));
-        sacc = mfma16x16x32(qf[ks], e4m3x8_to_bf16x8(kq[ks & 3].x, kq[ks & 3].y), sacc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      f32x4 racc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 16; ks < 18; ++ks) {
-        const bf16x8 kf = as_bf16x8(*(const uint4*)(kr + swz(row, 32 + (ks - 16) * 4 + g) * 16));
-        racc = mfma16x16x32(qf[ks], kf, racc);
-      }
-      rs = scale_s[ci * kChunk + row];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sacc[v] = sacc[v] * rs + racc[v];
-    }
-
-    // ---- online softmax. The two waves of a head quarter hold rows 0..15 and 16..31 of
-    // the chunk and agree on the chunk maximum through LDS. The running max only moves when
-    // a score exceeds it by more than 2^8, so most chunks skip the rescale of O.
-    const bool ok = slot_s[ci * kChunk + row] >= 0;
+  // online softmax in base 2 for head h0 + c over chunk ci's 32 rows (both partners compute
+  // the same values), from this wave's score tile and the partner's; leaves the weights that
+  // meet the rows' values in pa. The running max only moves when a score exceeds it by more
+  // than 2^8, so most chunks skip the rescale of O.
+  auto softmax = [&](int ci) {
     float sv[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      sv[v] = ok ? sacc[v] * a.scale_log2 : -INFINITY;
-      const float mloc = max16(sv[v]);
-      if (c == 0) xmax[x][h0 + 4 * g + v] = mloc;
+    {
+      const int4 lv = *(const int4*)(slot_s + ci * kChunk + 16 * x + 4 * g);
+      float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
+      if constexpr (kFp8) sc = *(const float4*)(scale_s + ci * kChunk + 16 * x + 4 * g);
+      const float raw[4] = {kFp8 ? sl[0] * sc.x + sr[0] : sl[0], kFp8 ? sl[1] * sc.y + sr[1] : sl[1],
+                            kFp8 ? sl[2] * sc.z + sr[2] : sl[2], kFp8 ? sl[3] * sc.w + sr[3] : sl[3]};
+      sv[0] = lv.x >= 0 ? raw[0] * a.scale_log2 : -INFINITY;
+      sv[1] = lv.y >= 0 ? raw[1] * a.scale_log2 : -INFINITY;
+      sv[2] = lv.z >= 0 ? raw[2] * a.scale_log2 : -INFINITY;
+      sv[3] = lv.w >= 0 ? raw[3] * a.scale_log2 : -INFINITY;
     }
+    // swap tiles with the partner: afterwards f[4j + v] is row 16j + 4g + v for both. The
+    // partner read this wave's previous tile before it reached the barrier that this wave
+    // passed last, so the slot is free.
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sx[w][v][lane] = sv[v];
     lds_barrier();
-    float alpha[4];
-    bool grow = false;
+    float f[8];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float mc = fmaxf(xmax[0][h0 + 4 * g + v], xmax[1][h0 + 4 * g + v]);
-      const bool up = mc > m_run[v] + 8.0f;
-      const float mn = up ? mc : m_run[v];
-      alpha[v] = up ? __builtin_amdgcn_exp2f(m_run[v] - mn) : 1.0f;
-      grow |= up;
-      const float pv = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] - mn);
-      pw[(4 * g + v) * kPStride + row] = __builtin_bit_cast(uint16_t, (__bf16)(pv * rs));
-      l_run[v] = l_run[v] * alpha[v] + sum16(pv);
-      m_run[v] = mn;
+      const float o = sx[w ^ 4][v][lane];
+      f[v] = x == 0 ? sv[v] : o;
+      f[4 + v] = x == 0 ? o : sv[v];
     }
-    if (__any(grow)) {
+    float mloc = f[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mloc = fmaxf(mloc, f[i]);
+    mloc = max_rows(mloc);
+    const bool up = mloc > m_run + 8.0f;
+    const float mn = up ? mloc : m_run;
+    const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mn) : 1.0f;
+    float pv[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(f[i] - mn);
+      psum += pv[i];
+    }
+    l_part = l_part * alpha + psum;
+    if (__any(up && m_run != -INFINITY)) {
+      // O rows are heads h0 + 4g + v: their factors live in lanes c = 4g + v
+      float ah[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ah[v] = __shfl(alpha, 4 * g + v, 64);
 #pragma unroll
       for (int nt = 0; nt < 16; ++nt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) oacc[nt][v] *= alpha[v];
+        for (int v = 0; v < 4; ++v) oacc[nt][v] *= ah[v];
     }
-    lds_barrier();
-
-    // ---- O += P V: A = P[head h0 + c][rows 8g .. 8g+7], B = V[rows 8g .. 8g+7][256x + 16nt + c]
-    if constexpr (KV == SMLA_BF16) {
-      // Two 16x16x16 MFMAs per 16-column tile, over chunk rows 0..15 and 16..31. A = P[head
-      // h0 + c][rows 16kh + 4g .. +3]; B = V[rows 16kh + 4g .. +3][256x + 16nt + c], which one
-      // transposed 16-bit read delivers when the group's lane c points at row 16kh + 4g + c/4,
-      // columns 256x + 16nt + 4(c%4) .. +3: unit 32x + 2nt + (c%4)/2 of that row, stored at
-      // 32x + 8(nt >> 2) + 2((nt & 3) ^ (key >> 1)) + (((c%4)/2) ^ (key & 1)).
-      const i16x4 pa0 = *(const i16x4*)(pw + c * kPStride + 4 * g);
-      const i16x4 pa1 = *(const i16x4*)(pw + c * kPStride + 16 + 4 * g);
-      const int b = (c & 3) >> 1;
-      const char* vb0[4];
-      const char* vb1[4];
-      {
-        const int r0 = 4 * g + (c >> 2), r1 = r0 + 16;
-        const int k0 = (r0 >> 1) & 7, k1 = (r1 >> 1) & 7;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          vb0[m] = kb + r0 * kRowBytes + 512 * x + 32 * (m ^ (k0 >> 1)) + 16 * (b ^ (k0 & 1)) + 8 * (c & 1);
-          vb1[m] = kb + r1 * kRowBytes + 512 * x + 32 * (m ^ (k1 >> 1)) + 16 * (b ^ (k1 & 1)) + 8 * (c & 1);
-        }
-      }
-      auto vread = [&](int i) {          // i = 2 nt + kh
-        const char* const* vb = (i & 1) ? vb1 : vb0;
-        const int nt = i >> 1;
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vb[nt & 3] + 128 * (nt >> 2)));
-      };
-      i16x4 vq[4];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) vq[i] = vread(i);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i + 3 < 32) vq[(i + 3) & 3] = vread(i + 3);
-        oacc[i >> 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k((i & 1) ? pa1 : pa0, vq[i & 3], oacc[i >> 1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      const bf16x8 pf = as_bf16x8(*(const uint4*)(pw + c * kPStride + 8 * g));
-      // transposed 8-bit read: lane 16g + c receives V[8g + 0..7][256x + 16nt + c] when the
-      // group's lane c points at row 8g + c/2, columns 256x + 16nt + 8(c%2) .. +7: unit
-      // 16x + nt, stored at 16x + 8(nt >> 3) + ((nt & 7) ^ key): eight bases plus an immediate.
-      const int r = 8 * g + (c >> 1);
-      const int vkey = (r >> 1) & 7;
-      const char* vb[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) vb[m] = kb + r * kRowBytes + 256 * x + 16 * (m ^ vkey) + 8 * (c & 1);
-      auto vread = [&](int nt) {
-        return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2*)(vb[nt & 7] + 128 * (nt >> 3)));
-      };
-      i32x2 vq[4];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) vq[i] = vread(i);
-#pragma unroll
-      for (int nt = 0; nt < 16; ++nt) {
-        if (nt + 3 < 16) vq[(nt + 3) & 3] = vread(nt + 3);
-        oacc[nt] = mfma16x16x32(pf, e4m3x8_to_bf16x8((uint32_t)vq[nt & 3][0], (uint32_t)vq[nt & 3][1]), oacc[nt]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    m_run = mn;
+    if constexpr (kFp8) {
+      // the weight that meets row r's values is p * scale(r)
+      const float4 sc0 = *(const float4*)(scale_s + ci * kChunk + 4 * g);
+      const float4 sc1 = *(const float4*)(scale_s + ci * kChunk + 16 + 4 * g);
+      pv[0] *= sc0.x; pv[1] *= sc0.y; pv[2] *= sc0.z; pv[3] *= sc0.w;
+      pv[4] *= sc1.x; pv[5] *= sc1.y; pv[6] *= sc1.z; pv[7] *= sc1.w;
     }
-  }
-
-  // ---- combine the two row halves' sums, normalise, write the split's partials
-  if (c == 0) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) xsum[x][h0 + 4 * g + v] = l_run[v];
-  }
+    for (int i = 0; i < 8; ++i) pa[i] = (__bf16)pv[i];
+  };
+
+  // scores of chunk 0
+  wait_chunks_w<kNBuf - 2, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 2, nchunks - 1));
   lds_barrier();
+  chunk_step<KV, true, false>(kvbuf[0], kvbuf[0], off, x, g, c, qf, sl, sr, pa, oacc);
+  softmax(0);
+
+  // iteration ci: O += P V over chunk ci together with the scores of chunk ci + 1. The
+  // barrier at its top publishes chunk ci + 1 and tells that every wave is done with the
+  // ring slot of chunk ci - 1, which the iteration refills.
+  for (int ci = 0; ci + 1 < nchunks; ++ci) {
+    wait_chunks_w<kNBuf - 3, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 3, nchunks - 2 - ci));
+    lds_barrier();
+    chunk_step<KV, true, true>(kvbuf[(ci + 1) % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc);
+    // the next gathers go out once this step's work is issued: a copy instruction can wait
+    // for room in the compute unit's memory queue, and it must not hold up chunks that
+    // have already landed
+    if (ci + kNBuf - 1 < nchunks) issue(ci + kNBuf - 1);
+    softmax(ci + 1);
+  }
+  chunk_step<KV, false, true>(kvbuf[(nchunks - 1) % kNBuf], kvbuf[(nchunks - 1) % kNBuf], off, x, g, c, qf, sl, sr,
+                              pa, oacc);
+
+  // ---- normalise, write the split's partials
+  const float l = sum_rows(l_part);              // head h0 + c, all rows of the split
   const int64_t part = (int64_t)t * a.S + s;
+  if (x == 0 && g == 0) a.part_lse[part * a.H + h0 + c] = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  const float inv_c = l > 0.f ? 1.0f / l : 0.0f;
   float inv[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int h = h0 + 4 * g + v;
-    const float l = xsum[0][h] + xsum[1][h];
-    inv[v] = l > 0.f ? 1.0f / l : 0.0f;
-    if (x == 0 && c == 0) a.part_lse[part * a.H + h] = l > 0.f ? (m_run[v] + log2f(l)) * kLn2 : -INFINITY;
-  }
+  for (int v = 0; v < 4; ++v) inv[v] = __shfl(inv_c, 4 * g + v, 64);
   // bf16 partials in the accumulators' own order, so that one store instruction writes 512
   // contiguous bytes: lane (g, c) of wave (hq, x) stores heads h0 + 4g .. +3 of column
-  // 256x + 16nt + c as 8 bytes at packed_index(...) below
+  // 256x + 16nt + c as 8 bytes at ((hq * 2 + x) * 16 + nt) * 64 + lane
   uint2* po = (uint2*)((uint16_t*)a.part_o + part * (kHeads * kLatent)) + ((hq * 2 + x) * 16 * 64 + lane);
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt)
     po[nt * 64] = make_uint2(pack_bf16x2(oacc[nt][0] * inv[0], oacc[nt][1] * inv[1]),
                              pack_bf16x2(oacc[nt][2] * inv[2], oacc[nt][3] * inv[3]));
 }
+
 
 // fp32 q and fp32 cache: a plain VALU path, 16 heads per workgroup, rows in chunks of 16.
 __global__ void __launch_bounds__(kThreads) decode_stage1_f32(Stage1Args a) {
