@@ -175,8 +175,10 @@ smla_status smla_sparse_decode(const smla_decode_args* args, void* workspace, si
 
 /* The two stages on their own, for callers that time or overlap them: stage 1 leaves
  * each split's partial output and LSE in the workspace, stage 2 (same arguments, same
- * workspace, enqueued after stage 1) merges them into out and lse. Stage 1 followed by
- * stage 2 is exactly smla_sparse_decode. */
+ * workspace, enqueued after stage 1) merges them into out and lse. On the bf16 path a
+ * token whose rows fit one split (lens[t] * page_size-clamped <= the split length) is
+ * written by stage 1 directly and skipped by stage 2. Stage 1 followed by stage 2 is
+ * exactly smla_sparse_decode. */
 smla_status smla_sparse_decode_stage1(const smla_decode_args* args, void* workspace, size_t workspace_bytes,
                                       void* stream);
 smla_status smla_sparse_decode_stage2(const smla_decode_args* args, void* workspace, size_t workspace_bytes,

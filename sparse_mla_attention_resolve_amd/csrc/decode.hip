@@ -49,6 +49,11 @@ struct Stage1Args {
   int64_t map_pt_stride;
   const int32_t* map_seq;
   int32_t map_R, map_pt_width, map_log2_page;
+  // outputs, written by stage 1 itself for a token whose rows fit one split (bf16 path)
+  void* out;
+  int64_t out_tok_stride, out_head_stride;
+  float* lse;
+  int64_t lse_tok_stride;
 };
 
 // Physical slot of position p of token t's table row, or -1 when masked.
@@ -602,14 +607,26 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   chunk_step<KV, false, true>(kvbuf[(nchunks - 1) % kNBuf], kvbuf[(nchunks - 1) % kNBuf], off, x, g, c, qf, sl, sr,
                               pa, oacc);
 
-  // ---- normalise, write the split's partials
+  // ---- normalise. A token whose rows fit one split is finished here; the others leave
+  // their partials for stage 2.
   const float l = sum_rows(l_part);              // head h0 + c, all rows of the split
-  const int64_t part = (int64_t)t * a.S + s;
-  if (x == 0 && g == 0) a.part_lse[part * a.H + h0 + c] = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  const float lse_c = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
   const float inv_c = l > 0.f ? 1.0f / l : 0.0f;
   float inv[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) inv[v] = __shfl(inv_c, 4 * g + v, 64);
+  if (len <= a.rows_per_split) {
+    uint16_t* ob = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)(h0 + 4 * g) * a.out_head_stride +
+                   256 * x + c;
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ob[v * a.out_head_stride + 16 * nt] = (uint16_t)f32_to_bf16_rne(oacc[nt][v] * inv[v]);
+    if (a.lse && x == 0 && g == 0) a.lse[(int64_t)t * a.lse_tok_stride + h0 + c] = lse_c;
+    return;
+  }
+  const int64_t part = (int64_t)t * a.S + s;
+  if (x == 0 && g == 0) a.part_lse[part * a.H + h0 + c] = lse_c;
   // bf16 partials in the accumulators' own order, so that one store instruction writes 512
   // contiguous bytes: lane (g, c) of wave (hq, x) stores heads h0 + 4g .. +3 of column
   // 256x + 16nt + c as 8 bytes at ((hq * 2 + x) * 16 + nt) * 64 + lane
@@ -791,6 +808,7 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2_packed(Stage2Args a)
   const int hbase = 4 * q;
   int len = a.lens[t];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+  if (len > 0 && len <= a.rows_per_split) return;      // one split: stage 1 wrote the output
   const int nact = min(a.S, (len + a.rows_per_split - 1) / a.rows_per_split);
   const int64_t base = (int64_t)t * a.S;
   const int64_t off = ((((hq * 2 + x) * 16 + nt) * 4 + g) * 16 + 4 * cq) * 4;   // bf16 elements
@@ -877,6 +895,11 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   a.T = d.T;
   a.part_o = (float*)ws;
   a.part_lse = (float*)((char*)ws + plan.part_o_bytes);
+  a.out = d.out;
+  a.out_tok_stride = d.out_tok_stride;
+  a.out_head_stride = d.out_head_stride;
+  a.lse = d.lse;
+  a.lse_tok_stride = d.lse_tok_stride;
   a.map_req = nullptr;
   a.map_pt = nullptr;
   a.map_pt_stride = 0;
