@@ -42,8 +42,10 @@ struct Stage1Args {
   int32_t T;
   float* part_o;            // fp32 path: [T][S][H][512]; bf16 path: bf16 in the packed order below
   float* part_lse;          // [T][S][H], natural log
-  // page map: when map_req is set, the (page size 1) table holds request-relative positions,
-  // which the kernel resolves through the request's page-table row
+  // page map: when `mapped` is set, the (page size 1) table holds request-relative
+  // positions, which the kernel resolves through the request's page-table row. map_req is
+  // always a valid [T] array (lens when unmapped), so its load needs no branch.
+  int32_t mapped;
   const int32_t* map_req;
   const int32_t* map_pt;
   int64_t map_pt_stride;
@@ -245,11 +247,12 @@ struct Offsets {
 // and / or O += P V over another chunk's columns 256x .. 256x+255 (16 MFMAs, one per
 // 16-column tile), interleaved so that the matrix unit always has independent work while
 // the operand reads run kAhead steps ahead. sl receives the latent part of the scores, sr
-// the rotary part (fp8 only; bf16 sums both into sl).
-template <int KV, bool DO_S, bool DO_PV>
+// the rotary part (fp8 only; bf16 sums both into sl). after_step(k) runs after step k's
+// MFMAs are issued (the caller spreads its gathers of a later chunk over the steps).
+template <int KV, bool DO_S, bool DO_PV, typename Hook>
 __device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, const Offsets<KV>& off, int x, int g,
                                            int c, const bf16x8 (&qf)[kQLoads], f32x4& sl, f32x4& sr,
-                                           const bf16x8& pa, f32x4 (&oacc)[16]) {
+                                           const bf16x8& pa, f32x4 (&oacc)[16], Hook&& after_step) {
   constexpr bool kFp8 = KV == SMLA_FP8_E4M3;
   constexpr int kRowBytes = Lay<KV>::kUnits * 16;
   constexpr int kSteps = DO_S ? 18 : 16;
@@ -307,6 +310,7 @@ __device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, con
         oacc[k] = mfma16x16x32(pa, b, oacc[k]);
       }
     }
+    after_step(k);
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (DO_S) {
@@ -351,34 +355,51 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int h0 = 16 * hq;
   const bool hi = w < kHiWaves;
 
-  // the scalar loads the prologue depends on go out together
+  // the scalar loads the prologue depends on go out together: the token's length and
+  // request (no branch: map_req is lens when the table holds slots)
   const int lp = a.log2_page;
   const int r0 = s * a.rows_per_split;
-  const int len = token_len(a, t);
-  const bool mapped = a.map_req != nullptr;
-  int32_t req = mapped ? a.map_req[t] : -1;
-  int32_t seq = 0;
-  if (mapped) {
-    if (req >= 0 && req < a.map_R) seq = a.map_seq[req]; else req = -1;
-  }
+  const bool mapped = a.mapped != 0;
+  const int len_raw = a.lens[t];
+  const int req_raw = a.map_req[t];
+  const int len = len_raw < 0 ? 0 : (len_raw > a.max_len ? a.max_len : len_raw);
 
-  // ---- prologue. The waves copy the split's table entries and the token's q straight into
-  // LDS, so that no register waits for memory before the first gathers go out: entries
-  // table[t][e0 .. e0 + n_ent) (slots when the page size is 1, page ids otherwise) into
-  // slot_s / page_s, and q, in the order the lanes read it back (head quarter hq: piece ks
-  // of lane (g, c) = head 16hq + c, dims 32ks + 8g .. +7), into ring slots 2.. (free until
-  // the chunk gathers reach them). Wave (hq, x) copies pieces 9x .. 9x+8 of quarter hq.
+  // ---- prologue. The waves copy into LDS, with no register waiting for memory before the
+  // first gathers go out:
+  //   - the split's table entries table[t][e0 .. e0 + n_ent) (slots when the page size is 1,
+  //     page ids otherwise) into slot_s / page_s;
+  //   - for a page-mapped table, the request's page-table row into ring slot 1 (free until
+  //     chunk 1 is gathered), so that resolving positions needs no further memory trip;
+  //   - q, in the order the lanes read it back (head quarter hq: piece ks of lane (g, c) =
+  //     head 16hq + c, dims 32ks + 8g .. +7), into ring slots 2.. (free until the chunk
+  //     gathers reach them). Wave (hq, x) copies pieces 9x .. 9x+8 of quarter hq.
   const int32_t* trow = a.table + (int64_t)t * a.table_stride;
   const int e0 = r0 >> lp;
   const int n_ent = lp == 0 ? min(a.rows_per_split, a.max_len - r0)
                             : min((r0 + a.rows_per_split - 1) >> lp, a.table_width - 1) - e0 + 1;
   static_assert((kNBuf - 2) * kChunkBytes >= 4 * kQLoads * 1024, "q must fit the ring slots from 2 on");
   char* const qlds = kvbuf[2] + hq * (kQLoads * 1024);
+  const int32_t* const prow_lds = (const int32_t*)kvbuf[1];
+  const bool row_in_lds = a.map_pt_width <= kChunkBytes / 4;
+  int32_t req = -1, seq = 0;
   {
     int32_t* ent = lp == 0 ? slot_s : page_s;
     for (int k = w; k * 64 < n_ent; k += kS1Waves) {
       const int e = k * 64 + lane;
       dma4(e < n_ent ? (const void*)(trow + e0 + e) : (const void*)kZeroRow, (char*)(ent + k * 64));
+    }
+    if (mapped) {
+      if (req_raw >= 0 && req_raw < a.map_R) {
+        req = req_raw;
+        seq = a.map_seq[req];
+      }
+      if (row_in_lds) {
+        const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
+        for (int k = w; k * 64 < a.map_pt_width; k += kS1Waves) {
+          const int e = k * 64 + lane;
+          dma4(e < a.map_pt_width ? (const void*)(ptrow + e) : (const void*)kZeroRow, (char*)(prow_lds + k * 64));
+        }
+      }
     }
     const uint16_t* qh = a.q + (int64_t)t * a.q_tok_stride + (int64_t)(h0 + c) * a.q_head_stride + 8 * g;
 #pragma unroll
@@ -386,7 +407,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       const int ks = 9 * x + k;
       dma16(qh + 32 * ks, qlds + ks * 1024);
     }
-    wait_vmcnt<kQLoads / 2>();                  // this wave's entries (issued first) are in LDS
+    wait_vmcnt<kQLoads / 2>();                  // this wave's entries and row (issued first) are in LDS
   }
   if (r0 >= len) {                              // inactive split: stage 2 never reads it
     wait_vmcnt<0>();                            // no copy may land after the workgroup is gone
@@ -401,8 +422,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   // page id, or a slot outside the pool)
   if (mapped) {
     // positions -> slots exactly as smla_resolve_slots computes them: a position counts when
-    // 0 <= pos < the request's context and its page is inside the row with an id >= 0. Both
-    // of a thread's page-id loads are issued before either is used.
+    // 0 <= pos < the request's context and its page is inside the row with an id >= 0
     constexpr int kPer = kMaxSplitRows / kS1Threads;
     static_assert(kMaxSplitRows % kS1Threads == 0, "rows per thread");
     const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
@@ -414,7 +434,9 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       const int i = tid + k * kS1Threads;
       pos[k] = i < nrows ? slot_s[i] : -1;
       ok[k] = req >= 0 && pos[k] >= 0 && pos[k] < seq && (pos[k] >> mlp) < a.map_pt_width;
-      page[k] = ptrow[ok[k] ? (pos[k] >> mlp) : 0];
+      // the row is in LDS unless it is longer than a ring slot; then each thread loads its
+      // page ids (all before any is used)
+      page[k] = !ok[k] ? -1 : row_in_lds ? prow_lds[pos[k] >> mlp] : ptrow[pos[k] >> mlp];
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -472,32 +494,42 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     const int row = pos / L::kUnits, unit = swz<KV>(row, pos % L::kUnits);   // the swizzle is an involution
     lpos[k] = row | (unit << 8);
   }
-  auto issue = [&](int ci) {
-    char* base = kvbuf[ci % kNBuf];
-    const int32_t* srow = slot_s + ci * kChunk;
-    // every slot is read before the first copy goes out: a copy's asm statement is a memory
-    // barrier for the compiler, so a read placed after one would wait for LDS on its own
-    int32_t sls[kLoadsHi];
-#pragma unroll
-    for (int k = 0; k < kLoadsHi; ++k) sls[k] = (k < kLoadsLo || hi) ? srow[lpos[k] & 0xff] : -1;
-#pragma unroll
-    for (int k = 0; k < kLoadsHi; ++k) {
-      if (k == kLoadsLo && !hi) break;
-      const int32_t sl = sls[k];
-      const int unit = lpos[k] >> 8;
-      const bool live = sl >= 0;
-      const uint32_t slot = live ? (uint32_t)sl : 0u;
-      const char* src;
-      if constexpr (!kFp8) {
-        src = (live ? (const char*)a.kv.rows : (const char*)kZeroRow) + (uint64_t)slot * row_stride32 + unit * 16;
-      } else {
-        const bool lat = unit < 32;
-        const char* plane = live ? (lat ? lat8 : rope16_m32) : (const char*)kZeroRow;
-        src = plane + (uint64_t)slot * (lat ? lat8_stride32 : rope16_stride32) + unit * 16;
-      }
-      dma16(src, base + (k * kS1Waves + w) * 1024);
-    }
+  // a chunk's copies in two steps: src_of reads the slots and forms each copy's source
+  // address (every slot is read before the first copy goes out: a copy's asm statement is
+  // a memory barrier for the compiler, so a read placed after one would wait for LDS on
+  // its own); fire(k) then issues copy k, possibly interleaved with other work
+  struct Copies {
+    int32_t slot[kLoadsHi];                     // -1: masked row, copied from the zero row
   };
+  auto src_of = [&](int ci) {
+    Copies cp;
+    const int32_t* srow = slot_s + ci * kChunk;
+#pragma unroll
+    for (int k = 0; k < kLoadsHi; ++k) cp.slot[k] = (k < kLoadsLo || hi) ? srow[lpos[k] & 0xff] : -1;
+    return cp;
+  };
+  auto fire = [&](const Copies& cp, int ci, int k) {
+    if (!(k < kLoadsLo || hi)) return;
+    const int32_t sl = cp.slot[k];
+    const int unit = lpos[k] >> 8;
+    const bool live = sl >= 0;
+    const uint32_t slot = live ? (uint32_t)sl : 0u;
+    const char* src;
+    if constexpr (!kFp8) {
+      src = (live ? (const char*)a.kv.rows : (const char*)kZeroRow) + (uint64_t)slot * row_stride32 + unit * 16;
+    } else {
+      const bool lat = unit < 32;
+      const char* plane = live ? (lat ? lat8 : rope16_m32) : (const char*)kZeroRow;
+      src = plane + (uint64_t)slot * (lat ? lat8_stride32 : rope16_stride32) + unit * 16;
+    }
+    dma16(src, kvbuf[ci % kNBuf] + (k * kS1Waves + w) * 1024);
+  };
+  auto issue = [&](int ci) {
+    const Copies cp = src_of(ci);
+#pragma unroll
+    for (int k = 0; k < kLoadsHi; ++k) fire(cp, ci, k);
+  };
+  auto no_hook = [](int) {};
 
   // chunks 0 and 1 go out first (their ring slots hold no q); once q has landed every wave
   // moves its quarter to registers, and after every wave has done so the slots q occupied
@@ -588,7 +620,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   // scores of chunk 0
   wait_chunks_w<kNBuf - 2, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 2, nchunks - 1));
   lds_barrier();
-  chunk_step<KV, true, false>(kvbuf[0], kvbuf[0], off, x, g, c, qf, sl, sr, pa, oacc);
+  chunk_step<KV, true, false>(kvbuf[0], kvbuf[0], off, x, g, c, qf, sl, sr, pa, oacc, no_hook);
   softmax(0);
 
   // iteration ci: O += P V over chunk ci together with the scores of chunk ci + 1. The
@@ -597,15 +629,20 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   for (int ci = 0; ci + 1 < nchunks; ++ci) {
     wait_chunks_w<kNBuf - 3, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 3, nchunks - 2 - ci));
     lds_barrier();
-    chunk_step<KV, true, true>(kvbuf[(ci + 1) % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc);
-    // the next gathers go out once this step's work is issued: a copy instruction can wait
-    // for room in the compute unit's memory queue, and it must not hold up chunks that
-    // have already landed
-    if (ci + kNBuf - 1 < nchunks) issue(ci + kNBuf - 1);
+    // the gathers of chunk ci + kNBuf - 1 go out one at a time among this step's MFMAs: a
+    // copy instruction can wait for room in the compute unit's memory queue, and the MFMAs
+    // already issued keep the matrix unit busy meanwhile
+    const int cn = ci + kNBuf - 1;
+    const bool refill = cn < nchunks;
+    const Copies cp = src_of(refill ? cn : ci);   // (ci: a valid chunk whose slots go unused)
+    chunk_step<KV, true, true>(kvbuf[(ci + 1) % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
+                               [&](int k) {
+                                 if (refill && (k & 3) == 1 && (k >> 2) < kLoadsHi) fire(cp, cn, k >> 2);
+                               });
     softmax(ci + 1);
   }
   chunk_step<KV, false, true>(kvbuf[(nchunks - 1) % kNBuf], kvbuf[(nchunks - 1) % kNBuf], off, x, g, c, qf, sl, sr,
-                              pa, oacc);
+                              pa, oacc, no_hook);
 
   // ---- normalise. A token whose rows fit one split is finished here; the others leave
   // their partials for stage 2.
@@ -900,7 +937,8 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   a.out_head_stride = d.out_head_stride;
   a.lse = d.lse;
   a.lse_tok_stride = d.lse_tok_stride;
-  a.map_req = nullptr;
+  a.mapped = map != nullptr;
+  a.map_req = d.lens;                           // a valid [T] array when there is no map
   a.map_pt = nullptr;
   a.map_pt_stride = 0;
   a.map_seq = nullptr;
