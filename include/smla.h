@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 2
+#define SMLA_ABI_VERSION 3
 
 #define SMLA_LATENT 512          /* latent (value) columns of a cache row */
 #define SMLA_ROPE 64             /* rotary columns of a cache row */
@@ -134,9 +134,13 @@ smla_status smla_resolve_slots(const int32_t* idx, int64_t idx_stride, const int
  * Breakthrough"). lens[t] is clamped to [0, table_width * page_size].
  *
  * Stage 1 splits each token's rows into num_splits contiguous ranges and computes, per
- * range, a partial output and its log-sum-exp; stage 2 merges the ranges by LSE
+ * range, a partial output and its log-sum-exp; the ranges are then merged by LSE
  * (IBM Triton paged-attention explainer, section 4 table, "Parallel Tiled Softmax"),
- * all on `stream`, through the workspace.
+ * all on `stream`, through the workspace. On the bf16 path (T <= 4096) the merge runs at
+ * the end of stage 1: the workgroups of a token take tickets on a counter word in the
+ * workspace and share the merge once every partial is written (each waits a bounded
+ * time for the others; the last to arrive merges whatever was given up), so one kernel
+ * produces out and lse. Otherwise a second kernel (stage 2) merges.
  *
  * Supported combinations:
  *   q_dtype SMLA_BF16, kv dtype SMLA_BF16 or SMLA_FP8_E4M3, H == 64 (bf16 MFMA path);
@@ -162,23 +166,36 @@ typedef struct {
 } smla_decode_args;
 
 /* Workspace bytes smla_sparse_decode needs for these arguments (a function of the
- * scalar fields only). Validates like smla_sparse_decode, pointers excepted. */
+ * scalar fields only). Validates like smla_sparse_decode, pointers excepted.
+ *
+ * Workspace contract (bf16 path): its first 256 KiB hold the merge counters and must be
+ * zero before the workspace is first used (allocate it zero-filled, or call
+ * smla_sparse_decode_workspace_init once); every call returns the counters it used to
+ * zero, so a workspace may be reused for calls of any shape, and inside a captured graph.
+ * The rest (the partial outputs) needs no initial contents. Calls that share a workspace
+ * must not overlap in time (they would share counters and partials). */
 smla_status smla_sparse_decode_workspace(const smla_decode_args* args, size_t* bytes);
+
+/* Zero the merge counters of a workspace of `workspace_bytes` bytes (a fill kernel on
+ * `stream`, so it may be captured in a graph); needed once per workspace unless it was
+ * allocated zero-filled. Errors: SMLA_ERR_NULL (NULL workspace with a nonzero size),
+ * SMLA_ERR_ALIGN (not 256-byte aligned), SMLA_ERR_DEVICE (launch failure). */
+smla_status smla_sparse_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of splits smla_sparse_decode uses for these arguments. */
 smla_status smla_sparse_decode_splits(const smla_decode_args* args, int32_t* num_splits);
 
-/* Enqueue stage 1 and stage 2. `workspace` (256-byte aligned) must hold at least the
- * bytes smla_sparse_decode_workspace reports; its contents on entry do not matter. */
+/* Enqueue the decode. `workspace` (256-byte aligned) must hold at least the bytes
+ * smla_sparse_decode_workspace reports and meet the contract above. */
 smla_status smla_sparse_decode(const smla_decode_args* args, void* workspace, size_t workspace_bytes,
                                void* stream);
 
-/* The two stages on their own, for callers that time or overlap them: stage 1 leaves
- * each split's partial output and LSE in the workspace, stage 2 (same arguments, same
- * workspace, enqueued after stage 1) merges them into out and lse. On the bf16 path a
- * token whose rows fit one split (lens[t] * page_size-clamped <= the split length) is
- * written by stage 1 directly and skipped by stage 2. Stage 1 followed by stage 2 is
- * exactly smla_sparse_decode. */
+/* The two stages on their own, for callers that time or overlap them. Stage 1 followed
+ * by stage 2 (same arguments, same workspace) is exactly smla_sparse_decode. When stage 1
+ * merges the splits itself (bf16 path, T <= 4096) it writes out and lse, and stage 2
+ * enqueues nothing; otherwise stage 1 leaves each split's partial output and LSE in the
+ * workspace and stage 2 merges them. On the bf16 path a token whose rows fit one split is
+ * always written by stage 1 directly. */
 smla_status smla_sparse_decode_stage1(const smla_decode_args* args, void* workspace, size_t workspace_bytes,
                                       void* stream);
 smla_status smla_sparse_decode_stage2(const smla_decode_args* args, void* workspace, size_t workspace_bytes,

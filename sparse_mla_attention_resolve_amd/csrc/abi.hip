@@ -80,6 +80,26 @@ int32_t device_cus() {
   return n;
 }
 
+// Ticks of the device's wall clock (s_memrealtime) in `us` microseconds; 100 MHz when the
+// attribute is unavailable.
+int32_t wall_ticks(int32_t us) {
+  static int32_t cached_khz[64] = {};
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return us * 100;
+  }
+  if (dev >= 0 && dev < 64 && cached_khz[dev] > 0) {
+    khz = cached_khz[dev];
+  } else if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) {
+    (void)hipGetLastError();
+    khz = 100000;
+  } else if (dev >= 0 && dev < 64) {
+    cached_khz[dev] = khz;
+  }
+  return (int32_t)((int64_t)khz * us / 1000);
+}
+
 // Split count and rows per split, from the scalar arguments and the device's compute-unit
 // count. A stage-1 workgroup fills a compute unit (its LDS ring), so the default gives
 // every compute unit one (token, split) and no second round: floor(CUs / T) splits per
@@ -160,7 +180,13 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   // the bf16 path keeps its partial outputs in bf16, the fp32 path in fp32
   plan->part_o_bytes = (size_t)a->T * plan->S * a->H * SMLA_LATENT * (bf16 ? 2 : 4);
   plan->part_lse_bytes = (size_t)a->T * plan->S * a->H * sizeof(float);
-  plan->ws_bytes = (plan->part_o_bytes + plan->part_lse_bytes + 255) / 256 * 256;
+  // bf16 q: the splits of a token merge at the end of stage 1 through a word per token at
+  // the head of the workspace; a workgroup waits for its token's other splits (at most
+  // 10 us) only when the whole grid is resident at once
+  plan->sync_bytes = bf16 ? smla::kSyncBytes : 0;
+  plan->fused = bf16 && a->T <= smla::kSyncTokens;
+  plan->wait_ticks = (int64_t)a->T * plan->S <= device_cus() ? wall_ticks(10) : 0;
+  plan->ws_bytes = plan->sync_bytes + (plan->part_o_bytes + plan->part_lse_bytes + 255) / 256 * 256;
   return SMLA_OK;
 }
 
@@ -221,6 +247,15 @@ smla_status smla_sparse_decode_workspace(const smla_decode_args* args, size_t* b
   if (st != SMLA_OK) return st;
   *bytes = args->T == 0 ? 0 : plan.ws_bytes;
   return ok();
+}
+
+smla_status smla_sparse_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "smla_sparse_decode_workspace_init";
+  if (workspace_bytes == 0) return ok();
+  CHECK(workspace != nullptr, SMLA_ERR_NULL, "%s: workspace is NULL", fn);
+  CHECK(aligned(workspace, 256), SMLA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  const size_t n = workspace_bytes < smla::kSyncBytes ? workspace_bytes / 16 * 16 : smla::kSyncBytes;
+  return device_status(smla::launch_zero(workspace, n, (hipStream_t)stream), fn);
 }
 
 smla_status smla_sparse_decode_splits(const smla_decode_args* args, int32_t* num_splits) {

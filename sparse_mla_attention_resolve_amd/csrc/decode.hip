@@ -56,6 +56,11 @@ struct Stage1Args {
   int64_t out_tok_stride, out_head_stride;
   float* lse;
   int64_t lse_tok_stride;
+  // merge inside stage 1 (bf16 q): the per-token words at the head of the workspace
+  // (nullptr: stage 2 merges), and how long a workgroup may wait for its token's other
+  // splits, in wall-clock ticks (0: never wait)
+  uint32_t* sync;
+  int32_t wait_ticks;
 };
 
 // Physical slot of position p of token t's table row, or -1 when masked.
@@ -319,6 +324,161 @@ __device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, con
   }
 }
 
+// ---- merge of a token's splits inside stage 1
+//
+// The split workgroups of a token write their partials with agent-coherent stores (sc1:
+// written through to the device-wide coherence point) and read the other workgroups'
+// partials with agent-coherent loads, so no cache-wide write-back or invalidate is needed:
+// a workgroup's stores are complete (s_waitcnt vmcnt(0)) before it takes its ticket, and
+// a reader issues its loads only after it has seen every ticket.
+//
+// Word of token t (zero on entry, zero again when its last workgroup leaves):
+//   bits 0 .. 8    tickets taken (arrivals), bits 9 .. 17 departures,
+//   bits 18 .. 25  parts given up by tickets 0 .. 7.
+// The merge has 8 parts (head quarter x column half). Ticket q < 8 owns parts q, q + nact,
+// ... < 8. A ticket holder waits a bounded time for the remaining arrivals and then merges
+// its parts; when the time runs out it gives them up with one atomic add, which also tells
+// it whether the last arrival has already come (then it merges them after all). The last
+// arrival never waits: it merges its own parts and every part given up before it came.
+constexpr uint32_t kArrMask = 0x1ff;
+constexpr int kExitShift = 9, kGiveUpShift = 18;
+constexpr int kBufFlags = 0x00020000;       // buffer descriptor word 3: 32-bit data format
+constexpr int kSc1 = 16;                    // cache-policy operand of buffer loads: sc1
+
+__device__ __forceinline__ uint32_t parts_of(int q, int nact) {
+  uint32_t m = 0;
+  if (q < 8)
+    for (int k = q; k < 8; k += nact) m |= 1u << k;
+  return m;
+}
+
+// Part p (0 .. 7) of token t's merge: heads 16(p >> 1) .. +15 x columns 256(p & 1) .. +255,
+// which are packed entries 1024p .. 1024p + 1023 of every split's partial. Thread i merges
+// entries 1024p + 2i and + 1: heads hb .. hb + 3 at columns col and col + 1 (the entries of
+// lanes c and c + 1 of one group g). Per batch of eight splits, 128 threads fetch the
+// part's 16 x 8 LSEs into LDS (`scratch`, 128 floats) while every thread has its eight
+// 16-byte slices in flight; the weights keep a running maximum:
+// O = sum_s exp(lse_s - lse) O_s with lse = log sum_s exp(lse_s).
+__device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact, int p, int tid, float* scratch) {
+  constexpr int kBatch = 8;
+  const int j = 1024 * p + 2 * tid;
+  const int lanep = j & 63, ntp = (j >> 6) & 15;
+  const int hp = 4 * (lanep >> 4);                       // head offset inside the part's 16
+  const int hb = 16 * (p >> 1) + hp;
+  const int col = 256 * (p & 1) + 16 * ntp + (lanep & 15);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((uint16_t*)a.part_o + (int64_t)t * a.S * (kHeads * kLatent)), (short)0, 0x7fffffff, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rl =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.part_lse + (int64_t)t * a.S * a.H), (short)0, 0x7fffffff, kBufFlags);
+  float mx[4], ws[4], acc[4][2];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    mx[v] = -INFINITY;
+    ws[v] = 0.f;
+    acc[v][0] = acc[v][1] = 0.f;
+  }
+  for (int s0 = 0; s0 < nact; s0 += kBatch) {
+    // (every thread loads an in-range LSE, unconditionally, so that no wait for it comes
+    // before the slices go out; only threads < 128 keep theirs)
+    const int ls = s0 + ((tid >> 4) & (kBatch - 1));
+    const float lv = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rl, ((ls < nact ? ls : s0) * a.H + 16 * (p >> 1) + (tid & 15)) * 4, 0, kSc1));
+    uint4 o[kBatch];
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      const int sp = s0 + jj < nact ? s0 + jj : s0;
+      o[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ro, sp * (kHeads * kLatent * 2) + 8 * j, 0, kSc1));
+    }
+    __syncthreads();                                     // the previous batch's LSEs are read
+    if (tid < 16 * kBatch) scratch[tid] = ls < nact ? lv * kLog2e : -INFINITY;   // base 2 from here on
+    __syncthreads();
+    float4 l[kBatch];
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) l[jj] = *(const float4*)(scratch + 16 * jj + hp);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float bm = mx[v];
+#pragma unroll
+      for (int jj = 0; jj < kBatch; ++jj) bm = fmaxf(bm, ((const float*)&l[jj])[v]);
+      if (bm == -INFINITY) continue;                     // nothing but empty splits so far
+      const float r = __builtin_amdgcn_exp2f(mx[v] - bm);   // 0 on the first non-empty pass
+      ws[v] *= r;
+      acc[v][0] *= r;
+      acc[v][1] *= r;
+#pragma unroll
+      for (int jj = 0; jj < kBatch; ++jj) {
+        const float lw = ((const float*)&l[jj])[v];
+        const float wgt = lw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lw - bm);
+        ws[v] += wgt;
+        // entry 2i: words x, y = heads (0, 1), (2, 3) at col; entry 2i + 1: z, w at col + 1
+        const uint32_t w0 = v < 2 ? o[jj].x : o[jj].y, w1 = v < 2 ? o[jj].z : o[jj].w;
+        acc[v][0] += wgt * bf16_to_f32((v & 1) ? (w0 >> 16) : (w0 & 0xffffu));
+        acc[v][1] += wgt * bf16_to_f32((v & 1) ? (w1 >> 16) : (w1 & 0xffffu));
+      }
+      mx[v] = bm;
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float inv = ws[v] > 0.f ? 1.0f / ws[v] : 0.f;
+    uint32_t* o = (uint32_t*)((uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)(hb + v) * a.out_head_stride + col);
+    *o = pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv);
+    if (a.lse && (p & 1) == 0 && ntp == 0 && (lanep & 15) == 0)
+      a.lse[(int64_t)t * a.lse_tok_stride + hb + v] = ws[v] > 0.f ? (mx[v] + log2f(ws[v])) * kLn2 : -INFINITY;
+  }
+}
+
+// Called by every active split workgroup of token t once its partial is stored, with nact >= 2 the
+// token's active splits.
+__device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int nact, int tid, float* scratch) {
+  __shared__ uint32_t bcast;
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this thread's partial stores are complete
+  __syncthreads();
+  uint32_t* const word = a.sync + (int64_t)t * kSyncStride;
+  if (tid == 0) bcast = __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t old = bcast;
+  const int q = (int)(old & kArrMask);
+  uint32_t todo = 0;
+  if (q == nact - 1) {
+    todo = parts_of(q, nact);
+    const uint32_t gave_up = (old >> kGiveUpShift) & 0xffu;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if ((gave_up >> k) & 1u) todo |= parts_of(k, nact);
+  } else if (q < 8) {
+    __syncthreads();                                           // every thread has read bcast
+    if (tid == 0) {
+      uint32_t seen = 0;
+      if (a.wait_ticks > 0) {
+        const uint64_t t0 = wall_clock64();
+        do {
+          if ((__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kArrMask) >= (uint32_t)nact) {
+            seen = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        } while (wall_clock64() - t0 < (uint64_t)a.wait_ticks);
+      }
+      if (!seen) {
+        const uint32_t o2 = __hip_atomic_fetch_add(word, 1u << (kGiveUpShift + q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        seen = (o2 & kArrMask) >= (uint32_t)nact;             // the last arrival came first: keep the parts
+      }
+      bcast = seen;
+    }
+    __syncthreads();
+    if (bcast) todo = parts_of(q, nact);
+  }
+#pragma unroll 1
+  for (int k = 0; k < 8; ++k)
+    if ((todo >> k) & 1u) merge_part(a, t, nact, k, tid, scratch);
+  if (tid == 0) {
+    const uint32_t o3 = __hip_atomic_fetch_add(word, 1u << kExitShift, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (((o3 >> kExitShift) & kArrMask) == (uint32_t)nact - 1)   // everyone else is done with the word
+      __hip_atomic_store(word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Stage 1. The scores are computed transposed, S^T = K Q^T (chunk rows are the M dimension
 // of a 16x16x32 MFMA tile, heads the N dimension, K = 576), so that lane (g, c) holds head
 // c's scores for rows 4g .. 4g+3 of its half. The two partners swap their tiles through LDS,
@@ -409,8 +569,18 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     }
     wait_vmcnt<kQLoads / 2>();                  // this wave's entries and row (issued first) are in LDS
   }
-  if (r0 >= len) {                              // inactive split: stage 2 never reads it
+  if (r0 >= len) {                              // inactive split: no merge reads it
     wait_vmcnt<0>();                            // no copy may land after the workgroup is gone
+    if (a.sync != nullptr && len == 0 && s == 0) {
+      // a token with no rows: zero output and lse -inf (stage 2 would write them otherwise)
+      uint16_t* ob = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride;
+#pragma unroll
+      for (int k = 0; k < kHeads * kLatent / 8 / kS1Threads; ++k) {
+        const int i = k * kS1Threads + tid;
+        *(uint4*)(ob + (int64_t)(i >> 6) * a.out_head_stride + 8 * (i & 63)) = make_uint4(0u, 0u, 0u, 0u);
+      }
+      if (a.lse && tid < kHeads) a.lse[(int64_t)t * a.lse_tok_stride + tid] = -INFINITY;
+    }
     return;
   }
   const int r1 = min(r0 + a.rows_per_split, len);
@@ -662,16 +832,24 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     if (a.lse && x == 0 && g == 0) a.lse[(int64_t)t * a.lse_tok_stride + h0 + c] = lse_c;
     return;
   }
+  // (agent-coherent stores: workgroups of this launch may merge them)
   const int64_t part = (int64_t)t * a.S + s;
-  if (x == 0 && g == 0) a.part_lse[part * a.H + h0 + c] = lse_c;
+  if (x == 0 && g == 0)
+    __hip_atomic_store((uint32_t*)a.part_lse + part * a.H + h0 + c, __float_as_uint(lse_c), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   // bf16 partials in the accumulators' own order, so that one store instruction writes 512
   // contiguous bytes: lane (g, c) of wave (hq, x) stores heads h0 + 4g .. +3 of column
   // 256x + 16nt + c as 8 bytes at ((hq * 2 + x) * 16 + nt) * 64 + lane
-  uint2* po = (uint2*)((uint16_t*)a.part_o + part * (kHeads * kLatent)) + ((hq * 2 + x) * 16 * 64 + lane);
+  uint64_t* po = (uint64_t*)((uint16_t*)a.part_o + part * (kHeads * kLatent)) + ((hq * 2 + x) * 16 * 64 + lane);
 #pragma unroll
-  for (int nt = 0; nt < 16; ++nt)
-    po[nt * 64] = make_uint2(pack_bf16x2(oacc[nt][0] * inv[0], oacc[nt][1] * inv[1]),
-                             pack_bf16x2(oacc[nt][2] * inv[2], oacc[nt][3] * inv[3]));
+  for (int nt = 0; nt < 16; ++nt) {
+    const uint64_t v = (uint64_t)pack_bf16x2(oacc[nt][0] * inv[0], oacc[nt][1] * inv[1]) |
+                       ((uint64_t)pack_bf16x2(oacc[nt][2] * inv[2], oacc[nt][3] * inv[3]) << 32);
+    __hip_atomic_store(po + nt * 64, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // (the LDS ring is idle from here on: its first slot holds the merge's LSE staging)
+  if (a.sync != nullptr)
+    merge_splits(a, t, min(a.S, (len + a.rows_per_split - 1) / a.rows_per_split), tid, (float*)kvbuf[0]);
 }
 
 
@@ -930,8 +1108,10 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   a.S = plan.S;
   a.H = d.H;
   a.T = d.T;
-  a.part_o = (float*)ws;
-  a.part_lse = (float*)((char*)ws + plan.part_o_bytes);
+  a.part_o = (float*)((char*)ws + plan.sync_bytes);
+  a.part_lse = (float*)((char*)ws + plan.sync_bytes + plan.part_o_bytes);
+  a.sync = plan.fused ? (uint32_t*)ws : nullptr;
+  a.wait_ticks = plan.wait_ticks;
   a.out = d.out;
   a.out_tok_stride = d.out_tok_stride;
   a.out_head_stride = d.out_head_stride;
@@ -965,7 +1145,7 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
     hipLaunchKernelGGL(decode_stage1_mfma<SMLA_FP8_E4M3>, dim3(plan.S * d.T), dim3(kS1Threads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !(stages & 2)) return e;
+  if (e != hipSuccess || !(stages & 2) || plan.fused) return e;   // fused: stage 1 has merged
 
   Stage2Args b;
   b.T = d.T;
@@ -986,6 +1166,21 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
     hipLaunchKernelGGL(decode_stage2, dim3(d.T * ((d.H + 1) / 2)), dim3(kS2Threads), 0, stream, b);
   else
     hipLaunchKernelGGL(decode_stage2_packed, dim3(d.T * (16 * 128 / kS2Threads)), dim3(kS2Threads), 0, stream, b);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ void zero_kernel(uint4* p, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+}  // namespace
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, stream, (uint4*)p, n16);
   return hipGetLastError();
 }
 

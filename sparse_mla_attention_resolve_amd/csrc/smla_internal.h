@@ -14,6 +14,15 @@ constexpr int kChunk = 32;
 // Most rows one stage-1 split may hold (its slot list is staged in LDS).
 constexpr int kMaxSplitRows = 1024;
 
+// Workspace bytes reserved, at offset 0, for the per-token words through which the split
+// workgroups of stage 1 share the merge (one 32-bit word per token, 64 bytes apart). The
+// region must hold zeros before a workspace is first used; every call returns the words it
+// touched to zero, so one buffer serves calls of any shape. Decodes of more tokens than it
+// covers merge in a separate stage-2 kernel.
+constexpr size_t kSyncBytes = 256 * 1024;
+constexpr int32_t kSyncStride = 16;                       // 32-bit words per token
+constexpr int32_t kSyncTokens = (int32_t)(kSyncBytes / (4 * kSyncStride));
+
 // Decode plan: everything the launches need, computed from scalar arguments only.
 struct DecodePlan {
   int32_t T, H, S;           // tokens, heads, splits
@@ -21,6 +30,9 @@ struct DecodePlan {
   int32_t max_len;           // table_width * page_size
   size_t part_o_bytes;       // [T, S, H, 512]: bf16 (packed order) on the bf16 path, fp32 on the fp32 path
   size_t part_lse_bytes;     // [T, S, H] fp32
+  bool fused;                 // bf16 q with T <= kSyncTokens: stage 1 merges the splits itself
+  int32_t wait_ticks;        // how long a stage-1 workgroup may wait for its token's other splits (wall-clock ticks)
+  size_t sync_bytes;         // kSyncBytes on the bf16 path, else 0 (the partials follow it)
   size_t ws_bytes;
 };
 
@@ -44,5 +56,8 @@ hipError_t launch_union(const int32_t* slots, int64_t slots_stride, const int32_
                         int64_t enc_stride, int32_t* lens, hipStream_t stream);
 
 hipError_t launch_prefill(const smla_prefill_args& a, hipStream_t stream);
+
+// Zero-fill bytes / 16 16-byte words at p (a kernel, so it may be captured in a graph).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace smla

@@ -25,7 +25,8 @@ STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_AL
           4: "SMLA_ERR_UNSUPPORTED", 5: "SMLA_ERR_RANGE", 6: "SMLA_ERR_WORKSPACE", 7: "SMLA_ERR_DEVICE"}
 STATUS_CODES = {v: k for k, v in STATUS.items()}
 
-EXPORTS = ["smla_resolve_slots", "smla_sparse_decode_workspace", "smla_sparse_decode_splits",
+EXPORTS = ["smla_resolve_slots", "smla_sparse_decode_workspace", "smla_sparse_decode_workspace_init",
+           "smla_sparse_decode_splits",
            "smla_sparse_decode", "smla_sparse_decode_stage1", "smla_sparse_decode_stage2",
            "smla_sparse_decode_topk", "smla_sparse_decode_topk_stage1",
            "smla_build_group_union", "smla_grouped_prefill", "smla_kv_write",
@@ -82,6 +83,7 @@ class smla_page_map(ctypes.Structure):
 _sig = {
     "smla_resolve_slots": [c_p, c_i64, c_p, c_p, c_i32, c_p, c_i64, c_i32, c_p, c_i32, c_i32, c_i32, c_p, c_i64, c_p],
     "smla_sparse_decode_workspace": [ctypes.POINTER(smla_decode_args), ctypes.POINTER(c_sz)],
+    "smla_sparse_decode_workspace_init": [c_p, c_sz, c_p],
     "smla_sparse_decode_splits": [ctypes.POINTER(smla_decode_args), ctypes.POINTER(c_i32)],
     "smla_sparse_decode": [ctypes.POINTER(smla_decode_args), c_p, c_sz, c_p],
     "smla_sparse_decode_stage1": [ctypes.POINTER(smla_decode_args), c_p, c_sz, c_p],
@@ -239,6 +241,17 @@ def _decode_args(q, kv: KvCache, table, lens, page_size, scale, out, lse, num_sp
     return a
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A decode workspace of at least nbytes bytes, zero-filled: its leading counter region
+    must hold zeros before first use, and every decode leaves it so (see smla.h)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def smla_sparse_decode_workspace_init(workspace: torch.Tensor, stream=None):
+    """Zero the merge counters of an existing workspace (a fill kernel on the stream)."""
+    _check(_lib.smla_sparse_decode_workspace_init(_ptr(workspace), workspace.numel(), _stream(stream)))
+
+
 def smla_sparse_decode_workspace(q, kv: KvCache, table, lens, page_size: int, scale: float,
                                  num_splits: int = 0) -> int:
     a = _decode_args(q, kv, table, lens, page_size, scale, None, None, num_splits)
@@ -269,7 +282,7 @@ def smla_sparse_decode(q, kv: KvCache, table, lens, page_size: int, scale: float
     need = c_sz(0)
     _check(_lib.smla_sparse_decode_workspace(ctypes.byref(a), ctypes.byref(need)))
     if workspace is None or workspace.numel() < need.value:
-        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need.value, q.device)
     _check(_lib.smla_sparse_decode(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
 
@@ -301,7 +314,7 @@ def smla_sparse_decode_topk(q, kv: KvCache, idx, valid, tok_req, page_table, seq
     need = c_sz(0)
     _check(_lib.smla_sparse_decode_workspace(ctypes.byref(a), ctypes.byref(need)))
     if workspace is None or workspace.numel() < need.value:
-        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need.value, q.device)
     _check(_lib.smla_sparse_decode_topk(ctypes.byref(a), ctypes.byref(m), _ptr(workspace), workspace.numel(),
                                         _stream(stream)))
     return out, lse
@@ -319,7 +332,7 @@ class DecodeCall:
         need = c_sz(0)
         _check(_lib.smla_sparse_decode_workspace(ctypes.byref(self.args), ctypes.byref(need)))
         if workspace is None:
-            workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=q.device)
+            workspace = new_workspace(need.value, q.device)
         self.workspace = workspace
         self.map = None if page_map is None else _page_map(*page_map)
         self.keep = (q, kv, table, lens, out, lse, page_map)

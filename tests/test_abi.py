@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_struct_sizes_and_version():
     lib = S.lib()
-    assert lib.smla_abi_version() == 2
+    assert lib.smla_abi_version() == 3
     assert lib.smla_sizeof_page_map() == ctypes.sizeof(S.smla_page_map) == 48
     assert lib.smla_sizeof_kv() == ctypes.sizeof(S.smla_kv) == 80
     assert lib.smla_sizeof_decode_args() == ctypes.sizeof(S.smla_decode_args)

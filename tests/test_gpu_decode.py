@@ -175,7 +175,7 @@ def test_decode_graph_replay():
     slots = torch.empty_like(idx)
     out = torch.empty((8, 64, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((8, 64), dtype=torch.float32, device="cuda")
-    ws = torch.empty(smla.smla_sparse_decode_workspace(qt, kv, idx, valid, 1, c.scale), dtype=torch.uint8, device="cuda")
+    ws = smla.new_workspace(smla.smla_sparse_decode_workspace(qt, kv, idx, valid, 1, c.scale), "cuda")
 
     def step():
         smla.smla_resolve_slots(idx, valid, req, pt, ctx, lay.page_size, slots=slots)
@@ -199,6 +199,7 @@ def test_decode_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+        assert int(ws[:256 * 1024].count_nonzero()) == 0, "merge counters not returned to zero by a replay"
 
 
 @pytest.mark.parametrize("name", ["decode_bf16_b32", "decode_ragged_b128", "decode_fp8_b64"])
@@ -246,3 +247,71 @@ def test_topk_fused_masks(splits):
     o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, oslots, valid, 1, 1 / 16)
     _check(b[0], b[1], o_ref, l_ref, BF16_ATOL, BF16_RTOL, f"fused masks splits={splits}")
     assert int((oslots >= 0).sum(axis=1).min()) == 0 and int((oslots >= 0).sum(axis=1).max()) > 100
+
+
+def _ws_counters(ws):
+    return ws[:256 * 1024]
+
+
+def test_merge_counters_return_to_zero_and_workspace_reuse():
+    """The splits of a token merge inside stage 1 through counters at the head of the
+    workspace: each call leaves them zero, so one workspace serves calls of different
+    shapes one after another."""
+    cases = []
+    for seed, lens, splits in ((21, [2048, 900, 33, 1, 0, 1500, 64, 2048], 8), (22, [700, 2048, 5], 3)):
+        q, table, lens, live, vals = _random_case(seed, len(lens), 2048, lens, 30000)
+        cases.append((q, table, lens, live, vals, splits))
+    need = max(smla.smla_sparse_decode_workspace(gc.q_tensor(c[0], "bf16"), smla.KvCache.empty(smla.SMLA_BF16, 8),
+                                                 _t(c[1]), _t(c[2]), 1, 1 / 16, num_splits=c[5]) for c in cases)
+    ws = smla.new_workspace(need, "cuda")
+    for rep in range(2):
+        for q, table, lens, live, vals, splits in cases:
+            kv, pool = _pools(live, vals, 30000, "bf16")
+            out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(table), _t(lens), 1, 1 / 16,
+                                               num_splits=splits, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(_ws_counters(ws).count_nonzero()) == 0, "merge counters not returned to zero"
+            o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, table, lens, 1, 1 / 16)
+            _check(out, lse, o_ref, l_ref, BF16_ATOL, BF16_RTOL, f"reuse rep={rep} splits={splits}")
+
+
+def test_merge_when_grid_exceeds_device():
+    """More (token, split) workgroups than compute units: no workgroup waits for another,
+    the last of each token to finish merges its splits."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    splits = 8
+    T = cus // splits + 9
+    lens = [2048 - 37 * (t % 11) for t in range(T)]
+    q, table, lens, live, vals = _random_case(23, T, 2048, lens, 200000)
+    kv, pool = _pools(live, vals, 200000, "bf16")
+    assert T * splits > cus
+    out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(table), _t(lens), 1, 1 / 16, num_splits=splits)
+    o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, table, lens, 1, 1 / 16)
+    _check(out, lse, o_ref, l_ref, BF16_ATOL, BF16_RTOL, "grid larger than the device")
+
+
+def test_workspace_init_clears_counters():
+    lens = [2048, 1000, 3]
+    q, table, lens, live, vals = _random_case(24, 3, 2048, lens, 30000)
+    kv, pool = _pools(live, vals, 30000, "bf16")
+    qt = gc.q_tensor(q, "bf16")
+    need = smla.smla_sparse_decode_workspace(qt, kv, _t(table), _t(lens), 1, 1 / 16, num_splits=4)
+    ws = torch.full((need,), 0x5a, dtype=torch.uint8, device="cuda")
+    smla.smla_sparse_decode_workspace_init(ws)
+    out, lse = smla.smla_sparse_decode(qt, kv, _t(table), _t(lens), 1, 1 / 16, num_splits=4, workspace=ws)
+    o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, table, lens, 1, 1 / 16)
+    _check(out, lse, o_ref, l_ref, BF16_ATOL, BF16_RTOL, "initialised workspace")
+
+
+def test_merge_in_stage2_past_counter_region():
+    """More tokens than the workspace's counter words cover (4096): stage 2 merges the
+    splits; a sample of tokens against the oracle."""
+    T = 4097
+    rng = np.random.default_rng(25)
+    lens = rng.integers(1100, 2049, T)
+    q, table, lens, live, vals = _random_case(25, T, 2048, lens, 30000)
+    kv, pool = _pools(live, vals, 30000, "bf16")
+    out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(table), _t(lens), 1, 1 / 16, num_splits=2)
+    sample = [0, 1, 2047, 4095, 4096]
+    o_ref, l_ref = oracle.sparse_decode(q[sample], "bf16", pool, table[sample], lens[sample], 1, 1 / 16)
+    _check(out[sample], lse[sample], o_ref, l_ref, BF16_ATOL, BF16_RTOL, "stage-2 merge")
