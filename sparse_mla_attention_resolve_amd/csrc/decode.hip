@@ -515,34 +515,40 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int h0 = 16 * hq;
   const bool hi = w < kHiWaves;
 
-  // the scalar loads the prologue depends on go out together: the token's length and
-  // request (no branch: map_req is lens when the table holds slots)
+  // ---- prologue. Everything the first gathers need goes out as early as it can:
+  //   - at once (it needs only the kernel's arguments): q, in the order the lanes read it
+  //     back (head quarter hq: piece ks of lane (g, c) = head 16hq + c, dims 32ks + 8g .. +7),
+  //     into ring slots 2.. (wave (hq, x) copies pieces 9x .. 9x+8 of quarter hq); the split's
+  //     table entries table[t][e0 .. e0 + n_ent) (slots when the page size is 1, page ids
+  //     otherwise) into slot_s / page_s; the scalar loads of the token's length and request
+  //     (no branch: map_req is lens when the table holds slots);
+  //   - once the request is known, for a page-mapped table: its context length (a scalar
+  //     load) and its page-table row, into ring slot 1 when the row fits there.
+  // All of it lands before the slots are built, so that building them touches LDS only (a
+  // register that a global load may still be writing would make the compiler wait for
+  // every copy in flight, since it does not see them).
   const int lp = a.log2_page;
   const int r0 = s * a.rows_per_split;
   const bool mapped = a.mapped != 0;
   const int len_raw = a.lens[t];
   const int req_raw = a.map_req[t];
   const int len = len_raw < 0 ? 0 : (len_raw > a.max_len ? a.max_len : len_raw);
-
-  // ---- prologue. The waves copy into LDS, with no register waiting for memory before the
-  // first gathers go out:
-  //   - the split's table entries table[t][e0 .. e0 + n_ent) (slots when the page size is 1,
-  //     page ids otherwise) into slot_s / page_s;
-  //   - for a page-mapped table, the request's page-table row into ring slot 1 (free until
-  //     chunk 1 is gathered), so that resolving positions needs no further memory trip;
-  //   - q, in the order the lanes read it back (head quarter hq: piece ks of lane (g, c) =
-  //     head 16hq + c, dims 32ks + 8g .. +7), into ring slots 2.. (free until the chunk
-  //     gathers reach them). Wave (hq, x) copies pieces 9x .. 9x+8 of quarter hq.
   const int32_t* trow = a.table + (int64_t)t * a.table_stride;
   const int e0 = r0 >> lp;
   const int n_ent = lp == 0 ? min(a.rows_per_split, a.max_len - r0)
                             : min((r0 + a.rows_per_split - 1) >> lp, a.table_width - 1) - e0 + 1;
   static_assert((kNBuf - 2) * kChunkBytes >= 4 * kQLoads * 1024, "q must fit the ring slots from 2 on");
   char* const qlds = kvbuf[2] + hq * (kQLoads * 1024);
-  const int32_t* const prow_lds = (const int32_t*)kvbuf[1];
+  int32_t* const prow_lds = (int32_t*)kvbuf[1];
   const bool row_in_lds = a.map_pt_width <= kChunkBytes / 4;
   int32_t req = -1, seq = 0;
   {
+    const uint16_t* qh = a.q + (int64_t)t * a.q_tok_stride + (int64_t)(h0 + c) * a.q_head_stride + 8 * g;
+#pragma unroll
+    for (int k = 0; k < kQLoads / 2; ++k) {
+      const int ks = 9 * x + k;
+      dma16(qh + 32 * ks, qlds + ks * 1024);
+    }
     int32_t* ent = lp == 0 ? slot_s : page_s;
     for (int k = w; k * 64 < n_ent; k += kS1Waves) {
       const int e = k * 64 + lane;
@@ -550,8 +556,11 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     }
     if (mapped) {
       if (req_raw >= 0 && req_raw < a.map_R) {
+        // a scalar load through the constant address space (the array is read-only here):
+        // as a vector load after the copies above it would make the compiler wait for all of
+        // them before seq is used
         req = req_raw;
-        seq = a.map_seq[req];
+        seq = ((const __attribute__((address_space(4))) int32_t*)a.map_seq)[req];
       }
       if (row_in_lds) {
         const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
@@ -561,13 +570,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
         }
       }
     }
-    const uint16_t* qh = a.q + (int64_t)t * a.q_tok_stride + (int64_t)(h0 + c) * a.q_head_stride + 8 * g;
-#pragma unroll
-    for (int k = 0; k < kQLoads / 2; ++k) {
-      const int ks = 9 * x + k;
-      dma16(qh + 32 * ks, qlds + ks * 1024);
-    }
-    wait_vmcnt<kQLoads / 2>();                  // this wave's entries and row (issued first) are in LDS
+    wait_vmcnt<0>();
   }
   if (r0 >= len) {                              // inactive split: no merge reads it
     wait_vmcnt<0>();                            // no copy may land after the workgroup is gone
@@ -588,6 +591,11 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int nchunks = (nrows + kChunk - 1) / kChunk;
   lds_barrier();
 
+  // q to registers (the ring slots it occupied are free after the barrier below)
+  bf16x8 qf[kQLoads];
+#pragma unroll
+  for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
+
   // slots of the split's rows; -1 marks a masked row (past the length, a negative entry or
   // page id, or a slot outside the pool)
   if (mapped) {
@@ -595,25 +603,33 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     // 0 <= pos < the request's context and its page is inside the row with an id >= 0
     constexpr int kPer = kMaxSplitRows / kS1Threads;
     static_assert(kMaxSplitRows % kS1Threads == 0, "rows per thread");
-    const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
+    static_assert(kMaxSplitRows * 4 <= kChunkBytes, "a split's page ids fit one ring slot");
     const int mlp = a.map_log2_page;
-    int32_t pos[kPer], page[kPer];
+    int32_t pos[kPer];
     bool ok[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int i = tid + k * kS1Threads;
       pos[k] = i < nrows ? slot_s[i] : -1;
       ok[k] = req >= 0 && pos[k] >= 0 && pos[k] < seq && (pos[k] >> mlp) < a.map_pt_width;
-      // the row is in LDS unless it is longer than a ring slot; then each thread loads its
-      // page ids (all before any is used)
-      page[k] = !ok[k] ? -1 : row_in_lds ? prow_lds[pos[k] >> mlp] : ptrow[pos[k] >> mlp];
+    }
+    if (!row_in_lds) {
+      // the row is longer than a ring slot: each thread copies the page ids of its own
+      // positions into ring slot 1 (entry tid + k * kS1Threads) and reads them back
+      const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        dma4(ok[k] ? (const void*)(ptrow + (pos[k] >> mlp)) : (const void*)kZeroRow,
+             (char*)(prow_lds + k * kS1Threads + w * 64));
+      wait_vmcnt<0>();
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int i = tid + k * kS1Threads;
+      const int32_t page = ok[k] ? prow_lds[row_in_lds ? (pos[k] >> mlp) : i] : -1;
       if (i >= nchunks * kChunk) continue;
       int64_t sl = -1;
-      if (ok[k] && page[k] >= 0) sl = ((int64_t)page[k] << mlp) + (pos[k] & ((1 << mlp) - 1));
+      if (ok[k] && page >= 0) sl = ((int64_t)page << mlp) + (pos[k] & ((1 << mlp) - 1));
       slot_s[i] = (sl < 0 || sl >= a.kv.num_slots) ? -1 : (int32_t)sl;
     }
   } else {
@@ -701,17 +717,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   };
   auto no_hook = [](int) {};
 
-  // chunks 0 and 1 go out first (their ring slots hold no q); once q has landed every wave
-  // moves its quarter to registers, and after every wave has done so the slots q occupied
-  // take the next chunks
-  for (int ci = 0; ci < 2 && ci < nchunks; ++ci) issue(ci);
-  wait_chunks_w<2, kLoadsHi, kLoadsLo>(hi, min(2, nchunks));   // q was issued before these chunks
-  lds_barrier();
-  bf16x8 qf[kQLoads];
-#pragma unroll
-  for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
-  lds_barrier();
-  for (int ci = 2; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+  // the first kNBuf - 1 chunks go out together (q is in registers, the ring is free)
+  for (int ci = 0; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
 
   const Offsets<KV> off(x, g, c);
   f32x4 oacc[16];

@@ -249,6 +249,39 @@ def test_topk_fused_masks(splits):
     assert int((oslots >= 0).sum(axis=1).min()) == 0 and int((oslots >= 0).sum(axis=1).max()) > 100
 
 
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_topk_long_page_table_row(kv_dtype):
+    """A page-table row longer than the staging the fused path gives it in LDS (page size 1
+    rows of 12000 / 6000 entries): each thread fetches the page ids of its own positions."""
+    rng = np.random.default_rng(31)
+    T, W, R, P = 4, 2048, 2, 1
+    ptw = 12000 if kv_dtype == "bf16" else 6000
+    pages = ptw + 500
+    num_slots = pages * P
+    page_table = np.stack([rng.permutation(pages)[:ptw] for _ in range(R)]).astype(np.int32)
+    page_table[0, 5] = -1
+    seq_lens = np.array([ptw - 37, ptw], np.int32)
+    tok_req = np.array([0, 1, 0, 1], np.int32)
+    idx = np.stack([rng.choice(ptw + 50, size=W, replace=False) - 10 for _ in range(T)]).astype(np.int32)
+    idx[0, :3] = 5                                             # the page id < 0
+    valid = np.array([2048, 2000, 1500, 2048], np.int32)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((T, 64, 576)).astype(np.float32) * 0.5)
+    live = np.arange(num_slots, dtype=np.int32)
+    vals = rng.standard_normal((num_slots, 576)).astype(np.float32) * (1.0 if kv_dtype == "fp8" else 0.5)
+    kv, pool = _pools(live, vals, num_slots, kv_dtype)
+    qt = gc.q_tensor(q, "bf16")
+    args = (_t(idx), _t(valid), _t(tok_req), _t(page_table), _t(seq_lens))
+    slots = smla.smla_resolve_slots(*args, P)
+    a = smla.smla_sparse_decode(qt, kv, slots, _t(valid), 1, 1 / 16, num_splits=4)
+    b = smla.smla_sparse_decode_topk(qt, kv, *args, P, 1 / 16, num_splits=4)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    oslots = oracle.resolve_slots(idx, valid, tok_req, page_table, seq_lens, P)
+    assert np.array_equal(slots.cpu().numpy(), oslots)
+    o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, oslots, valid, 1, 1 / 16)
+    atol = FP8_ATOL if kv_dtype == "fp8" else BF16_ATOL
+    _check(b[0], b[1], o_ref, l_ref, atol, BF16_RTOL, f"long page-table row {kv_dtype}")
+
 def _ws_counters(ws):
     return ws[:256 * 1024]
 
