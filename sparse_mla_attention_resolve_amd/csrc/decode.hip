@@ -121,6 +121,11 @@ __device__ const uint4 kZeroRow[72] = {};
 // direct-to-LDS gathers of later chunks stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Materialise v in a register here: the compiler otherwise sinks work whose result is only
+// needed later (past the MFMAs it is meant to run between).
+template <typename V>
+__device__ __forceinline__ void pin(V& v) { __asm__ volatile("" : "+v"(v)); }
+
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -728,50 +733,84 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   bf16x8 pa;                                    // softmax weights of the chunk being multiplied
   f32x4 sl, sr;
 
-  // online softmax in base 2 for head h0 + c over chunk ci's 32 rows (both partners compute
-  // the same values), from this wave's score tile and the partner's; leaves the weights that
-  // meet the rows' values in pa. The running max only moves when a score exceeds it by more
-  // than 2^8, so most chunks skip the rescale of O.
-  auto softmax = [&](int ci) {
-    float sv[4];
-    {
-      const int4 lv = *(const int4*)(slot_s + ci * kChunk + 16 * x + 4 * g);
-      float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
-      if constexpr (kFp8) sc = *(const float4*)(scale_s + ci * kChunk + 16 * x + 4 * g);
-      const float raw[4] = {kFp8 ? sl[0] * sc.x + sr[0] : sl[0], kFp8 ? sl[1] * sc.y + sr[1] : sl[1],
-                            kFp8 ? sl[2] * sc.z + sr[2] : sl[2], kFp8 ? sl[3] * sc.w + sr[3] : sl[3]};
-      sv[0] = lv.x >= 0 ? raw[0] * a.scale_log2 : -INFINITY;
-      sv[1] = lv.y >= 0 ? raw[1] * a.scale_log2 : -INFINITY;
-      sv[2] = lv.z >= 0 ? raw[2] * a.scale_log2 : -INFINITY;
-      sv[3] = lv.w >= 0 ? raw[3] * a.scale_log2 : -INFINITY;
-    }
-    // swap tiles with the partner: afterwards f[4j + v] is row 16j + 4g + v for both. The
-    // partner read this wave's previous tile before it reached the barrier that this wave
-    // passed last, so the slot is free.
+  // Online softmax in base 2 for head h0 + c over chunk ci's 32 rows (both partners compute
+  // the same values). publish(ci) writes this wave's masked, scaled scores (rows 16x + 4g + v)
+  // to its exchange tile; after the barrier, piece(ci, k) for k = 0 .. 8 reads the partner's
+  // tile (then f[4j + v] is row 16j + 4g + v for both), updates the running max and sum, and
+  // leaves the weights that meet the rows' values in pa_next. The pieces run between the
+  // P V MFMAs of the previous chunk, so the matrix unit stays busy meanwhile; finish() then
+  // rescales O (after those MFMAs) when the running max moved. The max only moves when a
+  // score exceeds it by more than 2^8, so most chunks skip the rescale.
+  float sv[4], ex[4], f[8], mloc = 0.f, mn = 0.f, mn_safe = 0.f, alpha = 1.f, pv[8];
+  bool up = false;
+  float4 sc0 = make_float4(1.f, 1.f, 1.f, 1.f), sc1 = sc0;
+  bf16x8 pa_next;
+  auto publish = [&](int ci) {
+    const int4 lv = *(const int4*)(slot_s + ci * kChunk + 16 * x + 4 * g);
+    float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
+    if constexpr (kFp8) sc = *(const float4*)(scale_s + ci * kChunk + 16 * x + 4 * g);
+    const float raw[4] = {kFp8 ? sl[0] * sc.x + sr[0] : sl[0], kFp8 ? sl[1] * sc.y + sr[1] : sl[1],
+                          kFp8 ? sl[2] * sc.z + sr[2] : sl[2], kFp8 ? sl[3] * sc.w + sr[3] : sl[3]};
+    sv[0] = lv.x >= 0 ? raw[0] * a.scale_log2 : -INFINITY;
+    sv[1] = lv.y >= 0 ? raw[1] * a.scale_log2 : -INFINITY;
+    sv[2] = lv.z >= 0 ? raw[2] * a.scale_log2 : -INFINITY;
+    sv[3] = lv.w >= 0 ? raw[3] * a.scale_log2 : -INFINITY;
+    // the partner read this wave's previous tile before it reached the barrier that this
+    // wave passed last, so the slot is free
 #pragma unroll
     for (int v = 0; v < 4; ++v) sx[w][v][lane] = sv[v];
-    lds_barrier();
-    float f[8];
+  };
+  auto piece = [&](int ci, int k) {
+    if (k == 0) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float o = sx[w ^ 4][v][lane];
-      f[v] = x == 0 ? sv[v] : o;
-      f[4 + v] = x == 0 ? o : sv[v];
+      for (int v = 0; v < 4; ++v) ex[v] = sx[w ^ 4][v][lane];
+      if constexpr (kFp8) {
+        sc0 = *(const float4*)(scale_s + ci * kChunk + 4 * g);
+        sc1 = *(const float4*)(scale_s + ci * kChunk + 16 + 4 * g);
+      }
+    } else if (k == 2) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        f[v] = x == 0 ? sv[v] : ex[v];
+        f[4 + v] = x == 0 ? ex[v] : sv[v];
+      }
+      mloc = f[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mloc = fmaxf(mloc, f[i]);
+    } else if (k == 3) {
+      mloc = max_rows(mloc);
+    } else if (k == 4) {
+      // branch-free: with no finite score yet (mn = -inf) every f is -inf, and exp2 of
+      // f - 0 gives the zero weights; alpha is 1 when the max stays and 0 from -inf
+      up = mloc > m_run + 8.0f;
+      mn = up ? mloc : m_run;
+      mn_safe = mn == -INFINITY ? 0.f : mn;
+      alpha = __builtin_amdgcn_exp2f(m_run - mn_safe);
+    } else if (k == 5 || k == 6) {
+#pragma unroll
+      for (int i = 4 * (k - 5); i < 4 * (k - 4); ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(f[i] - mn_safe);
+        pin(pv[i]);
+      }
+    } else if (k == 7) {
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) psum += pv[i];
+      l_part = l_part * alpha + psum;
+      if constexpr (kFp8) {
+        // the weight that meets row r's values is p * scale(r)
+        pv[0] *= sc0.x; pv[1] *= sc0.y; pv[2] *= sc0.z; pv[3] *= sc0.w;
+        pv[4] *= sc1.x; pv[5] *= sc1.y; pv[6] *= sc1.z; pv[7] *= sc1.w;
+      }
+    } else if (k == 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pa_next[i] = (__bf16)pv[i];
+      uint4 pw = __builtin_bit_cast(uint4, pa_next);
+      pin(pw.x); pin(pw.y); pin(pw.z); pin(pw.w);
+      pa_next = __builtin_bit_cast(bf16x8, pw);
     }
-    float mloc = f[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mloc = fmaxf(mloc, f[i]);
-    mloc = max_rows(mloc);
-    const bool up = mloc > m_run + 8.0f;
-    const float mn = up ? mloc : m_run;
-    const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mn) : 1.0f;
-    float pv[8], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(f[i] - mn);
-      psum += pv[i];
-    }
-    l_part = l_part * alpha + psum;
+  };
+  auto finish = [&]() {
     if (__any(up && m_run != -INFINITY)) {
       // O rows are heads h0 + 4g + v: their factors live in lanes c = 4g + v
       float ah[4];
@@ -783,40 +822,41 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
         for (int v = 0; v < 4; ++v) oacc[nt][v] *= ah[v];
     }
     m_run = mn;
-    if constexpr (kFp8) {
-      // the weight that meets row r's values is p * scale(r)
-      const float4 sc0 = *(const float4*)(scale_s + ci * kChunk + 4 * g);
-      const float4 sc1 = *(const float4*)(scale_s + ci * kChunk + 16 + 4 * g);
-      pv[0] *= sc0.x; pv[1] *= sc0.y; pv[2] *= sc0.z; pv[3] *= sc0.w;
-      pv[4] *= sc1.x; pv[5] *= sc1.y; pv[6] *= sc1.z; pv[7] *= sc1.w;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pa[i] = (__bf16)pv[i];
+    pa = pa_next;
   };
 
-  // scores of chunk 0
+  // scores and weights of chunk 0
   wait_chunks_w<kNBuf - 2, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 2, nchunks - 1));
   lds_barrier();
   chunk_step<KV, true, false>(kvbuf[0], kvbuf[0], off, x, g, c, qf, sl, sr, pa, oacc, no_hook);
-  softmax(0);
+  publish(0);
+  lds_barrier();
+#pragma unroll
+  for (int k = 0; k <= 8; ++k) piece(0, k);
+  finish();
 
-  // iteration ci: O += P V over chunk ci together with the scores of chunk ci + 1. The
-  // barrier at its top publishes chunk ci + 1 and tells that every wave is done with the
-  // ring slot of chunk ci - 1, which the iteration refills.
+  // iteration ci, in two phases between three barriers: the scores of chunk ci + 1 (phase
+  // A, with the gathers of chunk ci + kNBuf - 1 spread over its MFMAs), the exchange of
+  // score tiles, then O += P V over chunk ci with the softmax of chunk ci + 1 in between
+  // (phase C). The barrier at the top publishes chunk ci + 1 and tells that every wave is
+  // done with the ring slot of chunk ci - 1, which the iteration refills.
   for (int ci = 0; ci + 1 < nchunks; ++ci) {
     wait_chunks_w<kNBuf - 3, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 3, nchunks - 2 - ci));
     lds_barrier();
-    // the gathers of chunk ci + kNBuf - 1 go out one at a time among this step's MFMAs: a
-    // copy instruction can wait for room in the compute unit's memory queue, and the MFMAs
-    // already issued keep the matrix unit busy meanwhile
+    // a copy instruction can wait for room in the compute unit's memory queue: one at a
+    // time among the MFMAs, the matrix unit keeps busy meanwhile
     const int cn = ci + kNBuf - 1;
     const bool refill = cn < nchunks;
     const Copies cp = src_of(refill ? cn : ci);   // (ci: a valid chunk whose slots go unused)
-    chunk_step<KV, true, true>(kvbuf[(ci + 1) % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
-                               [&](int k) {
-                                 if (refill && (k & 3) == 1 && (k >> 2) < kLoadsHi) fire(cp, cn, k >> 2);
-                               });
-    softmax(ci + 1);
+    chunk_step<KV, true, false>(kvbuf[(ci + 1) % kNBuf], kvbuf[(ci + 1) % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
+                                [&](int k) {
+                                  if (refill && (k & 3) == 1 && (k >> 2) < kLoadsHi) fire(cp, cn, k >> 2);
+                                });
+    publish(ci + 1);
+    lds_barrier();
+    chunk_step<KV, false, true>(kvbuf[ci % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
+                                [&](int k) { piece(ci + 1, k); });
+    finish();
   }
   chunk_step<KV, false, true>(kvbuf[(nchunks - 1) % kNBuf], kvbuf[(nchunks - 1) % kNBuf], off, x, g, c, qf, sl, sr,
                               pa, oacc, no_hook);
