@@ -121,9 +121,9 @@ def setup_decode(c, smla, torch):
 
 
 def time_decode(c, smla, torch, steps, warmup, flush):
-    """Cold steps (a 1 GiB read before each) of the fused step (stage 1 with in-kernel slot
-    resolution, then stage 2) with per-kernel events, the same for the two-kernel form
-    (smla_resolve_slots, then stage 1 over the resolved slots, then stage 2), and warm /
+    """Cold steps (a 1 GiB read before each) of the fused step, which is one kernel: stage 1
+    resolving the logical indices itself and merging the splits at its end. The same for the
+    two-kernel form (smla_resolve_slots, then the decode over the resolved slots), and warm /
     graph-replay figures of the fused step."""
     st = setup_decode(c, smla, torch)
     lay = c.layout
@@ -143,13 +143,11 @@ def time_decode(c, smla, torch, steps, warmup, flush):
         call()
     torch.cuda.synchronize()
 
-    # cold steps: the flush runs between steps, outside the events. Python's collector is
-    # off meanwhile, so that a collection cannot stall the host between two launches. The
-    # step is timed by one pair of events around it; the kernels are timed one by one in a
-    # second pass (an event between two launches adds its own gap to the step).
+    # cold steps: the flush runs between steps, outside the events, on the same stream as the
+    # decode kernel, so the event pair brackets exactly its one launch. Python's collector is
+    # off meanwhile, so that a collection cannot stall the host between two launches.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     gc.disable()
     wall0 = time.perf_counter()
@@ -163,32 +161,18 @@ def time_decode(c, smla, torch, steps, warmup, flush):
     wall = time.perf_counter() - wall0
     for k in range(steps):
         flush.sum()
-        e = ev[k]
-        e[0].record()
-        fused.stage1()
-        e[1].record()
-        fused.stage2()
-        e[2].record()
-    torch.cuda.synchronize()
-    for k in range(steps):
-        flush.sum()
         e = ev2[k]
         e[0].record()
         resolve()
         e[1].record()
-        call.stage1()
+        call()
         e[2].record()
-        call.stage2()
-        e[3].record()
     torch.cuda.synchronize()
     gc.enable()
     step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    s1_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    s2_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    two = {"step_ms": np.array([e[0].elapsed_time(e[3]) for e in ev2]),
+    two = {"step_ms": np.array([e[0].elapsed_time(e[2]) for e in ev2]),
            "resolve_ms": np.array([e[0].elapsed_time(e[1]) for e in ev2]),
-           "stage1_ms": np.array([e[1].elapsed_time(e[2]) for e in ev2]),
-           "stage2_ms": np.array([e[2].elapsed_time(e[3]) for e in ev2])}
+           "decode_ms": np.array([e[1].elapsed_time(e[2]) for e in ev2])}
 
     # warm steps: back to back, no flush
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -220,8 +204,8 @@ def time_decode(c, smla, torch, steps, warmup, flush):
         graph_ms = e0.elapsed_time(e1) / steps
     except Exception as ex:  # graph capture is a report-only extra
         log(f"graph capture skipped: {ex}")
-    return {"step_ms": step_ms, "stage1_ms": s1_ms, "stage2_ms": s2_ms, "two_kernel": two,
-            "warm_ms": warm_ms, "graph_ms": graph_ms, "wall_s": wall, "splits": fused.splits}
+    return {"step_ms": step_ms, "two_kernel": two, "warm_ms": warm_ms, "graph_ms": graph_ms, "wall_s": wall,
+            "splits": fused.splits}
 
 
 def cpu_baseline(c, seconds: float) -> dict:
@@ -284,16 +268,13 @@ def main():
     r = time_decode(c2, smla, torch, args.steps, args.warmup, flush)
     T = c2.q.shape[0]
     step_ms = float(r["step_ms"].mean())
-    s1_ms = float(r["stage1_ms"].mean())
     value = T / (step_ms / 1e3)
-    s1_gbs = ab["stage1"] / (s1_ms / 1e3) / 1e9
     step_gbs = ab["step"] / (step_ms / 1e3) / 1e9
     two = r["two_kernel"]
-    log(f"step {step_ms*1e3:.1f} us (stage1 with in-kernel resolution {s1_ms*1e3:.1f}, stage2 "
-        f"{r['stage2_ms'].mean()*1e3:.1f}); warm {r['warm_ms']*1e3:.1f} us; graph {(r['graph_ms'] or 0)*1e3:.1f} us; "
-        f"stage1 {s1_gbs:.0f} GB/s. Two-kernel form: {two['step_ms'].mean()*1e3:.1f} us (resolve "
-        f"{two['resolve_ms'].mean()*1e3:.1f}, stage1 {two['stage1_ms'].mean()*1e3:.1f}, stage2 "
-        f"{two['stage2_ms'].mean()*1e3:.1f})")
+    log(f"step {step_ms*1e3:.1f} us (one kernel: {step_gbs:.0f} GB/s of algorithmic bytes); warm "
+        f"{r['warm_ms']*1e3:.1f} us; graph {(r['graph_ms'] or 0)*1e3:.1f} us. Two-kernel form: "
+        f"{two['step_ms'].mean()*1e3:.1f} us (resolve {two['resolve_ms'].mean()*1e3:.1f}, decode "
+        f"{two['decode_ms'].mean()*1e3:.1f})")
 
     def us(a):
         return float(np.mean(a)) * 1e3
@@ -303,23 +284,22 @@ def main():
         "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "sparse MLA decode, bf16 q and KV, batch 32, 64 heads, latent 512 + rope 64, "
-                               "contexts U[8K,32K], 2^20-slot pool of 64-slot pages, top-k 2048; step = slot "
-                               "resolution + split decode (stage 1, resolving in-kernel) + LSE merge (stage 2); "
-                               "inputs HBM-resident (1 GiB read before each step)",
+                               "contexts U[8K,32K], 2^20-slot pool of 64-slot pages, top-k 2048; step = one "
+                               "kernel: slot resolution, split decode and LSE merge of the splits; inputs "
+                               "HBM-resident (1 GiB read before each step)",
                    "batch": T, "heads": 64, "topk": 2048, "splits": r["splits"], "parallelism": "none (1 GPU)"},
         "hbm_gbs_step": step_gbs, "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_step": ab["step"],
         "timing_us": {"step_median": float(np.median(r["step_ms"])) * 1e3,
                       "step_p10": float(np.percentile(r["step_ms"], 10)) * 1e3,
                       "step_p90": float(np.percentile(r["step_ms"], 90)) * 1e3,
-                      "stage1": s1_ms * 1e3, "stage2": us(r["stage2_ms"]),
                       "warm_step": r["warm_ms"] * 1e3,
                       "graph_replay_step": None if r["graph_ms"] is None else r["graph_ms"] * 1e3,
                       "two_kernel_form": {"step": us(two["step_ms"]), "resolve": us(two["resolve_ms"]),
-                                          "stage1": us(two["stage1_ms"]), "stage2": us(two["stage2_ms"])}},
-        "roofline": {"bound": "hbm", "kernel": "decode_stage1_mfma<bf16>", "achieved": s1_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": s1_gbs / HBM_PEAK_GBS,
-                     "algorithmic_bytes_per_launch": ab["stage1"], "avg_launch_us": s1_ms * 1e3,
+                                          "decode": us(two["decode_ms"])}},
+        "roofline": {"bound": "hbm", "kernel": "decode_stage1_mfma<bf16>", "achieved": step_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS,
+                     "algorithmic_bytes_per_launch": ab["step"], "avg_launch_us": step_ms * 1e3,
                      "traffic": measured_traffic("decode_stage1_mfma<bf16>", "bf16_batch_32")},
     }
 
@@ -330,21 +310,20 @@ def main():
         log("timing fp8-KV decode")
         r5 = time_decode(c5, smla, torch, args.steps, args.warmup, flush)
         ms5 = float(r5["step_ms"].mean())
-        s15 = float(r5["stage1_ms"].mean())
         two5 = r5["two_kernel"]
+        gbs5 = ab5["step"] / (ms5 / 1e3) / 1e9
         line["fp8_kv_decode"] = {
             "workload": "batch 64, 64 heads, fp8 e4m3 latent + bf16 rope + fp32 scale per row, context 64K, top-k 2048",
             "queries_per_s": c5.q.shape[0] / (ms5 / 1e3), "ms_per_step": ms5,
-            "hbm_gbs_step": ab5["step"] / (ms5 / 1e3) / 1e9,
-            "stage1_gbs": ab5["stage1"] / (s15 / 1e3) / 1e9, "stage1_us": s15 * 1e3,
-            "stage2_us": us(r5["stage2_ms"]),
+            "hbm_gbs_step": gbs5, "hbm_frac_step": gbs5 / HBM_PEAK_GBS,
+            "algorithmic_bytes_step": ab5["step"],
             "step_median_us": float(np.median(r5["step_ms"])) * 1e3,
-            "stage1_frac": ab5["stage1"] / (s15 / 1e3) / 1e9 / HBM_PEAK_GBS,
             "warm_step_us": r5["warm_ms"] * 1e3, "splits": r5["splits"],
+            "traffic": measured_traffic("decode_stage1_mfma<fp8>", "fp8_batch_64"),
             "two_kernel_form_us": {"step": us(two5["step_ms"]), "resolve": us(two5["resolve_ms"]),
-                                   "stage1": us(two5["stage1_ms"]), "stage2": us(two5["stage2_ms"])}}
-        log(f"fp8: step {ms5*1e3:.1f} us (median {np.median(r5['step_ms'])*1e3:.1f}; stage1 {s15*1e3:.1f}, stage2 "
-            f"{r5['stage2_ms'].mean()*1e3:.1f}); two-kernel form {us(two5['step_ms']):.1f} us")
+                                   "decode": us(two5["decode_ms"])}}
+        log(f"fp8: step {ms5*1e3:.1f} us (median {np.median(r5['step_ms'])*1e3:.1f}; {gbs5:.0f} GB/s); "
+            f"two-kernel form {us(two5['step_ms']):.1f} us")
 
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
