@@ -518,7 +518,9 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int hq = w & 3, x = w >> 2;
   const int h0 = 16 * hq;
-  const bool hi = w < kHiWaves;
+  // waves issuing kLoadsHi copies per chunk (the others kLoadsLo): the first kHiWaves, and for
+  // fp8 also the last wave, whose extra copy is the chunk's row scales
+  const bool hi = w < kHiWaves || (kFp8 && w == kS1Waves - 1);
 
   // ---- prologue. Everything the first gathers need goes out as early as it can:
   //   - at once (it needs only the kernel's arguments): q, in the order the lanes read it
@@ -663,17 +665,6 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const uint32_t lat8_stride32 = (uint32_t)a.kv.lat8_stride, rope16_stride32 = (uint32_t)a.kv.rope16_stride;
   const uint32_t row_stride32 = (uint32_t)a.kv.row_stride;
 
-  // fp8: the rows' scales go to LDS ahead of the first chunk (masked rows, and the entries
-  // past the split's last chunk, which hold no slot, read a zero)
-  if constexpr (kFp8) {
-    for (int k = 0; k * kS1Threads < nchunks * kChunk; ++k) {
-      const int i = k * kS1Threads + tid;
-      const int32_t sl = i < nchunks * kChunk ? slot_s[i] : -1;
-      const char* src = sl >= 0 ? (const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride : (const char*)kZeroRow;
-      dma4(src, (char*)(scale_s + k * kS1Threads + w * 64));
-    }
-  }
-
   // gather chunk ci into ring slot ci % kNBuf: copy instruction i = 8k + w of a chunk puts
   // the chunk's 16-byte units 64i .. 64i+63 (row-major, unit positions swizzled) at bytes
   // 1024i of the slot. Each lane's (row, stored unit) pairs are the same for every chunk;
@@ -692,15 +683,31 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   struct Copies {
     int32_t slot[kLoadsHi];                     // -1: masked row, copied from the zero row
   };
+  // fp8: the last wave, which has fewer row copies, copies the chunk's 32 row scales as its
+  // copy kLoadsLo (lanes 0 .. 31), next to the rows' own gathers (the scale shares a cache line
+  // with the row's rotary part)
+  const bool row_hi = w < kHiWaves;
+  const bool scale_wave = kFp8 && w == kS1Waves - 1;
+  static_assert(!kFp8 || (kHiWaves < kS1Waves && kLoadsHi == kLoadsLo + 1), "the scale copy fills a short wave");
   auto src_of = [&](int ci) {
     Copies cp;
     const int32_t* srow = slot_s + ci * kChunk;
 #pragma unroll
-    for (int k = 0; k < kLoadsHi; ++k) cp.slot[k] = (k < kLoadsLo || hi) ? srow[lpos[k] & 0xff] : -1;
+    for (int k = 0; k < kLoadsHi; ++k)
+      cp.slot[k] = (k < kLoadsLo || row_hi) ? srow[lpos[k] & 0xff] : scale_wave ? srow[lane & (kChunk - 1)] : -1;
     return cp;
   };
   auto fire = [&](const Copies& cp, int ci, int k) {
-    if (!(k < kLoadsLo || hi)) return;
+    if (!(k < kLoadsLo || row_hi)) {
+      if constexpr (kFp8) {
+        if (scale_wave && lane < kChunk) {
+          const int32_t sl = cp.slot[k];
+          dma4(sl >= 0 ? (const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride : (const char*)kZeroRow,
+               (char*)(scale_s + ci * kChunk));
+        }
+      }
+      return;
+    }
     const int32_t sl = cp.slot[k];
     const int unit = lpos[k] >> 8;
     const bool live = sl >= 0;
