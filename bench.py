@@ -208,6 +208,86 @@ def time_decode(c, smla, torch, steps, warmup, flush):
             "splits": fused.splits}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def time_prefill(c, smla, torch, steps, warmup, flush, cpu_seconds):
+    """Grouped sparse prefill (union build + grouped attention) on case `c`: cold steps (the
+    flush before each), each kernel alone and the two together, against the bf16 MFMA peak;
+    the oracle on a bounded sample of groups."""
+    dev = "cuda"
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    lay = c.layout
+    Q, H = c.q.shape[0], c.q.shape[1]
+    kv = smla.KvCache.empty(smla.SMLA_BF16, lay.num_slots, device=dev)
+    smap = smla.smla_resolve_slots(t(c.rows.pos[:, None]), None, t(c.rows.req), t(lay.page_table), t(lay.ctx),
+                                   lay.page_size)[:, 0].contiguous()
+    smla.smla_kv_write(t(c.rows.values.view(np.int16)).view(torch.bfloat16), smap, kv)
+    req = t(np.zeros(Q, np.int32))
+    slots = smla.smla_resolve_slots(t(c.idx), t(c.valid), req, t(lay.page_table), t(lay.ctx), lay.page_size)
+    valid = t(c.valid)
+    q = t(c.q.view(np.int16)).view(torch.bfloat16)
+    enc, lens = smla.smla_build_group_union(slots, valid, c.G, lay.num_slots)
+    out = torch.empty((Q, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Q, H), dtype=torch.float32, device=dev)
+
+    def union():
+        smla.smla_build_group_union(slots, valid, c.G, lay.num_slots, enc=enc, lens=lens)
+
+    def prefill():
+        smla.smla_grouped_prefill(q, kv, enc, lens, c.G, c.scale, out=out, lse=lse)
+
+    for _ in range(warmup):
+        flush.sum()
+        union()
+        prefill()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        flush.sum()
+        ev[k][0].record()
+        union()
+        ev[k][1].record()
+        prefill()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    u_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    p_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    both = np.array([e[0].elapsed_time(e[2]) for e in ev])
+    n_union = int(lens.sum().item())
+    flop_alg = float(c.valid.astype(np.int64).sum()) * H * 2 * (576 + 512)
+    flop_done = float(n_union) * c.G * H * 2 * (576 + 512)
+    p_mean = float(p_ms.mean())
+    res = {"workload": f"{c.name}: union build + grouped attention; KV pool {lay.num_slots} slots (cache-resident)",
+           "queries": Q, "group": c.G, "union_rows": n_union, "union_over_topk": n_union / float(c.valid.sum()) * c.G,
+           "step_ms": float(both.mean()), "union_us": float(u_ms.mean()) * 1e3, "prefill_ms": p_mean,
+           "tokens_per_s": Q / (float(both.mean()) / 1e3),
+           "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": flop_alg / (p_mean / 1e3) / 1e12,
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": flop_alg / (p_mean / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                        "algorithmic_flop_per_launch": flop_alg, "computed_flop_per_launch": flop_done,
+                        "computed_tflops": flop_done / (p_mean / 1e3) / 1e12, "avg_launch_us": p_mean * 1e3}}
+    if cpu_seconds > 0:
+        import oracle
+        pool = oracle.Pool(lay.num_slots, "bf16")
+        osl = oracle.resolve_slots(c.rows.pos[:, None], None, c.rows.req, lay.page_table, lay.ctx, lay.page_size)[:, 0]
+        oracle.kv_write(pool, c.rows.values, "bf16", osl)
+        enc_h, lens_h = enc.cpu().numpy(), lens.cpu().numpy()
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < cpu_seconds:
+            g = done % len(lens_h)
+            oracle.grouped_prefill(c.q, pool, enc_h, lens_h, c.G, c.scale, queries=np.arange(g * c.G, g * c.G + c.G))
+            done += 1
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": done * c.G / el, "unit": "queries/s", "kind": "oracle",
+                               "sample": f"{done} groups ({done * c.G} queries) of the same workload, fp64 grouped "
+                                         f"attention over the GPU-built union, {el:.1f} s wall on the host"}
+    return res
+
+
 def cpu_baseline(c, seconds: float) -> dict:
     import oracle
     try:
@@ -242,6 +322,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three plain 256 MiB fp32 copy kernels (y = x * 1), whose HBM counter "
@@ -324,6 +405,16 @@ def main():
                                    "decode": us(two5["decode_ms"])}}
         log(f"fp8: step {ms5*1e3:.1f} us (median {np.median(r5['step_ms'])*1e3:.1f}; {gbs5:.0f} GB/s); "
             f"two-kernel form {us(two5['step_ms']):.1f} us")
+
+    if not args.no_prefill:
+        log("generating the grouped-prefill workload (8192 queries on 16384 cached, G = 2)")
+        c4 = wl.prefill_grouped_q8192()
+        log("timing grouped prefill")
+        pr = time_prefill(c4, smla, torch, max(3, args.steps // 5), 2, flush,
+                          0.0 if args.no_cpu_baseline else min(5.0, args.cpu_seconds))
+        line["grouped_prefill"] = pr
+        log(f"grouped prefill: union {pr['union_us']:.0f} us + attention {pr['prefill_ms']:.2f} ms "
+            f"({pr['roofline']['achieved']:.0f} TFLOP/s algorithmic, {pr['roofline']['computed_tflops']:.0f} computed)")
 
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")

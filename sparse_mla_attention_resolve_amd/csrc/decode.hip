@@ -61,6 +61,10 @@ struct Stage1Args {
   // splits, in wall-clock ticks (0: never wait)
   uint32_t* sync;
   int32_t wait_ticks;
+  // union mode (grouped prefill), when > 0: token t is query t of group t / union_G, whose
+  // table row and length are the group's union (entries = row | member bits << 24); the
+  // kernel takes the entries whose bit t % union_G is set. One split per token (S = 1).
+  int32_t union_G;
 };
 
 // Physical slot of position p of token t's table row, or -1 when masked.
@@ -494,7 +498,7 @@ __device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int nac
 // software pipelined: while it accumulates P V for chunk ci it computes the scores of
 // chunk ci + 1.
 
-template <int KV>
+template <int KV, bool UNION>
 __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a) {
   using L = Lay<KV>;
   constexpr int kRowBytes = L::kUnits * 16;
@@ -510,6 +514,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   __shared__ int32_t page_s[kMaxSplitRows / 2 + 64];     // page ids of a split (page size >= 2)
   __shared__ __attribute__((aligned(16))) float scale_s[kFp8 ? kMaxSplitRows : 4];
   __shared__ float sx[kS1Waves][4][64];                    // score tiles swapped between partners
+  __shared__ int wcnt[kMaxSplitRows / kS1Threads][kS1Waves];   // union mode: kept entries per wave
 
   int t, s;
   stage1_coords(blockIdx.x, a.T, a.S, t, s);
@@ -537,10 +542,13 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int lp = a.log2_page;
   const int r0 = s * a.rows_per_split;
   const bool mapped = a.mapped != 0;
-  const int len_raw = a.lens[t];
-  const int req_raw = a.map_req[t];
+  constexpr bool umode = UNION;                         // a.union_G > 0
+  const int trow_id = umode ? t / a.union_G : t;       // the token's table row (union mode: its group's)
+  const int member = umode ? t % a.union_G : 0;
+  const int len_raw = a.lens[trow_id];
+  const int req_raw = a.map_req[trow_id];
   const int len = len_raw < 0 ? 0 : (len_raw > a.max_len ? a.max_len : len_raw);
-  const int32_t* trow = a.table + (int64_t)t * a.table_stride;
+  const int32_t* trow = a.table + (int64_t)trow_id * a.table_stride;
   const int e0 = r0 >> lp;
   const int n_ent = lp == 0 ? min(a.rows_per_split, a.max_len - r0)
                             : min((r0 + a.rows_per_split - 1) >> lp, a.table_width - 1) - e0 + 1;
@@ -581,81 +589,22 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   }
   if (r0 >= len) {                              // inactive split: no merge reads it
     wait_vmcnt<0>();                            // no copy may land after the workgroup is gone
-    if (a.sync != nullptr && len == 0 && s == 0) {
+    if ((a.sync != nullptr || umode) && len == 0 && s == 0) {
       // a token with no rows: zero output and lse -inf (stage 2 would write them otherwise)
       uint16_t* ob = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride;
-#pragma unroll
-      for (int k = 0; k < kHeads * kLatent / 8 / kS1Threads; ++k) {
-        const int i = k * kS1Threads + tid;
-        *(uint4*)(ob + (int64_t)(i >> 6) * a.out_head_stride + 8 * (i & 63)) = make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int i = tid; i < kHeads * kLatent; i += kS1Threads) ob[(int64_t)(i >> 9) * a.out_head_stride + (i & 511)] = 0;
       if (a.lse && tid < kHeads) a.lse[(int64_t)t * a.lse_tok_stride + tid] = -INFINITY;
     }
     return;
   }
   const int r1 = min(r0 + a.rows_per_split, len);
-  const int nrows = r1 - r0;
-  const int nchunks = (nrows + kChunk - 1) / kChunk;
   lds_barrier();
 
-  // q to registers (the ring slots it occupied are free after the barrier below)
+  // q to registers (the ring slots it occupied are free after the barrier that ends the
+  // first segment's slot building)
   bf16x8 qf[kQLoads];
 #pragma unroll
   for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
-
-  // slots of the split's rows; -1 marks a masked row (past the length, a negative entry or
-  // page id, or a slot outside the pool)
-  if (mapped) {
-    // positions -> slots exactly as smla_resolve_slots computes them: a position counts when
-    // 0 <= pos < the request's context and its page is inside the row with an id >= 0
-    constexpr int kPer = kMaxSplitRows / kS1Threads;
-    static_assert(kMaxSplitRows % kS1Threads == 0, "rows per thread");
-    static_assert(kMaxSplitRows * 4 <= kChunkBytes, "a split's page ids fit one ring slot");
-    const int mlp = a.map_log2_page;
-    int32_t pos[kPer];
-    bool ok[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kS1Threads;
-      pos[k] = i < nrows ? slot_s[i] : -1;
-      ok[k] = req >= 0 && pos[k] >= 0 && pos[k] < seq && (pos[k] >> mlp) < a.map_pt_width;
-    }
-    if (!row_in_lds) {
-      // the row is longer than a ring slot: each thread copies the page ids of its own
-      // positions into ring slot 1 (entry tid + k * kS1Threads) and reads them back
-      const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k)
-        dma4(ok[k] ? (const void*)(ptrow + (pos[k] >> mlp)) : (const void*)kZeroRow,
-             (char*)(prow_lds + k * kS1Threads + w * 64));
-      wait_vmcnt<0>();
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kS1Threads;
-      const int32_t page = ok[k] ? prow_lds[row_in_lds ? (pos[k] >> mlp) : i] : -1;
-      if (i >= nchunks * kChunk) continue;
-      int64_t sl = -1;
-      if (ok[k] && page >= 0) sl = ((int64_t)page << mlp) + (pos[k] & ((1 << mlp) - 1));
-      slot_s[i] = (sl < 0 || sl >= a.kv.num_slots) ? -1 : (int32_t)sl;
-    }
-  } else {
-    for (int i = tid; i < nchunks * kChunk; i += kS1Threads) {
-      int64_t sl = -1;
-      if (i < nrows) {
-        if (lp == 0) {
-          sl = slot_s[i];
-        } else {
-          const int p = r0 + i;
-          const int32_t pg = page_s[(p >> lp) - e0];
-          sl = pg < 0 ? -1 : ((int64_t)pg << lp) + (p & ((1 << lp) - 1));
-        }
-        if (sl >= a.kv.num_slots) sl = -1;
-      }
-      slot_s[i] = sl < 0 ? -1 : (int32_t)sl;
-    }
-  }
-  lds_barrier();
 
   // plane bases and strides as scalars (a per-lane choice between two fields of the
   // argument struct would otherwise become a memory load)
@@ -728,9 +677,6 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     for (int k = 0; k < kLoadsHi; ++k) fire(cp, ci, k);
   };
   auto no_hook = [](int) {};
-
-  // the first kNBuf - 1 chunks go out together (q is in registers, the ring is free)
-  for (int ci = 0; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
 
   const Offsets<KV> off(x, g, c);
   f32x4 oacc[16];
@@ -832,41 +778,160 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     pa = pa_next;
   };
 
-  // scores and weights of chunk 0
-  wait_chunks_w<kNBuf - 2, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 2, nchunks - 1));
-  lds_barrier();
-  chunk_step<KV, true, false>(kvbuf[0], kvbuf[0], off, x, g, c, qf, sl, sr, pa, oacc, no_hook);
-  publish(0);
-  lds_barrier();
-#pragma unroll
-  for (int k = 0; k <= 8; ++k) piece(0, k);
-  finish();
+  // The rows come in segments whose slots are built in LDS: decode walks one (the split's
+  // rows); the union mode walks its group's union in pieces of kMaxSplitRows entries, each
+  // compacted to the entries whose bit names its query. O and the running max and sum carry
+  // over from one segment to the next.
+  const int nseg = umode ? (len + kMaxSplitRows - 1) / kMaxSplitRows : 1;
+  for (int seg = 0; seg < nseg; ++seg) {
+    const int sb = r0 + seg * kMaxSplitRows;       // first entry of the segment
+    if (seg > 0) {
+      lds_barrier();                               // every wave is done with the slots and the ring
+      const int n_seg = min(kMaxSplitRows, a.max_len - sb);
+      for (int k = w; k * 64 < n_seg; k += kS1Waves) {
+        const int e = k * 64 + lane;
+        dma4(e < n_seg ? (const void*)(trow + sb + e) : (const void*)kZeroRow, (char*)(slot_s + k * 64));
+      }
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+    const int nraw = umode ? min(kMaxSplitRows, len - sb) : r1 - r0;
+    const int nch_raw = (nraw + kChunk - 1) / kChunk;
+    int nrows = nraw;
 
-  // iteration ci, in two phases between three barriers: the scores of chunk ci + 1 (phase
-  // A, with the gathers of chunk ci + kNBuf - 1 spread over its MFMAs), the exchange of
-  // score tiles, then O += P V over chunk ci with the softmax of chunk ci + 1 in between
-  // (phase C). The barrier at the top publishes chunk ci + 1 and tells that every wave is
-  // done with the ring slot of chunk ci - 1, which the iteration refills.
-  for (int ci = 0; ci + 1 < nchunks; ++ci) {
-    wait_chunks_w<kNBuf - 3, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 3, nchunks - 2 - ci));
+    // slots of the segment's rows; -1 marks a masked row (past the length, a negative entry or
+    // page id, or a slot outside the pool). Union mode keeps the entries whose membership bit
+    // names this query (and whose row is in the pool), in union order: a stable block-wide
+    // compaction (wave ballots, wave counts through LDS), then -1 past the kept rows up to the
+    // chunk boundary.
+    if (umode) {
+      constexpr int kPer = kMaxSplitRows / kS1Threads;
+      uint32_t ent[kPer];
+      bool keep[kPer];
+      int before[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kS1Threads;
+        const uint32_t e = i < nraw ? (uint32_t)slot_s[i] : 0u;
+        ent[k] = e & ((1u << SMLA_UNION_ROW_BITS) - 1u);
+        keep[k] = i < nraw && ((e >> (SMLA_UNION_ROW_BITS + member)) & 1u) && (int64_t)ent[k] < a.kv.num_slots;
+        const uint64_t b = __ballot(keep[k]);
+        before[k] = __popcll(b & ((1ull << lane) - 1ull));
+        if (lane == 0) wcnt[k][w] = __popcll(b);
+      }
+      lds_barrier();                               // counts published; every entry has been read
+      int total = 0, base[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        int pre = 0, tot = 0;
+#pragma unroll
+        for (int v = 0; v < kS1Waves; ++v) {
+          const int n = wcnt[k][v];
+          pre += v < w ? n : 0;
+          tot += n;
+        }
+        base[k] = total + pre;
+        total += tot;
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        if (keep[k]) slot_s[base[k] + before[k]] = (int32_t)ent[k];
+      nrows = total;
+      if (tid < (kChunk - (total & (kChunk - 1))) % kChunk) slot_s[total + tid] = -1;
+    } else if (mapped) {
+      // positions -> slots exactly as smla_resolve_slots computes them: a position counts when
+      // 0 <= pos < the request's context and its page is inside the row with an id >= 0
+      constexpr int kPer = kMaxSplitRows / kS1Threads;
+      static_assert(kMaxSplitRows % kS1Threads == 0, "rows per thread");
+      static_assert(kMaxSplitRows * 4 <= kChunkBytes, "a split's page ids fit one ring slot");
+      const int mlp = a.map_log2_page;
+      int32_t pos[kPer];
+      bool ok[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kS1Threads;
+        pos[k] = i < nraw ? slot_s[i] : -1;
+        ok[k] = req >= 0 && pos[k] >= 0 && pos[k] < seq && (pos[k] >> mlp) < a.map_pt_width;
+      }
+      if (!row_in_lds) {
+        // the row is longer than a ring slot: each thread copies the page ids of its own
+        // positions into ring slot 1 (entry tid + k * kS1Threads) and reads them back
+        const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+          dma4(ok[k] ? (const void*)(ptrow + (pos[k] >> mlp)) : (const void*)kZeroRow,
+               (char*)(prow_lds + k * kS1Threads + w * 64));
+        wait_vmcnt<0>();
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kS1Threads;
+        const int32_t page = ok[k] ? prow_lds[row_in_lds ? (pos[k] >> mlp) : i] : -1;
+        if (i >= nch_raw * kChunk) continue;
+        int64_t sl = -1;
+        if (ok[k] && page >= 0) sl = ((int64_t)page << mlp) + (pos[k] & ((1 << mlp) - 1));
+        slot_s[i] = (sl < 0 || sl >= a.kv.num_slots) ? -1 : (int32_t)sl;
+      }
+    } else {
+      for (int i = tid; i < nch_raw * kChunk; i += kS1Threads) {
+        int64_t sl = -1;
+        if (i < nraw) {
+          if (lp == 0) {
+            sl = slot_s[i];
+          } else {
+            const int p = r0 + i;
+            const int32_t pg = page_s[(p >> lp) - e0];
+            sl = pg < 0 ? -1 : ((int64_t)pg << lp) + (p & ((1 << lp) - 1));
+          }
+          if (sl >= a.kv.num_slots) sl = -1;
+        }
+        slot_s[i] = sl < 0 ? -1 : (int32_t)sl;
+      }
+    }
     lds_barrier();
-    // a copy instruction can wait for room in the compute unit's memory queue: one at a
-    // time among the MFMAs, the matrix unit keeps busy meanwhile
-    const int cn = ci + kNBuf - 1;
-    const bool refill = cn < nchunks;
-    const Copies cp = src_of(refill ? cn : ci);   // (ci: a valid chunk whose slots go unused)
-    chunk_step<KV, true, false>(kvbuf[(ci + 1) % kNBuf], kvbuf[(ci + 1) % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
-                                [&](int k) {
-                                  if (refill && (k & 3) == 1 && (k >> 2) < kLoadsHi) fire(cp, cn, k >> 2);
-                                });
-    publish(ci + 1);
+    const int nchunks = (nrows + kChunk - 1) / kChunk;
+    if (nchunks == 0) continue;
+
+    // the first kNBuf - 1 chunks go out together (q is in registers, the ring is free)
+    for (int ci = 0; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+
+
+    // scores and weights of chunk 0
+    wait_chunks_w<kNBuf - 2, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 2, nchunks - 1));
     lds_barrier();
-    chunk_step<KV, false, true>(kvbuf[ci % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
-                                [&](int k) { piece(ci + 1, k); });
+    chunk_step<KV, true, false>(kvbuf[0], kvbuf[0], off, x, g, c, qf, sl, sr, pa, oacc, no_hook);
+    publish(0);
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k <= 8; ++k) piece(0, k);
     finish();
+
+    // iteration ci, in two phases between three barriers: the scores of chunk ci + 1 (phase
+    // A, with the gathers of chunk ci + kNBuf - 1 spread over its MFMAs), the exchange of
+    // score tiles, then O += P V over chunk ci with the softmax of chunk ci + 1 in between
+    // (phase C). The barrier at the top publishes chunk ci + 1 and tells that every wave is
+    // done with the ring slot of chunk ci - 1, which the iteration refills.
+    for (int ci = 0; ci + 1 < nchunks; ++ci) {
+      wait_chunks_w<kNBuf - 3, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 3, nchunks - 2 - ci));
+      lds_barrier();
+      // a copy instruction can wait for room in the compute unit's memory queue: one at a
+      // time among the MFMAs, the matrix unit keeps busy meanwhile
+      const int cn = ci + kNBuf - 1;
+      const bool refill = cn < nchunks;
+      const Copies cp = src_of(refill ? cn : ci);   // (ci: a valid chunk whose slots go unused)
+      chunk_step<KV, true, false>(kvbuf[(ci + 1) % kNBuf], kvbuf[(ci + 1) % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
+                                  [&](int k) {
+                                    if (refill && (k & 3) == 1 && (k >> 2) < kLoadsHi) fire(cp, cn, k >> 2);
+                                  });
+      publish(ci + 1);
+      lds_barrier();
+      chunk_step<KV, false, true>(kvbuf[ci % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
+                                  [&](int k) { piece(ci + 1, k); });
+      finish();
+    }
+    chunk_step<KV, false, true>(kvbuf[(nchunks - 1) % kNBuf], kvbuf[(nchunks - 1) % kNBuf], off, x, g, c, qf, sl, sr,
+                                pa, oacc, no_hook);
   }
-  chunk_step<KV, false, true>(kvbuf[(nchunks - 1) % kNBuf], kvbuf[(nchunks - 1) % kNBuf], off, x, g, c, qf, sl, sr,
-                              pa, oacc, no_hook);
 
   // ---- normalise. A token whose rows fit one split is finished here; the others leave
   // their partials for stage 2.
@@ -876,7 +941,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   float inv[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) inv[v] = __shfl(inv_c, 4 * g + v, 64);
-  if (len <= a.rows_per_split) {
+  if (umode || len <= a.rows_per_split) {
     uint16_t* ob = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)(h0 + 4 * g) * a.out_head_stride +
                    256 * x + c;
 #pragma unroll
@@ -1166,6 +1231,7 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   a.part_lse = (float*)((char*)ws + plan.sync_bytes + plan.part_o_bytes);
   a.sync = plan.fused ? (uint32_t*)ws : nullptr;
   a.wait_ticks = plan.wait_ticks;
+  a.union_G = 0;
   a.out = d.out;
   a.out_tok_stride = d.out_tok_stride;
   a.out_head_stride = d.out_head_stride;
@@ -1194,9 +1260,9 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
     dim3 grid(plan.S * d.T, (d.H + 15) / 16);
     hipLaunchKernelGGL(decode_stage1_f32, grid, dim3(kThreads), 0, stream, a);
   } else if (d.kv.dtype == SMLA_BF16) {
-    hipLaunchKernelGGL(decode_stage1_mfma<SMLA_BF16>, dim3(plan.S * d.T), dim3(kS1Threads), 0, stream, a);
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, false>), dim3(plan.S * d.T), dim3(kS1Threads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_stage1_mfma<SMLA_FP8_E4M3>, dim3(plan.S * d.T), dim3(kS1Threads), 0, stream, a);
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, false>), dim3(plan.S * d.T), dim3(kS1Threads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(stages & 2) || plan.fused) return e;   // fused: stage 1 has merged
@@ -1220,6 +1286,43 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
     hipLaunchKernelGGL(decode_stage2, dim3(d.T * ((d.H + 1) / 2)), dim3(kS2Threads), 0, stream, b);
   else
     hipLaunchKernelGGL(decode_stage2_packed, dim3(d.T * (16 * 128 / kS2Threads)), dim3(kS2Threads), 0, stream, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_union_decode(const smla_prefill_args& d, hipStream_t stream) {
+  if (d.Q == 0) return hipSuccess;
+  Stage1Args a = {};
+  a.q = (const uint16_t*)d.q;
+  a.q_tok_stride = d.q_tok_stride;
+  a.q_head_stride = d.q_head_stride;
+  a.kv = d.kv;
+  a.table = (const int32_t*)d.enc;
+  a.table_stride = d.enc_stride;
+  a.lens = d.lens;                             // [groups]: read at the token's group
+  a.max_len = d.enc_width;
+  a.table_width = d.enc_width;
+  a.log2_page = 0;
+  a.scale_log2 = d.scale * kLog2e;
+  a.rows_per_split = kMaxSplitRows;            // the segment size; one split per query
+  a.S = 1;
+  a.H = d.H;
+  a.T = d.Q;
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
+  a.mapped = 0;
+  a.map_req = d.lens;                          // a valid array at the group index (unused)
+  a.out = d.out;
+  a.out_tok_stride = d.out_tok_stride;
+  a.out_head_stride = d.out_head_stride;
+  a.lse = d.lse;
+  a.lse_tok_stride = d.lse_tok_stride;
+  a.sync = nullptr;
+  a.wait_ticks = 0;
+  a.union_G = d.G;
+  if (d.kv.dtype == SMLA_BF16)
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, true>), dim3(d.Q), dim3(kS1Threads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, true>), dim3(d.Q), dim3(kS1Threads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -190,6 +190,7 @@ __global__ void __launch_bounds__(kPThreads, 1) prefill_kernel(PrefillKArgs a) {
 
 hipError_t launch_prefill(const smla_prefill_args& d, hipStream_t stream) {
   if (d.Q == 0) return hipSuccess;
+  if (d.H == 64) return launch_union_decode(d, stream);
   PrefillKArgs a;
   a.q = (const uint16_t*)d.q;
   a.q_tok_stride = d.q_tok_stride;

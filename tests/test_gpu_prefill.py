@@ -52,6 +52,46 @@ def test_prefill_small(Q, H, G):
         assert gc.rel_l2(o[1], ob[0]) > 0.05
 
 
+def _fp8_pool(vals, live, ns):
+    kv = smla.KvCache.empty(smla.SMLA_FP8_E4M3, ns)
+    smla.smla_kv_write(_t(vals[live]), _t(live), kv)
+    pool = oracle.Pool(ns, "fp8")
+    oracle.kv_write(pool, vals[live], "f32", live)
+    return kv, pool
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_prefill_h64_long_union(kv_dtype):
+    """H = 64 groups whose union spans several segments of the walk (W = 1024, little
+    overlap), a member with an empty list next to a full one, and an fp8 cache."""
+    rng = np.random.default_rng(61)
+    Q, H, G, W, ns = 6, 64, 2, 1024, 6000
+    slots, valid = wl.random_slot_lists(61, Q, W, ns, overlap=0.1, G=G)
+    valid[3] = 0                                           # member 1 of group 1: no rows
+    valid[4] = 700
+    vals = rng.standard_normal((ns, 576)).astype(np.float32) * (1.0 if kv_dtype == "fp8" else 0.5)
+    live = np.unique(slots[slots >= 0]).astype(np.int32)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((Q, H, 576)).astype(np.float32) * 0.5)
+    if kv_dtype == "bf16":
+        vb = wl.f32_to_bf16_bits(vals)
+        kv = smla.KvCache.empty(smla.SMLA_BF16, ns)
+        smla.smla_kv_write(gc.bits_to_torch_bf16(vb[live]), _t(live), kv)
+        pool = oracle.Pool(ns, "bf16")
+        oracle.kv_write(pool, vb[live], "bf16", live)
+    else:
+        kv, pool = _fp8_pool(vals, live, ns)
+    enc, lens = smla.smla_build_group_union(_t(slots), _t(valid), G, ns)
+    out, lse = smla.smla_grouped_prefill(gc.q_tensor(q, "bf16"), kv, enc, lens, G, 0.0625)
+    enc_o, lens_o = oracle.group_union(slots, valid, G, ns)
+    assert np.array_equal(lens.cpu().numpy(), lens_o) and int(lens_o.max()) > 1024
+    o_ref, l_ref = oracle.grouped_prefill(q, pool, enc_o, lens_o, G, 0.0625)
+    o = out.float().cpu().numpy()
+    atol = 6e-2 if kv_dtype == "fp8" else 2e-2
+    gc.assert_close(o, o_ref, atol, 1e-2, f"prefill H=64 {kv_dtype}")
+    gc.assert_lse(lse.cpu().numpy(), l_ref, 1e-3, f"prefill H=64 {kv_dtype} lse")
+    assert np.all(o[3] == 0) and np.all(np.isneginf(lse[3].cpu().numpy()))
+
+
 def test_prefill_grouped_q8192_sampled():
     c = gc.config("prefill_grouped_q8192")
     lay = c.layout
