@@ -208,6 +208,61 @@ def time_decode(c, smla, torch, steps, warmup, flush):
             "splits": fused.splits}
 
 
+def time_ragged(c, smla, torch, steps, warmup, flush):
+    """Ragged batch with dense requests: the fused top-k decode over the sparse tokens and the
+    dense paged decode (page 64, length = context) over the others, on one stream, cold."""
+    dev = "cuda"
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    lay = c.layout
+    T, H = c.q.shape[0], c.q.shape[1]
+    kv = smla.KvCache.empty(smla.SMLA_BF16, lay.num_slots, device=dev)
+    smap = smla.smla_resolve_slots(t(c.rows.pos[:, None]), None, t(c.rows.req), t(lay.page_table), t(lay.ctx),
+                                   lay.page_size)[:, 0].contiguous()
+    smla.smla_kv_write(t(c.rows.values.view(np.int16)).view(torch.bfloat16), smap, kv)
+    dense = np.asarray(c.dense_tokens, np.int64)
+    sparse = np.setdiff1d(np.arange(T), dense)
+    q = c.q.view(np.int16)
+    qs, qd = t(q[sparse]).view(torch.bfloat16), t(q[dense]).view(torch.bfloat16)
+    out_s = torch.empty((len(sparse), H, 512), dtype=torch.bfloat16, device=dev)
+    lse_s = torch.empty((len(sparse), H), dtype=torch.float32, device=dev)
+    out_d = torch.empty((len(dense), H, 512), dtype=torch.bfloat16, device=dev)
+    lse_d = torch.empty((len(dense), H), dtype=torch.float32, device=dev)
+    keep = [t(c.idx[sparse]), t(c.valid[sparse]), t(c.tok_req[sparse]), t(lay.page_table), t(lay.ctx),
+            t(lay.page_table[c.tok_req[dense]]), t(lay.ctx[c.tok_req[dense]])]
+    fs = smla.DecodeCall(qs, kv, keep[0], keep[1], 1, c.scale, out_s, lse_s,
+                         page_map=(keep[2], keep[3], keep[4], lay.page_size))
+    fd = smla.DecodeCall(qd, kv, keep[5], keep[6], lay.page_size, c.scale, out_d, lse_d)
+
+    def step():
+        fs()
+        fd()
+
+    for _ in range(warmup):
+        flush.sum()
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(steps):
+        flush.sum()
+        ev[k][0].record()
+        step()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    rows = int(c.valid[sparse].sum()) + int(lay.ctx[c.tok_req[dense]].sum())
+    alg = rows * 1152 + T * (73728 + 65536 + 256 + 8192)
+    m = float(ms.mean())
+    return {"workload": f"{c.name}: fused top-k decode over {len(sparse)} tokens + dense paged decode (page "
+                        f"{lay.page_size}, length = context) over {len(dense)}, one stream",
+            "queries_per_s": T / (m / 1e3), "ms_per_step": m, "step_median_us": float(np.median(ms)) * 1e3,
+            "rows": rows, "algorithmic_bytes_step": alg, "hbm_gbs_step": alg / (m / 1e3) / 1e9,
+            "hbm_frac_step": alg / (m / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "splits": {"sparse": fs.splits, "dense": fd.splits}}
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -323,6 +378,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three plain 256 MiB fp32 copy kernels (y = x * 1), whose HBM counter "
@@ -405,6 +461,14 @@ def main():
                                    "decode": us(two5["decode_ms"])}}
         log(f"fp8: step {ms5*1e3:.1f} us (median {np.median(r5['step_ms'])*1e3:.1f}; {gbs5:.0f} GB/s); "
             f"two-kernel form {us(two5['step_ms']):.1f} us")
+
+    if not args.no_ragged:
+        log("generating the ragged decode workload (batch 128, 13 dense requests)")
+        c3 = wl.decode_ragged_b128()
+        log("timing ragged decode")
+        rg = time_ragged(c3, smla, torch, args.steps, args.warmup, flush)
+        line["ragged_decode"] = rg
+        log(f"ragged: step {rg['ms_per_step']*1e3:.1f} us ({rg['hbm_gbs_step']:.0f} GB/s over {rg['rows']} rows)")
 
     if not args.no_prefill:
         log("generating the grouped-prefill workload (8192 queries on 16384 cached, G = 2)")

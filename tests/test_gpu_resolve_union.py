@@ -108,9 +108,10 @@ def test_union_golden():
 
 @pytest.mark.parametrize("G", [2, 4, 8])
 @pytest.mark.parametrize("Q", [1, 7, 64])
-def test_union_random(G, Q):
+@pytest.mark.parametrize("ns", [5000, 49152, 200000])
+def test_union_random(G, Q, ns):
+    # pools up to 49152 rows take the row-map kernel, larger ones the sorting kernel
     W = 2048 if G == 2 else (1024 if G == 4 else 300)
-    ns = 5000
     slots, valid = wl.random_slot_lists(1000 + G * 10 + Q, Q, W, ns, overlap=0.6, G=G, pad_frac=0.3)
     rng = np.random.default_rng(Q)
     # sprinkle negative rows, rows past the pool and in-list duplicates
