@@ -527,18 +527,16 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   // fp8 also the last wave, whose extra copy is the chunk's row scales
   const bool hi = w < kHiWaves || (kFp8 && w == kS1Waves - 1);
 
-  // ---- prologue. Everything the first gathers need goes out as early as it can:
-  //   - at once (it needs only the kernel's arguments): q, in the order the lanes read it
-  //     back (head quarter hq: piece ks of lane (g, c) = head 16hq + c, dims 32ks + 8g .. +7),
-  //     into ring slots 2.. (wave (hq, x) copies pieces 9x .. 9x+8 of quarter hq); the split's
-  //     table entries table[t][e0 .. e0 + n_ent) (slots when the page size is 1, page ids
-  //     otherwise) into slot_s / page_s; the scalar loads of the token's length and request
-  //     (no branch: map_req is lens when the table holds slots);
+  // ---- prologue. What the first gathers need goes out as early as it can:
+  //   - at once (it needs only the kernel's arguments): the split's table entries
+  //     table[t][e0 .. e0 + n_ent) (slots when the page size is 1, page ids otherwise) into
+  //     slot_s / page_s, and the scalar loads of the token's length and request (no branch:
+  //     map_req is lens when the table holds slots);
   //   - once the request is known, for a page-mapped table: its context length (a scalar
   //     load) and its page-table row, into ring slot 1 when the row fits there.
   // All of it lands before the slots are built, so that building them touches LDS only (a
   // register that a global load may still be writing would make the compiler wait for
-  // every copy in flight, since it does not see them).
+  // every copy in flight, since it does not see them). q follows with the first chunks.
   const int lp = a.log2_page;
   const int r0 = s * a.rows_per_split;
   const bool mapped = a.mapped != 0;
@@ -557,13 +555,19 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   int32_t* const prow_lds = (int32_t*)kvbuf[1];
   const bool row_in_lds = a.map_pt_width <= kChunkBytes / 4;
   int32_t req = -1, seq = 0;
-  {
+  // q, in the order the lanes read it back (head quarter hq: piece ks of lane (g, c) = head
+  // 16hq + c, dims 32ks + 8g .. +7) into ring slots 2.. (wave (hq, x) copies pieces 9x ..
+  // 9x+8 of quarter hq)
+  auto copy_q = [&]() {
     const uint16_t* qh = a.q + (int64_t)t * a.q_tok_stride + (int64_t)(h0 + c) * a.q_head_stride + 8 * g;
 #pragma unroll
     for (int k = 0; k < kQLoads / 2; ++k) {
       const int ks = 9 * x + k;
       dma16(qh + 32 * ks, qlds + ks * 1024);
     }
+  };
+  {
+    if constexpr (UNION) copy_q();              // union mode: q lands with the entries
     int32_t* ent = lp == 0 ? slot_s : page_s;
     for (int k = w; k * 64 < n_ent; k += kS1Waves) {
       const int e = k * 64 + lane;
@@ -600,11 +604,11 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int r1 = min(r0 + a.rows_per_split, len);
   lds_barrier();
 
-  // q to registers (the ring slots it occupied are free after the barrier that ends the
-  // first segment's slot building)
-  bf16x8 qf[kQLoads];
+  bf16x8 qf[kQLoads];                           // decode: loaded with the first chunks
+  if constexpr (UNION) {
 #pragma unroll
-  for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
+    for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
+  }
 
   // plane bases and strides as scalars (a per-lane choice between two fields of the
   // argument struct would otherwise become a memory load)
@@ -890,10 +894,23 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     }
     lds_barrier();
     const int nchunks = (nrows + kChunk - 1) / kChunk;
-    if (nchunks == 0) continue;
 
-    // the first kNBuf - 1 chunks go out together (q is in registers, the ring is free)
-    for (int ci = 0; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+    if constexpr (!UNION) {
+      // decode (one segment): q goes out now, followed by chunks 0 and 1; once q has landed
+      // every wave moves its quarter to registers, and the slots it held take the next
+      // chunks (q follows the slots so that the first gathers are not held up by it)
+      copy_q();
+      for (int ci = 0; ci < 2 && ci < nchunks; ++ci) issue(ci);
+      wait_chunks_w<2, kLoadsHi, kLoadsLo>(hi, min(2, nchunks));   // q, issued before them, has landed
+      lds_barrier();
+#pragma unroll
+      for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
+      lds_barrier();
+      for (int ci = 2; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+    } else {
+      for (int ci = 0; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+    }
+    if (nchunks == 0) continue;
 
 
     // scores and weights of chunk 0
