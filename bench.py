@@ -263,6 +263,34 @@ def time_ragged(c, smla, torch, steps, warmup, flush):
             "splits": {"sparse": fs.splits, "dense": fd.splits}}
 
 
+def time_kv_write(smla, torch, steps, warmup, flush, rows=1 << 20):
+    """smla_kv_write of `rows` bf16 rows into a bf16 pool and into an fp8 pool (e4m3 codes +
+    bf16 rope + fp32 scale per row), slots dealt as whole 64-slot pages in a seeded random
+    order (the page layout of the decode workloads), cold."""
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    src = (torch.randn((rows, 576), generator=gen) * 0.5).to(torch.bfloat16).cuda()
+    pages = torch.randperm(rows // 64, generator=gen).to(torch.int64)
+    smap = (pages[:, None] * 64 + torch.arange(64)[None, :]).reshape(-1).to(torch.int32).cuda()
+    res = {"workload": f"{rows} bf16 rows of 576, slots in 64-slot pages dealt in random order"}
+    for name, code, row_out in (("bf16", smla.SMLA_BF16, 1152), ("fp8", smla.SMLA_FP8_E4M3, 644)):
+        kv = smla.KvCache.empty(code, rows, device="cuda", poison=False)
+        for _ in range(warmup):
+            smla.smla_kv_write(src, smap, kv)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for k in range(steps):
+            flush.sum()
+            ev[k][0].record()
+            smla.smla_kv_write(src, smap, kv)
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))   # median: a first touch can stall one step
+        alg = rows * (1152 + 4 + row_out)                  # source row + slot index + stored payload
+        res[name] = {"us": ms * 1e3, "algorithmic_bytes": alg, "hbm_gbs": alg / (ms / 1e3) / 1e9,
+                     "hbm_frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del kv
+    return res
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -379,6 +407,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ragged", action="store_true")
+    ap.add_argument("--no-kv-write", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three plain 256 MiB fp32 copy kernels (y = x * 1), whose HBM counter "
@@ -479,6 +508,13 @@ def main():
         line["grouped_prefill"] = pr
         log(f"grouped prefill: union {pr['union_us']:.0f} us + attention {pr['prefill_ms']:.2f} ms "
             f"({pr['roofline']['achieved']:.0f} TFLOP/s algorithmic, {pr['roofline']['computed_tflops']:.0f} computed)")
+
+    if not args.no_kv_write:
+        log("timing smla_kv_write (1M rows)")
+        kw = time_kv_write(smla, torch, max(5, args.steps // 5), 3, flush)
+        line["kv_write"] = kw
+        log(f"kv_write: bf16 {kw['bf16']['us']:.0f} us ({kw['bf16']['hbm_gbs']:.0f} GB/s), fp8 {kw['fp8']['us']:.0f} us "
+            f"({kw['fp8']['hbm_gbs']:.0f} GB/s)")
 
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
