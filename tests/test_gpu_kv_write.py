@@ -69,3 +69,44 @@ def test_kv_write_fp8_b64_codes():
     assert np.array_equal(s[:, :512], want["lat8"])
     assert np.array_equal(s[:, 512:640].copy().view(np.uint16), want["rope16"])
     assert np.array_equal(s[:, 640:644].copy().view(np.float32)[:, 0], want["scale"])
+
+
+def _e4m3_values():
+    """Every e4m3 value, and for each pair of neighbours their exact midpoint (a tie) and the
+    fp32 values one step either side of it, both signs, plus zeros and the saturation edge."""
+    mags = [0.0]
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue                                           # 0x7f is NaN
+            mags.append((m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+    mags = np.array(sorted(set(mags)), np.float64)
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf)),
+                           mags.astype(np.float32), np.float32([448.0, np.nextafter(np.float32(448), np.float32(0))])])
+    vals = np.concatenate([near, -near, np.float32([0.0, -0.0, 1e-45, -1e-45, 2.0 ** -130])]).astype(np.float32)
+    return vals
+
+
+def test_kv_write_fp8_rounding_edges():
+    """The stored e4m3 codes of values at and around every rounding midpoint (ties to even),
+    subnormals, signed zeros and the top of the range equal the reference encoder's. A row
+    whose latent amax is 448 has scale 1, so its codes are the encodings of the values."""
+    vals = _e4m3_values()
+    per = 511
+    n = -(-len(vals) // per)
+    src = np.zeros((n, 576), np.float32)
+    src[:, 0] = 448.0
+    flat = np.zeros(n * per, np.float32)
+    flat[:len(vals)] = vals
+    src[:, 1:512] = flat.reshape(n, per)
+    ns = n + 3
+    smap = np.arange(n, dtype=np.int32) + 1
+    kv = smla.KvCache.empty(smla.SMLA_FP8_E4M3, ns)
+    smla.smla_kv_write(torch.from_numpy(src).cuda(), torch.from_numpy(smap).cuda(), kv)
+    pool = oracle.Pool(ns, "fp8")
+    oracle.kv_write(pool, src, "f32", smap)
+    want = pool.stored(smap)
+    s = kv.storage.cpu().numpy()[smap]
+    assert np.all(want["scale"] == np.float32(1.0))
+    assert np.array_equal(s[:, :512], want["lat8"])
