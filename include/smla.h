@@ -274,14 +274,14 @@ smla_status smla_build_group_union(const int32_t* slots, int64_t slots_stride, c
  * of members past Q are not written. Same score, value and LSE definitions as decode.
  *
  *   q    bf16 [Q, H, 576] token-major, strides in elements
- *   kv   bf16 pool, or fp8 e4m3 pool when H == 64 (dequantised in the kernel as in decode)
+ *   kv   bf16 pool, or fp8 e4m3 pool (dequantised in the kernel as in decode)
  *   enc, lens  as produced by smla_build_group_union for the same Q and G
  *   out  bf16 [Q, H, 512]; lse fp32 [Q, H] or NULL
  * Supported: G * H == 128 with G in {2, 4, 8} (H = 64, 32, 16); enc_width <= 2^24.
- * With H == 64 one query's heads already fill four 16-row MFMA tiles on gfx950: each
- * query runs as one workgroup of the decode kernel, which walks its group's union in
- * segments and keeps the entries its bit names (the group still shares one union and
- * its rows). Other H run one 128-row tile per group. Errors as smla_sparse_decode.
+ * On gfx950 64 heads fill four 16-row MFMA tiles: the group's 128 rows run as two
+ * workgroups of the decode kernel, each serving 64 / H queries of the group; each walks the
+ * group's union in segments, keeps the entries that name one of its queries, and masks each
+ * head by its own query's bit. Errors as smla_sparse_decode.
  * ------------------------------------------------------------------------------- */
 typedef struct {
   int32_t Q;

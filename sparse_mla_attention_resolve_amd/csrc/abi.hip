@@ -357,8 +357,8 @@ smla_status smla_grouped_prefill(const smla_prefill_args* a, void* stream) {
   CHECK(a->reserved1 == 0, SMLA_ERR_SHAPE, "%s: reserved1 must be 0", fn);
   CHECK((a->G == 2 || a->G == 4 || a->G == 8) && a->G * a->H == 128, SMLA_ERR_UNSUPPORTED,
         "%s: needs G in {2, 4, 8} and G * H == 128 (got G=%d, H=%d)", fn, a->G, a->H);
-  CHECK(a->kv.dtype == SMLA_BF16 || (a->kv.dtype == SMLA_FP8_E4M3 && a->H == 64), SMLA_ERR_UNSUPPORTED,
-        "%s: the cache must be bf16, or fp8 e4m3 with H == 64", fn);
+  CHECK(a->kv.dtype == SMLA_BF16 || a->kv.dtype == SMLA_FP8_E4M3, SMLA_ERR_UNSUPPORTED,
+        "%s: the cache must be bf16 or fp8 e4m3", fn);
   CHECK(a->enc_width <= (1 << 24), SMLA_ERR_RANGE, "%s: enc_width must be <= 2^24", fn);
   CHECK(a->enc_width >= 1 && a->enc_stride >= a->enc_width, SMLA_ERR_SHAPE,
         "%s: enc_width must be >= 1 and <= enc_stride", fn);

@@ -61,9 +61,12 @@ struct Stage1Args {
   // splits, in wall-clock ticks (0: never wait)
   uint32_t* sync;
   int32_t wait_ticks;
-  // union mode (grouped prefill), when > 0: token t is query t of group t / union_G, whose
-  // table row and length are the group's union (entries = row | member bits << 24); the
-  // kernel takes the entries whose bit t % union_G is set. One split per token (S = 1).
+  // union mode (grouped prefill), when > 0: the G = union_G queries of a group have H heads
+  // each (G * H = 128); workgroup t serves 64 / H of them (members m0 .. m0 + 64/H - 1 of
+  // group t / (G * H / 64)), its 64 heads being theirs in order. The table row and length are
+  // the group's union (entries = row | member bits << 24); the kernel keeps the entries that
+  // name one of its members, and each head attends only to its own member's. One split
+  // (S = 1); workgroups whose first member is past the last query do nothing.
   int32_t union_G;
 };
 
@@ -541,8 +544,18 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int r0 = s * a.rows_per_split;
   const bool mapped = a.mapped != 0;
   constexpr bool umode = UNION;                         // a.union_G > 0
-  const int trow_id = umode ? t / a.union_G : t;       // the token's table row (union mode: its group's)
-  const int member = umode ? t % a.union_G : 0;
+  // union mode: heads per query, queries per workgroup, workgroups per group, this
+  // workgroup's group and first member; head hh of the workgroup is head hh % uH of query
+  // grp * G + m0 + hh / uH
+  const int uH = umode ? a.H : kHeads;
+  const int mpw = kHeads / uH;
+  const int wgpg = umode ? a.union_G / mpw : 1;
+  const int grp = umode ? t / wgpg : t;
+  const int m0 = umode ? (t % wgpg) * mpw : 0;
+  auto tok_of = [&](int hh) { return umode ? grp * a.union_G + m0 + hh / uH : t; };
+  auto head_of = [&](int hh) { return umode ? hh % uH : hh; };
+  if (umode && tok_of(0) >= a.T) return;               // a short last group's missing members
+  const int trow_id = grp;                             // the table row (union mode: the group's)
   const int len_raw = a.lens[trow_id];
   const int req_raw = a.map_req[trow_id];
   const int len = len_raw < 0 ? 0 : (len_raw > a.max_len ? a.max_len : len_raw);
@@ -559,7 +572,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   // 16hq + c, dims 32ks + 8g .. +7) into ring slots 2.. (wave (hq, x) copies pieces 9x ..
   // 9x+8 of quarter hq)
   auto copy_q = [&]() {
-    const uint16_t* qh = a.q + (int64_t)t * a.q_tok_stride + (int64_t)(h0 + c) * a.q_head_stride + 8 * g;
+    const int qt = min(tok_of(h0 + c), a.T - 1);       // a short group repeats its last query
+    const uint16_t* qh = a.q + (int64_t)qt * a.q_tok_stride + (int64_t)head_of(h0 + c) * a.q_head_stride + 8 * g;
 #pragma unroll
     for (int k = 0; k < kQLoads / 2; ++k) {
       const int ks = 9 * x + k;
@@ -595,9 +609,13 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     wait_vmcnt<0>();                            // no copy may land after the workgroup is gone
     if ((a.sync != nullptr || umode) && len == 0 && s == 0) {
       // a token with no rows: zero output and lse -inf (stage 2 would write them otherwise)
-      uint16_t* ob = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride;
-      for (int i = tid; i < kHeads * kLatent; i += kS1Threads) ob[(int64_t)(i >> 9) * a.out_head_stride + (i & 511)] = 0;
-      if (a.lse && tid < kHeads) a.lse[(int64_t)t * a.lse_tok_stride + tid] = -INFINITY;
+      for (int i = tid; i < kHeads * kLatent; i += kS1Threads) {
+        const int hh = i >> 9, tk = tok_of(hh);
+        if (tk < a.T)
+          ((uint16_t*)a.out)[(int64_t)tk * a.out_tok_stride + (int64_t)head_of(hh) * a.out_head_stride + (i & 511)] = 0;
+      }
+      if (a.lse && tid < kHeads && tok_of(tid) < a.T)
+        a.lse[(int64_t)tok_of(tid) * a.lse_tok_stride + head_of(tid)] = -INFINITY;
     }
     return;
   }
@@ -654,14 +672,14 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     if (!(k < kLoadsLo || row_hi)) {
       if constexpr (kFp8) {
         if (scale_wave && lane < kChunk) {
-          const int32_t sl = cp.slot[k];
+          const int32_t sl = umode && cp.slot[k] >= 0 ? cp.slot[k] & ((1 << SMLA_UNION_ROW_BITS) - 1) : cp.slot[k];
           dma4(sl >= 0 ? (const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride : (const char*)kZeroRow,
                (char*)(scale_s + ci * kChunk));
         }
       }
       return;
     }
-    const int32_t sl = cp.slot[k];
+    const int32_t sl = umode && cp.slot[k] >= 0 ? cp.slot[k] & ((1 << SMLA_UNION_ROW_BITS) - 1) : cp.slot[k];
     const int unit = lpos[k] >> 8;
     const bool live = sl >= 0;
     const uint32_t slot = live ? (uint32_t)sl : 0u;
@@ -708,10 +726,14 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     if constexpr (kFp8) sc = *(const float4*)(scale_s + ci * kChunk + 16 * x + 4 * g);
     const float raw[4] = {kFp8 ? sl[0] * sc.x + sr[0] : sl[0], kFp8 ? sl[1] * sc.y + sr[1] : sl[1],
                           kFp8 ? sl[2] * sc.z + sr[2] : sl[2], kFp8 ? sl[3] * sc.w + sr[3] : sl[3]};
-    sv[0] = lv.x >= 0 ? raw[0] * a.scale_log2 : -INFINITY;
-    sv[1] = lv.y >= 0 ? raw[1] * a.scale_log2 : -INFINITY;
-    sv[2] = lv.z >= 0 ? raw[2] * a.scale_log2 : -INFINITY;
-    sv[3] = lv.w >= 0 ? raw[3] * a.scale_log2 : -INFINITY;
+    // a row counts for head h0 + c when its slot is valid and, in union mode, when it names
+    // the head's own member
+    const int mbit = SMLA_UNION_ROW_BITS + (umode ? (h0 + c) / uH : 0);
+    auto ok = [&](int e) { return e >= 0 && (!umode || ((e >> mbit) & 1)); };
+    sv[0] = ok(lv.x) ? raw[0] * a.scale_log2 : -INFINITY;
+    sv[1] = ok(lv.y) ? raw[1] * a.scale_log2 : -INFINITY;
+    sv[2] = ok(lv.z) ? raw[2] * a.scale_log2 : -INFINITY;
+    sv[3] = ok(lv.w) ? raw[3] * a.scale_log2 : -INFINITY;
     // the partner read this wave's previous tile before it reached the barrier that this
     // wave passed last, so the slot is free
 #pragma unroll
@@ -817,8 +839,10 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       for (int k = 0; k < kPer; ++k) {
         const int i = tid + k * kS1Threads;
         const uint32_t e = i < nraw ? (uint32_t)slot_s[i] : 0u;
-        ent[k] = e & ((1u << SMLA_UNION_ROW_BITS) - 1u);
-        keep[k] = i < nraw && ((e >> (SMLA_UNION_ROW_BITS + member)) & 1u) && (int64_t)ent[k] < a.kv.num_slots;
+        const uint32_t row = e & ((1u << SMLA_UNION_ROW_BITS) - 1u);
+        const uint32_t bits = (e >> (SMLA_UNION_ROW_BITS + m0)) & ((1u << mpw) - 1u);   // this workgroup's members
+        ent[k] = row | (bits << SMLA_UNION_ROW_BITS);
+        keep[k] = i < nraw && bits != 0u && (int64_t)row < a.kv.num_slots;
         const uint64_t b = __ballot(keep[k]);
         before[k] = __popcll(b & ((1ull << lane) - 1ull));
         if (lane == 0) wcnt[k][w] = __popcll(b);
@@ -959,13 +983,17 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
 #pragma unroll
   for (int v = 0; v < 4; ++v) inv[v] = __shfl(inv_c, 4 * g + v, 64);
   if (umode || len <= a.rows_per_split) {
-    uint16_t* ob = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)(h0 + 4 * g) * a.out_head_stride +
-                   256 * x + c;
 #pragma unroll
-    for (int nt = 0; nt < 16; ++nt)
+    for (int v = 0; v < 4; ++v) {
+      const int hh = h0 + 4 * g + v, tk = tok_of(hh);
+      if (tk >= a.T) continue;
+      uint16_t* ob = (uint16_t*)a.out + (int64_t)tk * a.out_tok_stride + (int64_t)head_of(hh) * a.out_head_stride +
+                     256 * x + c;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) ob[v * a.out_head_stride + 16 * nt] = (uint16_t)f32_to_bf16_rne(oacc[nt][v] * inv[v]);
-    if (a.lse && x == 0 && g == 0) a.lse[(int64_t)t * a.lse_tok_stride + h0 + c] = lse_c;
+      for (int nt = 0; nt < 16; ++nt) ob[16 * nt] = (uint16_t)f32_to_bf16_rne(oacc[nt][v] * inv[v]);
+    }
+    if (a.lse && x == 0 && g == 0 && tok_of(h0 + c) < a.T)
+      a.lse[(int64_t)tok_of(h0 + c) * a.lse_tok_stride + head_of(h0 + c)] = lse_c;
     return;
   }
   // (agent-coherent stores: workgroups of this launch may merge them)
@@ -1336,10 +1364,12 @@ hipError_t launch_union_decode(const smla_prefill_args& d, hipStream_t stream) {
   a.sync = nullptr;
   a.wait_ticks = 0;
   a.union_G = d.G;
+  // 64 / H queries per workgroup, G * H / 64 workgroups per group
+  const dim3 grid((unsigned)(((d.Q + d.G - 1) / d.G) * (d.G * d.H / kHeads)));
   if (d.kv.dtype == SMLA_BF16)
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, true>), dim3(d.Q), dim3(kS1Threads), 0, stream, a);
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, true>), grid, dim3(kS1Threads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, true>), dim3(d.Q), dim3(kS1Threads), 0, stream, a);
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, true>), grid, dim3(kS1Threads), 0, stream, a);
   return hipGetLastError();
 }
 

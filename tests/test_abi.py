@@ -169,9 +169,7 @@ def test_prefill_checks():
         return lib.smla_grouped_prefill(ctypes.byref(a), None)
     assert p(H=32) == UNSUP                          # G * H != 128
     assert p(G=3, H=43) == UNSUP
-    # an fp8 cache is read only on the H == 64 path
-    assert p(G=4, H=32, kv_dtype=S.SMLA_FP8_E4M3, kv_lat8=FAKE, kv_rope16=FAKE, kv_scale=FAKE, kv_lat8_stride=656,
-             kv_rope16_stride=656, kv_scale_stride=656) == UNSUP
+    assert p(kv_dtype=S.SMLA_F32, kv_row_stride=2304) == UNSUP   # fp32 caches are decode-only
     assert p(enc_width=5000) == SHAPE
     assert p(q=None) == NULL
     assert p(Q=0) == OK
