@@ -175,6 +175,10 @@ constexpr int kS1Waves = 8;
 constexpr int kS1Threads = 64 * kS1Waves;
 constexpr int kQLoads = 18;                 // 16-byte q pieces per lane: 16 heads x 72 units / 64 lanes
 constexpr int kAhead = 4;                   // LDS operand reads kept in flight ahead of the MFMAs
+#ifndef SMLA_PV_IN_A
+#define SMLA_PV_IN_A 4
+#endif
+constexpr int kPvA = SMLA_PV_IN_A;          // P V tiles of chunk ci computed with the scores of chunk ci + 1
 
 // Workgroup id -> (token, split). Workgroups are dispatched to the 8 XCDs round robin;
 // when T is a multiple of 8 every split of a token runs on one XCD, so the token's partial
@@ -266,13 +270,15 @@ struct Offsets {
 // the operand reads run kAhead steps ahead. sl receives the latent part of the scores, sr
 // the rotary part (fp8 only; bf16 sums both into sl). after_step(k) runs after step k's
 // MFMAs are issued (the caller spreads its gathers of a later chunk over the steps).
-template <int KV, bool DO_S, bool DO_PV, typename Hook>
+template <int KV, bool DO_S, bool DO_PV, typename Hook, int PV0 = 0, int PV1 = 16>
 __device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, const Offsets<KV>& off, int x, int g,
                                            int c, const bf16x8 (&qf)[kQLoads], f32x4& sl, f32x4& sr,
                                            const bf16x8& pa, f32x4 (&oacc)[16], Hook&& after_step) {
   constexpr bool kFp8 = KV == SMLA_FP8_E4M3;
   constexpr int kRowBytes = Lay<KV>::kUnits * 16;
-  constexpr int kSteps = DO_S ? 18 : 16;
+  // P V tiles PV0 .. PV1 - 1 (at steps 0 .. PV1 - PV0 - 1)
+  constexpr int kNPV = DO_PV ? PV1 - PV0 : 0;
+  constexpr int kSteps = DO_S ? 18 : kNPV;
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   f32x4 racc = f32x4{0.f, 0.f, 0.f, 0.f};
   // score step ks: bf16 k steps 0 .. 17; fp8 latent k steps 0 .. 15, then rotary 16, 17
@@ -304,7 +310,7 @@ __device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, con
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) {
     if constexpr (DO_S) kq[i] = kread(i);
-    if constexpr (DO_PV) vq[i] = vread(i);
+    if constexpr (DO_PV) { if (i < kNPV) vq[i] = vread(PV0 + i); }
   }
 #pragma unroll
   for (int k = 0; k < kSteps; ++k) {
@@ -320,11 +326,11 @@ __device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, con
       }
     }
     if constexpr (DO_PV) {
-      if (k < 16) {
-        if (k + kAhead < 16) vq[(k + kAhead) % (kAhead + 1)] = vread(k + kAhead);
+      if (k < kNPV) {
+        if (k + kAhead < kNPV) vq[(k + kAhead) % (kAhead + 1)] = vread(PV0 + k + kAhead);
         const uint4 vv = vq[k % (kAhead + 1)];
         const bf16x8 b = kFp8 ? e4m3x8_to_bf16x8(vv.x, vv.y) : as_bf16x8(vv);
-        oacc[k] = mfma16x16x32(pa, b, oacc[k]);
+        oacc[PV0 + k] = mfma16x16x32(pa, b, oacc[PV0 + k]);
       }
     }
     after_step(k);
@@ -960,14 +966,16 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       const int cn = ci + kNBuf - 1;
       const bool refill = cn < nchunks;
       const Copies cp = src_of(refill ? cn : ci);   // (ci: a valid chunk whose slots go unused)
-      chunk_step<KV, true, false>(kvbuf[(ci + 1) % kNBuf], kvbuf[(ci + 1) % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
-                                  [&](int k) {
-                                    if (refill && (k & 3) == 1 && (k >> 2) < kLoadsHi) fire(cp, cn, k >> 2);
-                                  });
+      auto gathers = [&](int k) {
+        if (refill && (k & 3) == 1 && (k >> 2) < kLoadsHi) fire(cp, cn, k >> 2);
+      };
+      chunk_step<KV, true, (kPvA > 0), decltype((gathers)), 0, kPvA>(kvbuf[(ci + 1) % kNBuf], kvbuf[ci % kNBuf], off, x,
+                                                                    g, c, qf, sl, sr, pa, oacc, gathers);
       publish(ci + 1);
       lds_barrier();
-      chunk_step<KV, false, true>(kvbuf[ci % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl, sr, pa, oacc,
-                                  [&](int k) { piece(ci + 1, k); });
+      auto pieces = [&](int k) { piece(ci + 1, k); };
+      chunk_step<KV, false, true, decltype((pieces)), kPvA, 16>(kvbuf[ci % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl,
+                                                              sr, pa, oacc, pieces);
       finish();
     }
     chunk_step<KV, false, true>(kvbuf[(nchunks - 1) % kNBuf], kvbuf[(nchunks - 1) % kNBuf], off, x, g, c, qf, sl, sr,
