@@ -363,11 +363,13 @@ constexpr int kExitShift = 9, kGiveUpShift = 18;
 constexpr int kBufFlags = 0x00020000;       // buffer descriptor word 3: 32-bit data format
 constexpr int kSc1 = 16;                    // cache-policy operand of buffer loads: sc1
 
+// The merge parts of the workgroup that arrived q-th among nact: a contiguous range of the
+// eight (one part each from 8 splits on, none for q >= 8), so that the two column halves of a
+// head quarter usually fall to one workgroup, which merges them in one pass.
 __device__ __forceinline__ uint32_t parts_of(int q, int nact) {
-  uint32_t m = 0;
-  if (q < 8)
-    for (int k = q; k < 8; k += nact) m |= 1u << k;
-  return m;
+  if (nact >= 8) return q < 8 ? 1u << q : 0u;
+  const int p0 = (8 * q + nact - 1) / nact, p1 = (8 * (q + 1) + nact - 1) / nact;
+  return ((1u << p1) - 1u) & ~((1u << p0) - 1u);
 }
 
 // Part p (0 .. 7) of token t's merge: heads 16(p >> 1) .. +15 x columns 256(p & 1) .. +255,
@@ -377,7 +379,11 @@ __device__ __forceinline__ uint32_t parts_of(int q, int nact) {
 // part's 16 x 8 LSEs into LDS (`scratch`, 128 floats) while every thread has its eight
 // 16-byte slices in flight; the weights keep a running maximum:
 // O = sum_s exp(lse_s - lse) O_s with lse = log sum_s exp(lse_s).
+// NP = 2 merges parts p and p + 1 (p even: the two column halves of one head quarter, entries
+// 1024 further on, columns 256 further on) with the same LSEs and weights.
+template <int NP>
 __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact, int p, int tid, float* scratch) {
+  static_assert(NP == 1 || NP == 2, "one part or a head quarter's two");
   constexpr int kBatch = 8;
   const int j = 1024 * p + 2 * tid;
   const int lanep = j & 63, ntp = (j >> 6) & 15;
@@ -388,12 +394,13 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact,
       (void*)((uint16_t*)a.part_o + (int64_t)t * a.S * (kHeads * kLatent)), (short)0, 0x7fffffff, kBufFlags);
   const __amdgpu_buffer_rsrc_t rl =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.part_lse + (int64_t)t * a.S * a.H), (short)0, 0x7fffffff, kBufFlags);
-  float mx[4], ws[4], acc[4][2];
+  float mx[4], ws[4], acc[NP][4][2];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     mx[v] = -INFINITY;
     ws[v] = 0.f;
-    acc[v][0] = acc[v][1] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NP; ++n) acc[n][v][0] = acc[n][v][1] = 0.f;
   }
   for (int s0 = 0; s0 < nact; s0 += kBatch) {
     // (every thread loads an in-range LSE, unconditionally, so that no wait for it comes
@@ -401,12 +408,15 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact,
     const int ls = s0 + ((tid >> 4) & (kBatch - 1));
     const float lv = __builtin_bit_cast(
         float, __builtin_amdgcn_raw_buffer_load_b32(rl, ((ls < nact ? ls : s0) * a.H + 16 * (p >> 1) + (tid & 15)) * 4, 0, kSc1));
-    uint4 o[kBatch];
+    uint4 o[NP][kBatch];
 #pragma unroll
-    for (int jj = 0; jj < kBatch; ++jj) {
-      const int sp = s0 + jj < nact ? s0 + jj : s0;
-      o[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ro, sp * (kHeads * kLatent * 2) + 8 * j, 0, kSc1));
-    }
+    for (int n = 0; n < NP; ++n)
+#pragma unroll
+      for (int jj = 0; jj < kBatch; ++jj) {
+        const int sp = s0 + jj < nact ? s0 + jj : s0;
+        o[n][jj] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(ro, sp * (kHeads * kLatent * 2) + 8 * (j + 1024 * n), 0, kSc1));
+      }
     __syncthreads();                                     // the previous batch's LSEs are read
     if (tid < 16 * kBatch) scratch[tid] = ls < nact ? lv * kLog2e : -INFINITY;   // base 2 from here on
     __syncthreads();
@@ -421,17 +431,23 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact,
       if (bm == -INFINITY) continue;                     // nothing but empty splits so far
       const float r = __builtin_amdgcn_exp2f(mx[v] - bm);   // 0 on the first non-empty pass
       ws[v] *= r;
-      acc[v][0] *= r;
-      acc[v][1] *= r;
+#pragma unroll
+      for (int n = 0; n < NP; ++n) {
+        acc[n][v][0] *= r;
+        acc[n][v][1] *= r;
+      }
 #pragma unroll
       for (int jj = 0; jj < kBatch; ++jj) {
         const float lw = ((const float*)&l[jj])[v];
         const float wgt = lw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lw - bm);
         ws[v] += wgt;
         // entry 2i: words x, y = heads (0, 1), (2, 3) at col; entry 2i + 1: z, w at col + 1
-        const uint32_t w0 = v < 2 ? o[jj].x : o[jj].y, w1 = v < 2 ? o[jj].z : o[jj].w;
-        acc[v][0] += wgt * bf16_to_f32((v & 1) ? (w0 >> 16) : (w0 & 0xffffu));
-        acc[v][1] += wgt * bf16_to_f32((v & 1) ? (w1 >> 16) : (w1 & 0xffffu));
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+          const uint32_t w0 = v < 2 ? o[n][jj].x : o[n][jj].y, w1 = v < 2 ? o[n][jj].z : o[n][jj].w;
+          acc[n][v][0] += wgt * bf16_to_f32((v & 1) ? (w0 >> 16) : (w0 & 0xffffu));
+          acc[n][v][1] += wgt * bf16_to_f32((v & 1) ? (w1 >> 16) : (w1 & 0xffffu));
+        }
       }
       mx[v] = bm;
     }
@@ -440,7 +456,8 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact,
   for (int v = 0; v < 4; ++v) {
     const float inv = ws[v] > 0.f ? 1.0f / ws[v] : 0.f;
     uint32_t* o = (uint32_t*)((uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)(hb + v) * a.out_head_stride + col);
-    *o = pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv);
+#pragma unroll
+    for (int n = 0; n < NP; ++n) o[128 * n] = pack_bf16x2(acc[n][v][0] * inv, acc[n][v][1] * inv);
     if (a.lse && (p & 1) == 0 && ntp == 0 && (lanep & 15) == 0)
       a.lse[(int64_t)t * a.lse_tok_stride + hb + v] = ws[v] > 0.f ? (mx[v] + log2f(ws[v])) * kLn2 : -INFINITY;
   }
@@ -488,8 +505,15 @@ __device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int nac
     if (bcast) todo = parts_of(q, nact);
   }
 #pragma unroll 1
-  for (int k = 0; k < 8; ++k)
-    if ((todo >> k) & 1u) merge_part(a, t, nact, k, tid, scratch);
+  for (int k = 0; k < 8; ++k) {
+    if (!((todo >> k) & 1u)) continue;
+    if ((k & 1) == 0 && ((todo >> (k + 1)) & 1u)) {
+      merge_part<2>(a, t, nact, k, tid, scratch);         // both column halves of a head quarter
+      ++k;
+    } else {
+      merge_part<1>(a, t, nact, k, tid, scratch);
+    }
+  }
   if (tid == 0) {
     const uint32_t o3 = __hip_atomic_fetch_add(word, 1u << kExitShift, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (((o3 >> kExitShift) & kArrMask) == (uint32_t)nact - 1)   // everyone else is done with the word
