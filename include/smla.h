@@ -136,14 +136,18 @@ smla_status smla_resolve_slots(const int32_t* idx, int64_t idx_stride, const int
  * Stage 1 splits each token's rows into num_splits contiguous ranges and computes, per
  * range, a partial output and its log-sum-exp; the ranges are then merged by LSE
  * (IBM Triton paged-attention explainer, section 4 table, "Parallel Tiled Softmax"),
- * all on `stream`, through the workspace. On the bf16 path (T <= 4096) the merge runs at
+ * all on `stream`, through the workspace. On the bf16 path (T * ceil(H / 64) <= 4096) the merge runs at
  * the end of stage 1: the workgroups of a token take tickets on a counter word in the
  * workspace and share the merge once every partial is written (each waits a bounded
  * time for the others; the last to arrive merges whatever was given up), so one kernel
  * produces out and lse. Otherwise a second kernel (stage 2) merges.
  *
  * Supported combinations:
- *   q_dtype SMLA_BF16, kv dtype SMLA_BF16 or SMLA_FP8_E4M3, H == 64 (bf16 MFMA path);
+ *   q_dtype SMLA_BF16, kv dtype SMLA_BF16 or SMLA_FP8_E4M3, 1 <= H <= 128 (bf16 MFMA path:
+ *     64 heads fill the four 16-row tiles of a workgroup, so a token of up to 64 heads is one
+ *     block of 64 head slots and a token of 65 .. 128 heads two, each block with its own
+ *     splits and workgroups; fewer than 64 heads leave slots that compute and are dropped,
+ *     which costs MFMA time but no memory traffic);
  *   q_dtype SMLA_F32,  kv dtype SMLA_F32, 1 <= H <= 128 (fp32 path).
  * Outputs: out[t, h, 0..511] in q's dtype; lse[t, h] = natural log of
  * sum_j exp(scale * q.k_j) in fp32, -inf (and out = 0) when a token has no rows.
@@ -192,7 +196,7 @@ smla_status smla_sparse_decode(const smla_decode_args* args, void* workspace, si
 
 /* The two stages on their own, for callers that time or overlap them. Stage 1 followed
  * by stage 2 (same arguments, same workspace) is exactly smla_sparse_decode. When stage 1
- * merges the splits itself (bf16 path, T <= 4096) it writes out and lse, and stage 2
+ * merges the splits itself (bf16 path, T * ceil(H / 64) <= 4096) it writes out and lse, and stage 2
  * enqueues nothing; otherwise stage 1 leaves each split's partial output and LSE in the
  * workspace and stage 2 merges them. On the bf16 path a token whose rows fit one split is
  * always written by stage 1 directly. */

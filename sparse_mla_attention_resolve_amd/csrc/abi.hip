@@ -136,7 +136,7 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   if (bf16) {
     CHECK(a->kv.dtype == SMLA_BF16 || a->kv.dtype == SMLA_FP8_E4M3, SMLA_ERR_UNSUPPORTED,
           "%s: bf16 q needs a bf16 or fp8 cache", fn);
-    CHECK(a->H == 64, SMLA_ERR_UNSUPPORTED, "%s: the bf16 path implements H == 64 (got %d)", fn, a->H);
+    CHECK(a->H >= 1 && a->H <= 128, SMLA_ERR_UNSUPPORTED, "%s: the bf16 path takes 1 <= H <= 128 (got %d)", fn, a->H);
   } else if (a->q_dtype == SMLA_F32) {
     CHECK(a->kv.dtype == SMLA_F32, SMLA_ERR_UNSUPPORTED, "%s: fp32 q needs an fp32 cache", fn);
     CHECK(a->H >= 1 && a->H <= 128, SMLA_ERR_UNSUPPORTED, "%s: the fp32 path takes 1 <= H <= 128", fn);
@@ -176,16 +176,22 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   plan->T = a->T;
   plan->H = a->H;
   plan->max_len = (int32_t)max_len;
-  plan_splits(a->T, (int32_t)max_len, a->num_splits, &plan->S, &plan->rows_per_split);
+  // bf16 q: tokens of up to 64 heads are one block, of 65 .. 128 heads two; the splits, the
+  // partials and the merge words are per (token, block), each block holding 64 head slots
+  plan->hblocks = bf16 ? (a->H + 63) / 64 : 1;
+  const int64_t tv = (int64_t)a->T * plan->hblocks;
+  CHECK(tv <= (1 << 24), SMLA_ERR_RANGE, "%s: T * ceil(H / 64) must be <= 2^24", fn);
+  const int64_t hslots = bf16 ? 64 : a->H;
+  plan_splits((int32_t)tv, (int32_t)max_len, a->num_splits, &plan->S, &plan->rows_per_split);
   // the bf16 path keeps its partial outputs in bf16, the fp32 path in fp32
-  plan->part_o_bytes = (size_t)a->T * plan->S * a->H * SMLA_LATENT * (bf16 ? 2 : 4);
-  plan->part_lse_bytes = (size_t)a->T * plan->S * a->H * sizeof(float);
-  // bf16 q: the splits of a token merge at the end of stage 1 through a word per token at
-  // the head of the workspace; a workgroup waits for its token's other splits (at most
+  plan->part_o_bytes = (size_t)tv * plan->S * hslots * SMLA_LATENT * (bf16 ? 2 : 4);
+  plan->part_lse_bytes = (size_t)tv * plan->S * hslots * sizeof(float);
+  // bf16 q: the splits of a block merge at the end of stage 1 through a word per block at
+  // the head of the workspace; a workgroup waits for its block's other splits (at most
   // 10 us) only when the whole grid is resident at once
   plan->sync_bytes = bf16 ? smla::kSyncBytes : 0;
-  plan->fused = bf16 && a->T <= smla::kSyncTokens;
-  plan->wait_ticks = (int64_t)a->T * plan->S <= device_cus() ? wall_ticks(10) : 0;
+  plan->fused = bf16 && tv <= smla::kSyncTokens;
+  plan->wait_ticks = tv * plan->S <= device_cus() ? wall_ticks(10) : 0;
   plan->ws_bytes = plan->sync_bytes + (plan->part_o_bytes + plan->part_lse_bytes + 255) / 256 * 256;
   return SMLA_OK;
 }

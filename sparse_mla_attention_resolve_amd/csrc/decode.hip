@@ -68,6 +68,11 @@ struct Stage1Args {
   // name one of its members, and each head attends only to its own member's. One split
   // (S = 1); workgroups whose first member is past the last query do nothing.
   int32_t union_G;
+  // decode, bf16 q: blocks of 64 heads per token (1, or 2 for H up to 128). Workgroups cover
+  // hblocks * T virtual tokens, block-major (virtual token b * T + t is block b of token t),
+  // each with 64 head slots; slots past the block's real heads read the block's last head
+  // and write nothing. Partials and merge words are per virtual token.
+  int32_t hblocks;
 };
 
 // Physical slot of position p of token t's table row, or -1 when masked.
@@ -381,8 +386,11 @@ __device__ __forceinline__ uint32_t parts_of(int q, int nact) {
 // O = sum_s exp(lse_s - lse) O_s with lse = log sum_s exp(lse_s).
 // NP = 2 merges parts p and p + 1 (p even: the two column halves of one head quarter, entries
 // 1024 further on, columns 256 further on) with the same LSEs and weights.
+// t is the virtual token (its partials and LSEs), tr the token and hbase + hb its output heads,
+// of which the first hv of the 64 exist.
 template <int NP>
-__device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact, int p, int tid, float* scratch) {
+__device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int tr, int hbase, int hv, int nact, int p,
+                                           int tid, float* scratch) {
   static_assert(NP == 1 || NP == 2, "one part or a head quarter's two");
   constexpr int kBatch = 8;
   const int j = 1024 * p + 2 * tid;
@@ -393,7 +401,7 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact,
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((uint16_t*)a.part_o + (int64_t)t * a.S * (kHeads * kLatent)), (short)0, 0x7fffffff, kBufFlags);
   const __amdgpu_buffer_rsrc_t rl =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.part_lse + (int64_t)t * a.S * a.H), (short)0, 0x7fffffff, kBufFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.part_lse + (int64_t)t * a.S * kHeads), (short)0, 0x7fffffff, kBufFlags);
   float mx[4], ws[4], acc[NP][4][2];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -407,7 +415,7 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact,
     // before the slices go out; only threads < 128 keep theirs)
     const int ls = s0 + ((tid >> 4) & (kBatch - 1));
     const float lv = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rl, ((ls < nact ? ls : s0) * a.H + 16 * (p >> 1) + (tid & 15)) * 4, 0, kSc1));
+        float, __builtin_amdgcn_raw_buffer_load_b32(rl, ((ls < nact ? ls : s0) * kHeads + 16 * (p >> 1) + (tid & 15)) * 4, 0, kSc1));
     uint4 o[NP][kBatch];
 #pragma unroll
     for (int n = 0; n < NP; ++n)
@@ -454,18 +462,21 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int nact,
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
+    if (hb + v >= hv) continue;                         // a head slot past the block's heads
     const float inv = ws[v] > 0.f ? 1.0f / ws[v] : 0.f;
-    uint32_t* o = (uint32_t*)((uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)(hb + v) * a.out_head_stride + col);
+    uint32_t* o =
+        (uint32_t*)((uint16_t*)a.out + (int64_t)tr * a.out_tok_stride + (int64_t)(hbase + hb + v) * a.out_head_stride + col);
 #pragma unroll
     for (int n = 0; n < NP; ++n) o[128 * n] = pack_bf16x2(acc[n][v][0] * inv, acc[n][v][1] * inv);
     if (a.lse && (p & 1) == 0 && ntp == 0 && (lanep & 15) == 0)
-      a.lse[(int64_t)t * a.lse_tok_stride + hb + v] = ws[v] > 0.f ? (mx[v] + log2f(ws[v])) * kLn2 : -INFINITY;
+      a.lse[(int64_t)tr * a.lse_tok_stride + hbase + hb + v] = ws[v] > 0.f ? (mx[v] + log2f(ws[v])) * kLn2 : -INFINITY;
   }
 }
 
-// Called by every active split workgroup of token t once its partial is stored, with nact >= 2 the
-// token's active splits.
-__device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int nact, int tid, float* scratch) {
+// Called by every active split workgroup of virtual token t (token tr, heads hbase .. hbase + hv
+// - 1) once its partial is stored, with nact >= 2 the token's active splits.
+__device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int tr, int hbase, int hv, int nact, int tid,
+                                             float* scratch) {
   __shared__ uint32_t bcast;
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this thread's partial stores are complete
   __syncthreads();
@@ -508,10 +519,10 @@ __device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int nac
   for (int k = 0; k < 8; ++k) {
     if (!((todo >> k) & 1u)) continue;
     if ((k & 1) == 0 && ((todo >> (k + 1)) & 1u)) {
-      merge_part<2>(a, t, nact, k, tid, scratch);         // both column halves of a head quarter
+      merge_part<2>(a, t, tr, hbase, hv, nact, k, tid, scratch);   // both column halves of a head quarter
       ++k;
     } else {
-      merge_part<1>(a, t, nact, k, tid, scratch);
+      merge_part<1>(a, t, tr, hbase, hv, nact, k, tid, scratch);
     }
   }
   if (tid == 0) {
@@ -550,7 +561,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   __shared__ int wcnt[kMaxSplitRows / kS1Threads][kS1Waves];   // union mode: kept entries per wave
 
   int t, s;
-  stage1_coords(blockIdx.x, a.T, a.S, t, s);
+  stage1_coords(blockIdx.x, UNION ? a.T : a.T * a.hblocks, a.S, t, s);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform, kept in an SGPR
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -582,10 +593,16 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int wgpg = umode ? a.union_G / mpw : 1;
   const int grp = umode ? t / wgpg : t;
   const int m0 = umode ? (t % wgpg) * mpw : 0;
-  auto tok_of = [&](int hh) { return umode ? grp * a.union_G + m0 + hh / uH : t; };
-  auto head_of = [&](int hh) { return umode ? hh % uH : hh; };
+  // decode: t is a virtual token, tr its token, hbk its block of 64 heads, hv the block's
+  // real heads
+  const int tr = umode ? t : t % a.T;
+  const int hbk = umode ? 0 : t / a.T;
+  const int hv = umode ? kHeads : min(kHeads, a.H - kHeads * hbk);
+  auto tok_of = [&](int hh) { return umode ? grp * a.union_G + m0 + hh / uH : tr; };
+  auto head_of = [&](int hh) { return umode ? hh % uH : kHeads * hbk + min(hh, hv - 1); };
+  auto writes = [&](int hh) { return umode ? tok_of(hh) < a.T : hh < hv; };   // head slot hh has an output
   if (umode && tok_of(0) >= a.T) return;               // a short last group's missing members
-  const int trow_id = grp;                             // the table row (union mode: the group's)
+  const int trow_id = umode ? grp : tr;                // the table row (union mode: the group's)
   const int len_raw = a.lens[trow_id];
   const int req_raw = a.map_req[trow_id];
   const int len = len_raw < 0 ? 0 : (len_raw > a.max_len ? a.max_len : len_raw);
@@ -640,11 +657,11 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     if ((a.sync != nullptr || umode) && len == 0 && s == 0) {
       // a token with no rows: zero output and lse -inf (stage 2 would write them otherwise)
       for (int i = tid; i < kHeads * kLatent; i += kS1Threads) {
-        const int hh = i >> 9, tk = tok_of(hh);
-        if (tk < a.T)
-          ((uint16_t*)a.out)[(int64_t)tk * a.out_tok_stride + (int64_t)head_of(hh) * a.out_head_stride + (i & 511)] = 0;
+        const int hh = i >> 9;
+        if (writes(hh))
+          ((uint16_t*)a.out)[(int64_t)tok_of(hh) * a.out_tok_stride + (int64_t)head_of(hh) * a.out_head_stride + (i & 511)] = 0;
       }
-      if (a.lse && tid < kHeads && tok_of(tid) < a.T)
+      if (a.lse && tid < kHeads && writes(tid))
         a.lse[(int64_t)tok_of(tid) * a.lse_tok_stride + head_of(tid)] = -INFINITY;
     }
     return;
@@ -1017,21 +1034,21 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   if (umode || len <= a.rows_per_split) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int hh = h0 + 4 * g + v, tk = tok_of(hh);
-      if (tk >= a.T) continue;
-      uint16_t* ob = (uint16_t*)a.out + (int64_t)tk * a.out_tok_stride + (int64_t)head_of(hh) * a.out_head_stride +
+      const int hh = h0 + 4 * g + v;
+      if (!writes(hh)) continue;
+      uint16_t* ob = (uint16_t*)a.out + (int64_t)tok_of(hh) * a.out_tok_stride + (int64_t)head_of(hh) * a.out_head_stride +
                      256 * x + c;
 #pragma unroll
       for (int nt = 0; nt < 16; ++nt) ob[16 * nt] = (uint16_t)f32_to_bf16_rne(oacc[nt][v] * inv[v]);
     }
-    if (a.lse && x == 0 && g == 0 && tok_of(h0 + c) < a.T)
+    if (a.lse && x == 0 && g == 0 && writes(h0 + c))
       a.lse[(int64_t)tok_of(h0 + c) * a.lse_tok_stride + head_of(h0 + c)] = lse_c;
     return;
   }
   // (agent-coherent stores: workgroups of this launch may merge them)
   const int64_t part = (int64_t)t * a.S + s;
   if (x == 0 && g == 0)
-    __hip_atomic_store((uint32_t*)a.part_lse + part * a.H + h0 + c, __float_as_uint(lse_c), __ATOMIC_RELAXED,
+    __hip_atomic_store((uint32_t*)a.part_lse + part * kHeads + h0 + c, __float_as_uint(lse_c), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   // bf16 partials in the accumulators' own order, so that one store instruction writes 512
   // contiguous bytes: lane (g, c) of wave (hq, x) stores heads h0 + 4g .. +3 of column
@@ -1045,7 +1062,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   }
   // (the LDS ring is idle from here on: its first slot holds the merge's LSE staging)
   if (a.sync != nullptr)
-    merge_splits(a, t, min(a.S, (len + a.rows_per_split - 1) / a.rows_per_split), tid, (float*)kvbuf[0]);
+    merge_splits(a, t, tr, kHeads * hbk, hv, min(a.S, (len + a.rows_per_split - 1) / a.rows_per_split), tid,
+                 (float*)kvbuf[0]);
 }
 
 
@@ -1126,6 +1144,7 @@ struct Stage2Args {
   float* lse;
   int64_t lse_tok_stride;
   int32_t out_f32;
+  int32_t hblocks;          // packed path: 64-head blocks per token, as in stage 1
 };
 
 // Thread = (token, head, 4 consecutive columns); a workgroup of 256 covers two heads. Every
@@ -1202,8 +1221,9 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2(Stage2Args a) {
 __global__ void __launch_bounds__(kS2Threads) decode_stage2_packed(Stage2Args a) {
   constexpr int kThreadsPerToken = 16 * 128;           // head quads x column quads
   constexpr int kBlocksPerToken = kThreadsPerToken / kS2Threads;
+  const int Tv = a.T * a.hblocks;                      // virtual tokens, as in stage 1
   int t, bi;
-  if ((a.T & 7) == 0) {
+  if ((Tv & 7) == 0) {
     const int i = blockIdx.x >> 3;
     t = (blockIdx.x & 7) + 8 * (i / kBlocksPerToken);
     bi = i % kBlocksPerToken;
@@ -1217,7 +1237,8 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2_packed(Stage2Args a)
   const int hq = q >> 2, g = q & 3;
   const int col0 = 256 * x + 16 * nt + 4 * cq;
   const int hbase = 4 * q;
-  int len = a.lens[t];
+  const int tr = t % a.T, hbk = t / a.T, hv = min(kHeads, a.H - kHeads * hbk);
+  int len = a.lens[tr];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
   if (len > 0 && len <= a.rows_per_split) return;      // one split: stage 1 wrote the output
   const int nact = min(a.S, (len + a.rows_per_split - 1) / a.rows_per_split);
@@ -1239,7 +1260,7 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2_packed(Stage2Args a)
     for (int jj = 0; jj < kS2Batch; ++jj) {
       const bool in = s0 + jj < nact;
       const int64_t ps = base + s0 + (in ? jj : 0);
-      l[jj] = in ? *(const float4*)(a.part_lse + ps * a.H + hbase)
+      l[jj] = in ? *(const float4*)(a.part_lse + ps * kHeads + hbase)
                  : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
       const uint4* src = (const uint4*)(po + ps * (kHeads * kLatent) + off);
       o[jj][0] = in ? src[0] : make_uint4(0, 0, 0, 0);
@@ -1272,12 +1293,13 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2_packed(Stage2Args a)
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int h = hbase + v;
+    if (hbase + v >= hv) continue;                     // a head slot past the block's heads
+    const int h = kHeads * hbk + hbase + v;
     const float inv = wsum[v] > 0.f ? 1.0f / wsum[v] : 0.f;
-    uint16_t* o = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)h * a.out_head_stride + col0;
+    uint16_t* o = (uint16_t*)a.out + (int64_t)tr * a.out_tok_stride + (int64_t)h * a.out_head_stride + col0;
     *(uint2*)o = make_uint2(pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv), pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv));
     if (a.lse && nt == 0 && x == 0 && cq == 0)
-      a.lse[(int64_t)t * a.lse_tok_stride + h] = wsum[v] > 0.f ? mx[v] + logf(wsum[v]) : -INFINITY;
+      a.lse[(int64_t)tr * a.lse_tok_stride + h] = wsum[v] > 0.f ? mx[v] + logf(wsum[v]) : -INFINITY;
   }
 }
 
@@ -1309,6 +1331,7 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   a.sync = plan.fused ? (uint32_t*)ws : nullptr;
   a.wait_ticks = plan.wait_ticks;
   a.union_G = 0;
+  a.hblocks = plan.hblocks;
   a.out = d.out;
   a.out_tok_stride = d.out_tok_stride;
   a.out_head_stride = d.out_head_stride;
@@ -1337,9 +1360,11 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
     dim3 grid(plan.S * d.T, (d.H + 15) / 16);
     hipLaunchKernelGGL(decode_stage1_f32, grid, dim3(kThreads), 0, stream, a);
   } else if (d.kv.dtype == SMLA_BF16) {
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, false>), dim3(plan.S * d.T), dim3(kS1Threads), 0, stream, a);
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, false>), dim3(plan.S * d.T * plan.hblocks), dim3(kS1Threads), 0,
+                       stream, a);
   } else {
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, false>), dim3(plan.S * d.T), dim3(kS1Threads), 0, stream, a);
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, false>), dim3(plan.S * d.T * plan.hblocks), dim3(kS1Threads),
+                       0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(stages & 2) || plan.fused) return e;   // fused: stage 1 has merged
@@ -1359,10 +1384,12 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   b.lse = d.lse;
   b.lse_tok_stride = d.lse_tok_stride;
   b.out_f32 = d.q_dtype == SMLA_F32;
+  b.hblocks = plan.hblocks;
   if (d.q_dtype == SMLA_F32)
     hipLaunchKernelGGL(decode_stage2, dim3(d.T * ((d.H + 1) / 2)), dim3(kS2Threads), 0, stream, b);
   else
-    hipLaunchKernelGGL(decode_stage2_packed, dim3(d.T * (16 * 128 / kS2Threads)), dim3(kS2Threads), 0, stream, b);
+    hipLaunchKernelGGL(decode_stage2_packed, dim3(d.T * plan.hblocks * (16 * 128 / kS2Threads)), dim3(kS2Threads), 0,
+                       stream, b);
   return hipGetLastError();
 }
 
@@ -1396,6 +1423,7 @@ hipError_t launch_union_decode(const smla_prefill_args& d, hipStream_t stream) {
   a.sync = nullptr;
   a.wait_ticks = 0;
   a.union_G = d.G;
+  a.hblocks = 1;
   // 64 / H queries per workgroup, G * H / 64 workgroups per group
   const dim3 grid((unsigned)(((d.Q + d.G - 1) / d.G) * (d.G * d.H / kHeads)));
   if (d.kv.dtype == SMLA_BF16)

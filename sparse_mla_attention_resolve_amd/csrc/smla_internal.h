@@ -26,6 +26,7 @@ constexpr int32_t kSyncTokens = (int32_t)(kSyncBytes / (4 * kSyncStride));
 // Decode plan: everything the launches need, computed from scalar arguments only.
 struct DecodePlan {
   int32_t T, H, S;           // tokens, heads, splits
+  int32_t hblocks;           // bf16 q: blocks of 64 head slots per token (1 or 2); fp32 q: 1
   int32_t rows_per_split;    // multiple of kChunk
   int32_t max_len;           // table_width * page_size
   size_t part_o_bytes;       // [T, S, H, 512]: bf16 (packed order) on the bf16 path, fp32 on the fp32 path

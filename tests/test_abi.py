@@ -97,7 +97,14 @@ def test_decode_checks_and_workspace():
     f32 = _decode_args(q_dtype=S.SMLA_F32, H=16, kv_dtype=S.SMLA_F32, kv_row_stride=2304)
     assert S.lib().smla_sparse_decode_splits(ctypes.byref(f32), ctypes.byref(splits)) == OK
     assert _ws(f32)[1] >= 4 * splits.value * 16 * 512 * 4 + 4 * splits.value * 16 * 4   # fp32 partials
-    assert _ws(_decode_args(H=32))[0] == UNSUP
+    # bf16 q: any 1 <= H <= 128; up to 64 heads a token is one block of 64 head slots, beyond
+    # that two, each with its own splits and partials
+    assert _ws(_decode_args(H=32))[0] == OK and _ws(_decode_args(H=16))[0] == OK
+    assert _ws(_decode_args(H=0))[0] == UNSUP and _ws(_decode_args(H=129))[0] == UNSUP
+    h128 = _decode_args(H=128, q_tok_stride=128 * 576, out_tok_stride=128 * 512, lse_tok_stride=128)
+    assert S.lib().smla_sparse_decode_splits(ctypes.byref(h128), ctypes.byref(splits)) == OK
+    assert _ws(h128)[1] >= 8 * splits.value * 64 * 512 * 2 + 8 * splits.value * 64 * 4   # 2 blocks x 4 tokens
+    assert _ws(_decode_args(H=128, lse_tok_stride=64))[0] == SHAPE                     # lse row shorter than H
     assert _ws(_decode_args(q_dtype=S.SMLA_F32))[0] == UNSUP          # fp32 q with a bf16 cache
     assert _ws(_decode_args(q_dtype=S.SMLA_F32, H=16, kv_dtype=S.SMLA_F32, kv_row_stride=2304))[0] == OK
     assert _ws(_decode_args(page_size=3))[0] == UNSUP
