@@ -120,6 +120,58 @@ def setup_decode(c, smla, torch):
     return st
 
 
+GRAPH_STEPS = 8
+
+
+def split_sweep(smla, torch, flush, steps, dtypes=("bf16", "fp8"), batches=(1, 2, 4, 8, 16, 32, 64, 128),
+                width=2048):
+    """Cold step time of the decode against the split count, per batch size and cache dtype, at
+    top-k `width` over a 2^20-slot pool of random rows (64 heads; the values do not change the
+    work). Prints one line per (dtype, T) and returns the table."""
+    n = 1 << 20
+    res = {}
+    for dt in dtypes:
+        code = {"bf16": smla.SMLA_BF16, "fp8": smla.SMLA_FP8_E4M3}[dt]
+        kv = smla.KvCache.empty(code, n, device="cuda", poison=False)
+        if dt == "bf16":
+            kv.storage.normal_(0.0, 0.5)
+        else:
+            kv.storage.copy_(torch.randint(0, 0x7E, kv.storage.shape, dtype=torch.uint8, device="cuda"))
+            kv.rope16().copy_((torch.randn(n, 64, device="cuda") * 0.5).to(torch.bfloat16).view(torch.int16))
+            kv.scale().fill_(0.01)
+        for T in batches:
+            g = torch.Generator(device="cuda").manual_seed(1000 + T)
+            q = (torch.randn(T, 64, 576, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+            table = torch.randint(0, n, (T, width), dtype=torch.int32, device="cuda", generator=g)
+            lens = torch.full((T,), width, dtype=torch.int32, device="cuda")
+            out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty((T, 64), dtype=torch.float32, device="cuda")
+            auto = smla.DecodeCall(q, kv, table, lens, 1, 1 / 16, out, lse).splits
+            row = {}
+            for S in sorted({1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, auto}):
+                if S < (width + 1023) // 1024 or S > width // 32:
+                    continue
+                call = smla.DecodeCall(q, kv, table, lens, 1, 1 / 16, out, lse, num_splits=S)
+                for _ in range(3):
+                    flush.sum()
+                    call()
+                ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+                for k in range(steps):
+                    flush.sum()
+                    ev[k][0].record()
+                    call()
+                    ev[k][1].record()
+                torch.cuda.synchronize()
+                row[call.splits] = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+            best = min(row, key=row.get)
+            res[(dt, T)] = {"auto": auto, "best": best, "us": row}
+            log(f"split sweep {dt} T={T}: auto S={auto} {row[auto]:.1f} us, best S={best} {row[best]:.1f} us; " +
+                " ".join(f"{k}:{v:.1f}" for k, v in sorted(row.items())))
+        del kv
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_decode(c, smla, torch, steps, warmup, flush):
     """Cold steps (a 1 GiB read before each) of the fused step, which is one kernel: stage 1
     resolving the logical indices itself and merging the splits at its end. The same for the
@@ -183,7 +235,8 @@ def time_decode(c, smla, torch, steps, warmup, flush):
     torch.cuda.synchronize()
     warm_ms = e0.elapsed_time(e1) / steps
 
-    # the same step captured in a HIP graph and replayed (warm)
+    # GRAPH_STEPS steps back to back captured in one HIP graph and replayed (warm): a layer
+    # loop's launches without the host in between; the figure is per step
     graph_ms = None
     try:
         s = torch.cuda.Stream()
@@ -193,7 +246,8 @@ def time_decode(c, smla, torch, steps, warmup, flush):
         torch.cuda.current_stream().wait_stream(s)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step()
+            for _ in range(GRAPH_STEPS):
+                step()
         g.replay()
         torch.cuda.synchronize()
         e0.record()
@@ -201,7 +255,7 @@ def time_decode(c, smla, torch, steps, warmup, flush):
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        graph_ms = e0.elapsed_time(e1) / steps
+        graph_ms = e0.elapsed_time(e1) / (steps * GRAPH_STEPS)
     except Exception as ex:  # graph capture is a report-only extra
         log(f"graph capture skipped: {ex}")
     return {"step_ms": step_ms, "two_kernel": two, "warm_ms": warm_ms, "graph_ms": graph_ms, "wall_s": wall,
@@ -409,6 +463,9 @@ def main():
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-kv-write", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="only time the decode against its split count for batches 1 .. 128 (bf16 and fp8, "
+                         "top-k 2048) and print the table; no JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three plain 256 MiB fp32 copy kernels (y = x * 1), whose HBM counter "
                          "readings give the scale for the decode kernels' FETCH_SIZE / WRITE_SIZE")
@@ -426,6 +483,9 @@ def main():
         raise SystemExit("libsmla.so is not built: run python -m sparse_mla_attention_resolve_amd.build")
     torch.cuda.set_device(0)
     flush = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device="cuda")
+    if args.split_sweep:
+        split_sweep(smla, torch, flush, max(5, args.steps // 2))
+        return
 
     log("generating the bf16 decode workload (batch 32, top-k 2048)")
     c2 = wl.decode_bf16_b32()
@@ -461,6 +521,7 @@ def main():
                       "step_p90": float(np.percentile(r["step_ms"], 90)) * 1e3,
                       "warm_step": r["warm_ms"] * 1e3,
                       "graph_replay_step": None if r["graph_ms"] is None else r["graph_ms"] * 1e3,
+                      "graph_steps_per_replay": GRAPH_STEPS,
                       "two_kernel_form": {"step": us(two["step_ms"]), "resolve": us(two["resolve_ms"]),
                                           "decode": us(two["decode_ms"])}},
         "roofline": {"bound": "hbm", "kernel": "decode_stage1_mfma<bf16>", "achieved": step_gbs,

@@ -104,7 +104,12 @@ int32_t wall_ticks(int32_t us) {
 // count. A stage-1 workgroup fills a compute unit (its LDS ring), so the default gives
 // every compute unit one (token, split) and no second round: floor(CUs / T) splits per
 // token, at least enough for the per-split row limit.
-void plan_splits(int32_t T, int32_t max_len, int32_t requested, int32_t* S_out, int32_t* R_out) {
+// Splits per token when the caller leaves it open: one workgroup per compute unit (CUs / T),
+// but no split shorter than min_rows, and none longer than kMaxSplitRows. The floor comes from
+// a sweep of split counts for batches 1 .. 128 at top-k 2048: below 128 rows (bf16 cache) or
+// 64 rows (fp8 cache) a split's fixed cost (first gathers, partial store, merge) outweighs
+// the compute units it adds; at batch 1 the floor takes the step from 28.6 to 23.2 us (bf16).
+void plan_splits(int32_t T, int32_t max_len, int32_t requested, int32_t min_rows, int32_t* S_out, int32_t* R_out) {
   const int32_t chunk = smla::kChunk;
   const int32_t max_chunks = (max_len + chunk - 1) / chunk;
   int32_t S;
@@ -113,6 +118,8 @@ void plan_splits(int32_t T, int32_t max_len, int32_t requested, int32_t* S_out, 
   } else {
     const int32_t Tq = T > 0 ? T : 1;
     S = device_cus() / Tq;
+    const int32_t cap = (max_len + min_rows - 1) / min_rows;
+    if (S > cap) S = cap;
     const int32_t need = (max_len + smla::kMaxSplitRows - 1) / smla::kMaxSplitRows;
     if (S < need) S = need;
   }
@@ -182,7 +189,8 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   const int64_t tv = (int64_t)a->T * plan->hblocks;
   CHECK(tv <= (1 << 24), SMLA_ERR_RANGE, "%s: T * ceil(H / 64) must be <= 2^24", fn);
   const int64_t hslots = bf16 ? 64 : a->H;
-  plan_splits((int32_t)tv, (int32_t)max_len, a->num_splits, &plan->S, &plan->rows_per_split);
+  const int32_t min_rows = !bf16 ? smla::kChunk : a->kv.dtype == SMLA_FP8_E4M3 ? 64 : 128;
+  plan_splits((int32_t)tv, (int32_t)max_len, a->num_splits, min_rows, &plan->S, &plan->rows_per_split);
   // the bf16 path keeps its partial outputs in bf16, the fp32 path in fp32
   plan->part_o_bytes = (size_t)tv * plan->S * hslots * SMLA_LATENT * (bf16 ? 2 : 4);
   plan->part_lse_bytes = (size_t)tv * plan->S * hslots * sizeof(float);
