@@ -172,6 +172,65 @@ def split_sweep(smla, torch, flush, steps, dtypes=("bf16", "fp8"), batches=(1, 2
     return res
 
 
+def overlap_sweep(smla, torch, flush, steps, Q=4096, W=2048, ns=24576,
+                  overlaps=(0.0, 0.25, 0.5, 0.7, 0.9, 1.0), groups=(2, 4, 8)):
+    """Grouped prefill (union build + grouped attention, G queries of H = 128 / G heads per
+    group) against every query attending its own list alone (the decode kernel over the lists,
+    page size 1), for lists of W slots of which a fraction `overlap` is shared by the group's
+    members (the rest disjoint). bf16 cache of ns random rows. Prints a line per (G, overlap)."""
+    kv = smla.KvCache.empty(smla.SMLA_BF16, ns, device="cuda", poison=False)
+    kv.storage.normal_(0.0, 0.5)
+    res = {}
+    for G in groups:
+        H = 128 // G
+        ng = (Q + G - 1) // G
+        g = torch.Generator(device="cuda").manual_seed(77 + G)
+        q = (torch.randn(Q, H, 576, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+        out = torch.empty((Q, H, 512), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((Q, H), dtype=torch.float32, device="cuda")
+        valid = torch.full((Q,), W, dtype=torch.int32, device="cuda")
+        for ov in overlaps:
+            n_sh = int(round(ov * W))
+            own = W - n_sh
+            # per group one permutation of the pool: its first n_sh entries are shared, then each
+            # member's own entries follow, disjoint from the shared ones and from each other's
+            perm = torch.rand(ng, ns, device="cuda", generator=g).argsort(dim=1).to(torch.int32)
+            m = torch.arange(Q, device="cuda") % G
+            rows = perm[torch.arange(Q, device="cuda") // G]
+            cols = torch.cat([torch.arange(n_sh, device="cuda").expand(Q, n_sh),
+                              n_sh + m[:, None] * own + torch.arange(own, device="cuda")[None, :]], dim=1)
+            lists = torch.gather(rows, 1, cols)
+            lists = torch.gather(lists, 1, torch.rand(Q, W, device="cuda", generator=g).argsort(dim=1)).contiguous()
+            del perm, rows
+            enc, lens = smla.smla_build_group_union(lists, valid, G, ns)
+            dec = smla.DecodeCall(q, kv, lists, valid, 1, 1 / 16, out, lse)
+
+            def grouped():
+                smla.smla_build_group_union(lists, valid, G, ns, enc=enc, lens=lens)
+                smla.smla_grouped_prefill(q, kv, enc, lens, G, 1 / 16, out=out, lse=lse)
+
+            def timed(fn):
+                for _ in range(2):
+                    flush.sum()
+                    fn()
+                ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+                for k in range(steps):
+                    flush.sum()
+                    ev[k][0].record()
+                    fn()
+                    ev[k][1].record()
+                torch.cuda.synchronize()
+                return float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+
+            tg, td = timed(grouped), timed(dec)
+            ratio = float(lens.float().mean()) / W
+            res[(G, ov)] = {"grouped_us": tg, "alone_us": td, "union_per_list": ratio}
+            log(f"overlap sweep G={G} H={H} overlap {ov:.2f}: union {ratio:.2f} x W per group, grouped {tg:.0f} us, "
+                f"each query alone {td:.0f} us, speedup {td / tg:.2f}x")
+            del lists, enc, lens, dec
+    return res
+
+
 def time_decode(c, smla, torch, steps, warmup, flush):
     """Cold steps (a 1 GiB read before each) of the fused step, which is one kernel: stage 1
     resolving the logical indices itself and merging the splits at its end. The same for the
@@ -463,6 +522,9 @@ def main():
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-kv-write", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--overlap-sweep", action="store_true",
+                    help="only time grouped prefill against per-query decode for G = 2 / 4 / 8 over list "
+                         "overlaps 0 .. 1 and print the table; no JSON line")
     ap.add_argument("--split-sweep", action="store_true",
                     help="only time the decode against its split count for batches 1 .. 128 (bf16 and fp8, "
                          "top-k 2048) and print the table; no JSON line")
@@ -485,6 +547,9 @@ def main():
     flush = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device="cuda")
     if args.split_sweep:
         split_sweep(smla, torch, flush, max(5, args.steps // 2))
+        return
+    if args.overlap_sweep:
+        overlap_sweep(smla, torch, flush, max(3, args.steps // 10))
         return
 
     log("generating the bf16 decode workload (batch 32, top-k 2048)")
