@@ -449,12 +449,14 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int tr, i
         const float lw = ((const float*)&l[jj])[v];
         const float wgt = lw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lw - bm);
         ws[v] += wgt;
-        // entry 2i: words x, y = heads (0, 1), (2, 3) at col; entry 2i + 1: z, w at col + 1
+        // entry 2i: words x, y = heads (0, 1), (2, 3) at col; entry 2i + 1: z, w at col + 1.
+        // Explicit fused multiply-adds: a part merged alone (NP = 1) or with its neighbour
+        // (NP = 2) must round the same, since which of the two runs depends on arrival order
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
           const uint32_t w0 = v < 2 ? o[n][jj].x : o[n][jj].y, w1 = v < 2 ? o[n][jj].z : o[n][jj].w;
-          acc[n][v][0] += wgt * bf16_to_f32((v & 1) ? (w0 >> 16) : (w0 & 0xffffu));
-          acc[n][v][1] += wgt * bf16_to_f32((v & 1) ? (w1 >> 16) : (w1 & 0xffffu));
+          acc[n][v][0] = __builtin_fmaf(wgt, bf16_to_f32((v & 1) ? (w0 >> 16) : (w0 & 0xffffu)), acc[n][v][0]);
+          acc[n][v][1] = __builtin_fmaf(wgt, bf16_to_f32((v & 1) ? (w1 >> 16) : (w1 & 0xffffu)), acc[n][v][1]);
         }
       }
       mx[v] = bm;

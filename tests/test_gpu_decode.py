@@ -348,3 +348,20 @@ def test_merge_in_stage2_past_counter_region():
     sample = [0, 1, 2047, 4095, 4096]
     o_ref, l_ref = oracle.sparse_decode(q[sample], "bf16", pool, table[sample], lens[sample], 1, 1 / 16)
     _check(out[sample], lse[sample], o_ref, l_ref, BF16_ATOL, BF16_RTOL, "stage-2 merge")
+
+
+def test_merge_bits_independent_of_arrival_order():
+    """With more workgroups than compute units the merge parts fall to whichever workgroups
+    arrive when, one part at a time or a head quarter's two halves together: the bits must
+    not depend on it. Five repeats of a 32-token, 16-split decode (512 workgroups) agree."""
+    rng = np.random.default_rng(26)
+    lens = rng.integers(200, 2049, 32)
+    q, table, lens, live, vals = _random_case(26, 32, 2048, lens, 60000)
+    kv, pool = _pools(live, vals, 60000, "bf16")
+    qt = gc.q_tensor(q, "bf16")
+    runs = [smla.smla_sparse_decode(qt, kv, _t(table), _t(lens), 1, 0.1, num_splits=16) for _ in range(5)]
+    for o, l in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(l, runs[0][1])
+    sample = [0, 17, 31]
+    o_ref, l_ref = oracle.sparse_decode(q[sample], "bf16", pool, table[sample], lens[sample], 1, 0.1)
+    _check(runs[0][0][sample], runs[0][1][sample], o_ref, l_ref, BF16_ATOL, BF16_RTOL, "arrival-order merge")
