@@ -118,3 +118,47 @@ def test_random_decode_shape(seed):
     o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, oslots, valid, 1, scale)
     gc.assert_close(b[0].float().cpu().numpy(), o_ref, atol, RTOL, what + " top-k out")
     gc.assert_lse(b[1].cpu().numpy(), l_ref, LSE_ATOL, what + " top-k lse")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill_shape(seed):
+    """Union build + grouped prefill on random shapes: G in {2, 4, 8} (H = 128 / G), a query
+    count that may leave the last group short, list widths, empty and partial lists, list
+    overlap, pools below and above the union row-map limit, and every cache format."""
+    rng = np.random.default_rng(2000 + seed)
+    G = int(rng.choice([2, 4, 8]))
+    H = 128 // G
+    Q = int(rng.integers(1, 4 * G + 1))
+    W = int(rng.choice([32, 300, 1024, 2048]))
+    ns = int(rng.choice([3000, 40000, 200000]))
+    kv_dtype = str(rng.choice(["bf16", "fp8", "fp8-planes"]))
+    fmt = "fp8" if kv_dtype.startswith("fp8") else "bf16"
+    overlap = float(rng.choice([0.0, 0.5, 0.9]))
+    slots, valid = wl.random_slot_lists(3000 + seed, Q, W, ns, overlap=overlap, G=G, pad_frac=0.3)
+    if Q > 1:
+        valid[rng.integers(0, Q)] = 0
+    live = np.unique(slots[slots >= 0]).astype(np.int32)
+    vals = rng.standard_normal((len(live), 576)).astype(np.float32) * (1.0 if fmt == "fp8" else 0.5)
+    kv = smla.KvCache.empty(gc.KV_CODE[fmt], ns)
+    src = vals if fmt == "fp8" else wl.f32_to_bf16_bits(vals)
+    st, sd = gc.src_tensor(src)
+    smla.smla_kv_write(st, _t(live), kv)
+    pool = oracle.Pool(ns, fmt)
+    oracle.kv_write(pool, src, sd, live)
+    if kv_dtype == "fp8-planes":
+        kv = PlanarKv(kv)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((Q, H, 576)).astype(np.float32) * 0.5)
+    scale = float(rng.choice([1 / 16, 0.1]))
+    what = f"seed {seed}: G={G} Q={Q} W={W} ns={ns} {kv_dtype} overlap={overlap}"
+    enc, lens = smla.smla_build_group_union(_t(slots), _t(valid), G, ns)
+    enc_o, lens_o = oracle.group_union(slots, valid, G, ns)
+    lens_g = lens.cpu().numpy()
+    assert np.array_equal(lens_g, lens_o), what
+    enc_g = enc.cpu().numpy().view(np.uint32)
+    for g in range(len(lens_o)):
+        assert np.array_equal(enc_g[g, :lens_o[g]], enc_o[g, :lens_o[g]].view(np.uint32)), what + f" group {g}"
+    out, lse = smla.smla_grouped_prefill(gc.q_tensor(q, "bf16"), kv, enc, lens, G, scale)
+    o_ref, l_ref = oracle.grouped_prefill(q, pool, enc_o, lens_o, G, scale)
+    atol = FP8_ATOL if fmt == "fp8" else BF16_ATOL
+    gc.assert_close(out.float().cpu().numpy(), o_ref, atol, RTOL, what + " out")
+    gc.assert_lse(lse.cpu().numpy(), l_ref, LSE_ATOL, what + " lse")
