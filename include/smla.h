@@ -186,7 +186,11 @@ smla_status smla_sparse_decode_workspace(const smla_decode_args* args, size_t* b
  * SMLA_ERR_ALIGN (not 256-byte aligned), SMLA_ERR_DEVICE (launch failure). */
 smla_status smla_sparse_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
-/* Number of splits smla_sparse_decode uses for these arguments. */
+/* Number of splits smla_sparse_decode uses for these arguments. Exception: a dense paged
+ * decode (page_size > 1) of at most 64 tokens (64 blocks of heads) with num_splits 0 on the
+ * bf16 path sizes each token's splits on the device from the actual lengths (rows per split
+ * from the launch's total, so that the splits of short and long contexts share the compute
+ * units evenly); the count reported is then the one a uniform plan would use. */
 smla_status smla_sparse_decode_splits(const smla_decode_args* args, int32_t* num_splits);
 
 /* Enqueue the decode. `workspace` (256-byte aligned) must hold at least the bytes

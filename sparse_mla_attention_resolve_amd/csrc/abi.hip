@@ -191,15 +191,29 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   const int64_t hslots = bf16 ? 64 : a->H;
   const int32_t min_rows = !bf16 ? smla::kChunk : a->kv.dtype == SMLA_FP8_E4M3 ? 64 : 128;
   plan_splits((int32_t)tv, (int32_t)max_len, a->num_splits, min_rows, &plan->S, &plan->rows_per_split);
+  plan->min_rows = min_rows;
+  plan->cus = device_cus();
+  // A dense paged decode (page size > 1: contexts of any length) of at most 64 tokens lets the
+  // workgroups size the splits from the actual lengths (no host copy of them), so that short
+  // and long contexts share the compute units evenly. The grid bounds the splits any lengths
+  // can produce: at most one workgroup per compute unit while the rows per split stay under
+  // the cap, else ceil(max_len / kMaxSplitRows) per token, plus one per token.
+  plan->balanced = bf16 && a->page_size > 1 && a->num_splits == 0 && tv <= 64 && tv < plan->cus;
+  int64_t items = tv * plan->S;
+  if (plan->balanced) {
+    const int64_t capped = tv * ((max_len + smla::kMaxSplitRows - 1) / smla::kMaxSplitRows) + tv;
+    items = capped > plan->cus ? capped : plan->cus;
+  }
+  plan->grid = (int32_t)items;
   // the bf16 path keeps its partial outputs in bf16, the fp32 path in fp32
-  plan->part_o_bytes = (size_t)tv * plan->S * hslots * SMLA_LATENT * (bf16 ? 2 : 4);
-  plan->part_lse_bytes = (size_t)tv * plan->S * hslots * sizeof(float);
+  plan->part_o_bytes = (size_t)items * hslots * SMLA_LATENT * (bf16 ? 2 : 4);
+  plan->part_lse_bytes = (size_t)items * hslots * sizeof(float);
   // bf16 q: the splits of a block merge at the end of stage 1 through a word per block at
   // the head of the workspace; a workgroup waits for its block's other splits (at most
   // 10 us) only when the whole grid is resident at once
   plan->sync_bytes = bf16 ? smla::kSyncBytes : 0;
   plan->fused = bf16 && tv <= smla::kSyncTokens;
-  plan->wait_ticks = tv * plan->S <= device_cus() ? wall_ticks(10) : 0;
+  plan->wait_ticks = (plan->balanced || tv * plan->S <= device_cus()) ? wall_ticks(10) : 0;
   plan->ws_bytes = plan->sync_bytes + (plan->part_o_bytes + plan->part_lse_bytes + 255) / 256 * 256;
   return SMLA_OK;
 }

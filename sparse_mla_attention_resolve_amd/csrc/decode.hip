@@ -73,6 +73,10 @@ struct Stage1Args {
   // each with 64 head slots; slots past the block's real heads read the block's last head
   // and write nothing. Partials and merge words are per virtual token.
   int32_t hblocks;
+  // dense paged decode of at most 64 (virtual) tokens, bf16 q: the workgroups plan the splits
+  // themselves from the tokens' lengths (balanced), with at least min_rows rows per split,
+  // for a device of `cus` compute units
+  int32_t balanced, min_rows, cus;
 };
 
 // Physical slot of position p of token t's table row, or -1 when masked.
@@ -386,11 +390,11 @@ __device__ __forceinline__ uint32_t parts_of(int q, int nact) {
 // O = sum_s exp(lse_s - lse) O_s with lse = log sum_s exp(lse_s).
 // NP = 2 merges parts p and p + 1 (p even: the two column halves of one head quarter, entries
 // 1024 further on, columns 256 further on) with the same LSEs and weights.
-// t is the virtual token (its partials and LSEs), tr the token and hbase + hb its output heads,
-// of which the first hv of the 64 exist.
+// pbase is the first of the token's partials (its splits' partials are consecutive), tr the
+// token and hbase + hb its output heads, of which the first hv of the 64 exist.
 template <int NP>
-__device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int tr, int hbase, int hv, int nact, int p,
-                                           int tid, float* scratch) {
+__device__ __forceinline__ void merge_part(const Stage1Args& a, int64_t pbase, int tr, int hbase, int hv, int nact,
+                                           int p, int tid, float* scratch) {
   static_assert(NP == 1 || NP == 2, "one part or a head quarter's two");
   constexpr int kBatch = 8;
   const int j = 1024 * p + 2 * tid;
@@ -399,9 +403,9 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int tr, i
   const int hb = 16 * (p >> 1) + hp;
   const int col = 256 * (p & 1) + 16 * ntp + (lanep & 15);
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((uint16_t*)a.part_o + (int64_t)t * a.S * (kHeads * kLatent)), (short)0, 0x7fffffff, kBufFlags);
+      (void*)((uint16_t*)a.part_o + pbase * (kHeads * kLatent)), (short)0, 0x7fffffff, kBufFlags);
   const __amdgpu_buffer_rsrc_t rl =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.part_lse + (int64_t)t * a.S * kHeads), (short)0, 0x7fffffff, kBufFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.part_lse + pbase * kHeads), (short)0, 0x7fffffff, kBufFlags);
   float mx[4], ws[4], acc[NP][4][2];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -477,8 +481,8 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int t, int tr, i
 
 // Called by every active split workgroup of virtual token t (token tr, heads hbase .. hbase + hv
 // - 1) once its partial is stored, with nact >= 2 the token's active splits.
-__device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int tr, int hbase, int hv, int nact, int tid,
-                                             float* scratch) {
+__device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int64_t pbase, int tr, int hbase, int hv,
+                                             int nact, int tid, float* scratch) {
   __shared__ uint32_t bcast;
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this thread's partial stores are complete
   __syncthreads();
@@ -521,10 +525,10 @@ __device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int tr,
   for (int k = 0; k < 8; ++k) {
     if (!((todo >> k) & 1u)) continue;
     if ((k & 1) == 0 && ((todo >> (k + 1)) & 1u)) {
-      merge_part<2>(a, t, tr, hbase, hv, nact, k, tid, scratch);   // both column halves of a head quarter
+      merge_part<2>(a, pbase, tr, hbase, hv, nact, k, tid, scratch);   // both column halves of a head quarter
       ++k;
     } else {
-      merge_part<1>(a, t, tr, hbase, hv, nact, k, tid, scratch);
+      merge_part<1>(a, pbase, tr, hbase, hv, nact, k, tid, scratch);
     }
   }
   if (tid == 0) {
@@ -562,8 +566,63 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   __shared__ float sx[kS1Waves][4][64];                    // score tiles swapped between partners
   __shared__ int wcnt[kMaxSplitRows / kS1Threads][kS1Waves];   // union mode: kept entries per wave
 
-  int t, s;
-  stage1_coords(blockIdx.x, UNION ? a.T : a.T * a.hblocks, a.S, t, s);
+  // t, s: the (virtual) token and split; rps rows per split, pbase the token's first partial,
+  // smax the cap on a token's splits
+  int t, s, rps = a.rows_per_split, smax = a.S;
+  int64_t pbase;
+  if (!UNION && a.balanced) {
+    // Splits planned from the lengths (a dense paged decode of at most 64 tokens, whose
+    // contexts may differ widely): rows per split from the launch's total rows, so that every
+    // token's splits fit the compute units at once (at least min_rows, at most kMaxSplitRows,
+    // whole chunks); token v gets ceil(len_v / rows) splits, at least one (which writes an
+    // empty token's output); workgroup b takes the b-th split in token order, or leaves past
+    // the last. Wave 0 plans, lane v for token v.
+    __shared__ int bplan[4];
+    const int tv = a.T * a.hblocks;
+    if (threadIdx.x < 64) {
+      const int v = threadIdx.x;
+      int ln = 0;
+      if (v < tv) {
+        const int l = a.lens[v % a.T];
+        ln = l < 0 ? 0 : (l > a.max_len ? a.max_len : l);
+      }
+      int tot = ln;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
+      const int room = a.cus - tv;                         // splits beyond one per token
+      int r = (tot + room - 1) / room;
+      r = (r + kChunk - 1) / kChunk * kChunk;
+      r = r < a.min_rows ? a.min_rows : (r > kMaxSplitRows ? kMaxSplitRows : r);
+      const int n = v < tv ? max(1, (ln + r - 1) / r) : 0;
+      int incl = n;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (v >= o) incl += y;
+      }
+      const int base = incl - n, b = blockIdx.x;
+      const bool mine = v < tv && b >= base && b < base + n;
+      const uint64_t m = __ballot(mine);
+      if (v == 0) {
+        bplan[0] = m ? __builtin_ffsll((long long)m) - 1 : -1;
+        bplan[2] = r;
+      }
+      if (mine) {
+        bplan[1] = b - base;
+        bplan[3] = base;
+      }
+    }
+    __syncthreads();
+    t = bplan[0];
+    if (t < 0) return;                                     // past the last split
+    s = bplan[1];
+    rps = bplan[2];
+    pbase = bplan[3];
+    smax = kMaxSplitRows;                                  // no cap: ceil(len / rps) splits
+  } else {
+    stage1_coords(blockIdx.x, UNION ? a.T : a.T * a.hblocks, a.S, t, s);
+    pbase = (int64_t)t * a.S;
+  }
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform, kept in an SGPR
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -584,7 +643,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   // register that a global load may still be writing would make the compiler wait for
   // every copy in flight, since it does not see them). q follows with the first chunks.
   const int lp = a.log2_page;
-  const int r0 = s * a.rows_per_split;
+  const int r0 = s * rps;
   const bool mapped = a.mapped != 0;
   constexpr bool umode = UNION;                         // a.union_G > 0
   // union mode: heads per query, queries per workgroup, workgroups per group, this
@@ -610,8 +669,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int len = len_raw < 0 ? 0 : (len_raw > a.max_len ? a.max_len : len_raw);
   const int32_t* trow = a.table + (int64_t)trow_id * a.table_stride;
   const int e0 = r0 >> lp;
-  const int n_ent = lp == 0 ? min(a.rows_per_split, a.max_len - r0)
-                            : min((r0 + a.rows_per_split - 1) >> lp, a.table_width - 1) - e0 + 1;
+  const int n_ent = lp == 0 ? min(rps, a.max_len - r0) : min((r0 + rps - 1) >> lp, a.table_width - 1) - e0 + 1;
   static_assert((kNBuf - 2) * kChunkBytes >= 4 * kQLoads * 1024, "q must fit the ring slots from 2 on");
   char* const qlds = kvbuf[2] + hq * (kQLoads * 1024);
   int32_t* const prow_lds = (int32_t*)kvbuf[1];
@@ -668,7 +726,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     }
     return;
   }
-  const int r1 = min(r0 + a.rows_per_split, len);
+  const int r1 = min(r0 + rps, len);
   lds_barrier();
 
   bf16x8 qf[kQLoads];                           // decode: loaded with the first chunks
@@ -1033,7 +1091,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   float inv[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) inv[v] = __shfl(inv_c, 4 * g + v, 64);
-  if (umode || len <= a.rows_per_split) {
+  if (umode || len <= rps) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int hh = h0 + 4 * g + v;
@@ -1048,7 +1106,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     return;
   }
   // (agent-coherent stores: workgroups of this launch may merge them)
-  const int64_t part = (int64_t)t * a.S + s;
+  const int64_t part = pbase + s;
   if (x == 0 && g == 0)
     __hip_atomic_store((uint32_t*)a.part_lse + part * kHeads + h0 + c, __float_as_uint(lse_c), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -1064,8 +1122,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   }
   // (the LDS ring is idle from here on: its first slot holds the merge's LSE staging)
   if (a.sync != nullptr)
-    merge_splits(a, t, tr, kHeads * hbk, hv, min(a.S, (len + a.rows_per_split - 1) / a.rows_per_split), tid,
-                 (float*)kvbuf[0]);
+    merge_splits(a, t, pbase, tr, kHeads * hbk, hv, min(smax, (len + rps - 1) / rps), tid, (float*)kvbuf[0]);
 }
 
 
@@ -1334,6 +1391,9 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   a.wait_ticks = plan.wait_ticks;
   a.union_G = 0;
   a.hblocks = plan.hblocks;
+  a.balanced = plan.balanced;
+  a.min_rows = plan.min_rows;
+  a.cus = plan.cus;
   a.out = d.out;
   a.out_tok_stride = d.out_tok_stride;
   a.out_head_stride = d.out_head_stride;
@@ -1362,11 +1422,9 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
     dim3 grid(plan.S * d.T, (d.H + 15) / 16);
     hipLaunchKernelGGL(decode_stage1_f32, grid, dim3(kThreads), 0, stream, a);
   } else if (d.kv.dtype == SMLA_BF16) {
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, false>), dim3(plan.S * d.T * plan.hblocks), dim3(kS1Threads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, false>), dim3(plan.grid), dim3(kS1Threads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, false>), dim3(plan.S * d.T * plan.hblocks), dim3(kS1Threads),
-                       0, stream, a);
+    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, false>), dim3(plan.grid), dim3(kS1Threads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(stages & 2) || plan.fused) return e;   // fused: stage 1 has merged
@@ -1426,6 +1484,9 @@ hipError_t launch_union_decode(const smla_prefill_args& d, hipStream_t stream) {
   a.wait_ticks = 0;
   a.union_G = d.G;
   a.hblocks = 1;
+  a.balanced = 0;
+  a.min_rows = kChunk;
+  a.cus = 0;
   // 64 / H queries per workgroup, G * H / 64 workgroups per group
   const dim3 grid((unsigned)(((d.Q + d.G - 1) / d.G) * (d.G * d.H / kHeads)));
   if (d.kv.dtype == SMLA_BF16)

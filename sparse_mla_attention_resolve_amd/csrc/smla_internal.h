@@ -27,6 +27,9 @@ constexpr int32_t kSyncTokens = (int32_t)(kSyncBytes / (4 * kSyncStride));
 struct DecodePlan {
   int32_t T, H, S;           // tokens, heads, splits
   int32_t hblocks;           // bf16 q: blocks of 64 head slots per token (1 or 2); fp32 q: 1
+  int32_t grid;              // stage-1 workgroups
+  int32_t balanced;          // the workgroups plan the splits from the lengths (dense paged, <= 64 tokens)
+  int32_t min_rows, cus;     // fewest rows per split; compute units of the device
   int32_t rows_per_split;    // multiple of kChunk
   int32_t max_len;           // table_width * page_size
   size_t part_o_bytes;       // [T, S, H, 512]: bf16 (packed order) on the bf16 path, fp32 on the fp32 path
