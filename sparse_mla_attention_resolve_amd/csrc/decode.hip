@@ -1,13 +1,14 @@
 // Split decode attention over a block table.
 //
-// Stage 1 (one workgroup per token and split) walks the split's rows in chunks of 32:
-// it gathers the chunk's 576-wide rows from the pool into LDS, computes the scores of
-// all 64 heads against them with bf16 MFMA (the heads of one token are the M dimension,
-// the rows the N dimension), keeps a running max and sum per head (online softmax), and
-// accumulates P * V with MFMA, V being the first 512 columns of the same rows. It writes
-// the split's normalised output and log-sum-exp. Stage 2 merges a token's splits by LSE
-// (IBM Triton paged-attention explainer, section 4 table: "Q-Block" for stacking the
-// heads that share a KV row, "Parallel Tiled Softmax" for the split and merge).
+// Stage 1 (one workgroup per token, block of 64 heads and split) walks the split's rows in
+// chunks of 32: it gathers the chunk's 576-wide rows from the pool into LDS, computes the
+// scores of the block's 64 heads against them with bf16 MFMA (every head of the token meets
+// each gathered row; the scores are computed transposed, rows on the M dimension and heads
+// on N), keeps a running max and sum per head (online softmax), and accumulates P * V with
+// MFMA, V being the first 512 columns of the same rows. The splits of a token are merged by
+// LSE at the end of stage 1 (bf16 q), or by stage 2 (IBM Triton paged-attention explainer,
+// section 4 table: "Q-Block" for stacking the heads that share a KV row, "Parallel Tiled
+// Softmax" for the split and merge).
 //
 // The block table is either resolved slots (page size 1, the virtual block table of
 // The Virtual Block Table: Reusing Triton MLA for Sparse Attention on Blackwell GPUs,
@@ -362,11 +363,11 @@ __device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, con
 // Word of token t (zero on entry, zero again when its last workgroup leaves):
 //   bits 0 .. 8    tickets taken (arrivals), bits 9 .. 17 departures,
 //   bits 18 .. 25  parts given up by tickets 0 .. 7.
-// The merge has 8 parts (head quarter x column half). Ticket q < 8 owns parts q, q + nact,
-// ... < 8. A ticket holder waits a bounded time for the remaining arrivals and then merges
-// its parts; when the time runs out it gives them up with one atomic add, which also tells
-// it whether the last arrival has already come (then it merges them after all). The last
-// arrival never waits: it merges its own parts and every part given up before it came.
+// The merge has 8 parts (head quarter x column half), owned by tickets 0 .. 7 (parts_of).
+// A ticket holder waits a bounded time for the remaining arrivals and then merges its parts;
+// when the time runs out it gives them up with one atomic add, which also tells it whether
+// the last arrival has already come (then it merges them after all). The last arrival never
+// waits: it merges its own parts and every part given up before it came.
 constexpr uint32_t kArrMask = 0x1ff;
 constexpr int kExitShift = 9, kGiveUpShift = 18;
 constexpr int kBufFlags = 0x00020000;       // buffer descriptor word 3: 32-bit data format
