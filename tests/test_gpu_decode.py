@@ -365,3 +365,43 @@ def test_merge_bits_independent_of_arrival_order():
     sample = [0, 17, 31]
     o_ref, l_ref = oracle.sparse_decode(q[sample], "bf16", pool, table[sample], lens[sample], 1, 0.1)
     _check(runs[0][0][sample], runs[0][1][sample], o_ref, l_ref, BF16_ATOL, BF16_RTOL, "arrival-order merge")
+
+
+def _dense_case(seed, ctx, P, pool_extra=16):
+    """Requests with contexts `ctx`, each with its own pages (dealt from a permutation), the
+    slots of the pages a context covers written; q for 64 heads."""
+    rng = np.random.default_rng(seed)
+    T = len(ctx)
+    ptw = max(1, -(-int(max(ctx)) // P))
+    num_pages = T * ptw + pool_extra
+    pt = rng.permutation(num_pages)[:T * ptw].reshape(T, ptw).astype(np.int32)
+    used = np.concatenate([pt[t, :-(-int(c) // P)] for t, c in enumerate(ctx)] + [np.zeros(0, np.int32)])
+    live = np.unique((used[:, None] * P + np.arange(P)[None, :]).reshape(-1)).astype(np.int32)
+    vals = rng.standard_normal((len(live), 576)).astype(np.float32) * 0.5
+    kv, pool = _pools(live, vals, num_pages * P, "bf16")
+    q = wl.f32_to_bf16_bits(rng.standard_normal((T, 64, 576)).astype(np.float32) * 0.5)
+    return q, pt, np.asarray(ctx, np.int32), kv, pool
+
+
+@pytest.mark.parametrize("T", [64, 65])
+def test_dense_paged_planned_splits(T):
+    """Dense paged decode with contexts from 0 to 32K: up to 64 tokens plan their splits on
+    the device from the lengths, 65 use the uniform plan; sampled tokens against the oracle."""
+    rng = np.random.default_rng(27 + T)
+    ctx = rng.integers(0, 8193, T)
+    ctx[0], ctx[1], ctx[2] = 0, 32768, 1
+    q, pt, ctx, kv, pool = _dense_case(27 + T, ctx, 64)
+    out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(pt), _t(ctx), 64, 1 / 16)
+    sample = [0, 1, 2, T // 2, T - 1]
+    o_ref, l_ref = oracle.sparse_decode(q[sample], "bf16", pool, pt[sample], ctx[sample], 64, 1 / 16)
+    _check(out[sample], lse[sample], o_ref, l_ref, BF16_ATOL, BF16_RTOL, f"dense planned T={T}")
+    assert torch.all(out[0] == 0)
+
+
+def test_dense_paged_planned_one_long_context():
+    """One 64K context and one short one: the plan gives the long one about 220 splits (rows
+    per split from the total), merged through one token word; the result against the oracle."""
+    q, pt, ctx, kv, pool = _dense_case(28, [65536, 300], 64)
+    out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(pt), _t(ctx), 64, 1 / 16)
+    o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, pt, ctx, 64, 1 / 16)
+    _check(out, lse, o_ref, l_ref, BF16_ATOL, BF16_RTOL, "dense planned 64K")
