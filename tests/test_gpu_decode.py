@@ -336,18 +336,19 @@ def test_workspace_init_clears_counters():
     _check(out, lse, o_ref, l_ref, BF16_ATOL, BF16_RTOL, "initialised workspace")
 
 
-def test_merge_in_stage2_past_counter_region():
-    """More tokens than the workspace's counter words cover (4096): stage 2 merges the
-    splits; a sample of tokens against the oracle."""
-    T = 4097
+@pytest.mark.parametrize("T", [4096, 4097])
+def test_merge_in_stage2_past_counter_region(T):
+    """The counter words cover 4,096 tokens. At 4,096 stage 1 still merges (the last token
+    uses the last word); one token more and stage 2 merges the splits. A sample of tokens,
+    the first and last of each region among them, against the oracle."""
     rng = np.random.default_rng(25)
     lens = rng.integers(1100, 2049, T)
     q, table, lens, live, vals = _random_case(25, T, 2048, lens, 30000)
     kv, pool = _pools(live, vals, 30000, "bf16")
     out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(table), _t(lens), 1, 1 / 16, num_splits=2)
-    sample = [0, 1, 2047, 4095, 4096]
+    sample = [i for i in (0, 1, 2047, 4095, 4096) if i < T]
     o_ref, l_ref = oracle.sparse_decode(q[sample], "bf16", pool, table[sample], lens[sample], 1, 1 / 16)
-    _check(out[sample], lse[sample], o_ref, l_ref, BF16_ATOL, BF16_RTOL, "stage-2 merge")
+    _check(out[sample], lse[sample], o_ref, l_ref, BF16_ATOL, BF16_RTOL, f"merge at T={T}")
 
 
 def test_merge_bits_independent_of_arrival_order():
