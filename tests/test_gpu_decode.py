@@ -202,6 +202,48 @@ def test_decode_graph_replay():
         assert int(ws[:256 * 1024].count_nonzero()) == 0, "merge counters not returned to zero by a replay"
 
 
+@pytest.mark.parametrize("name", ["decode_bf16_b32", "decode_fp8_b64"])
+def test_topk_fused_graph_replay(name):
+    """The one-kernel step the benchmark times (top-k positions resolved inside stage 1, the
+    splits merged inside it) captured twice into one HIP graph: every replay, with eager work
+    and synchronisation between replays, equals the eager result bit for bit and leaves the
+    merge counters at zero."""
+    c = gc.config(name)
+    lay = c.layout
+    fmt = "fp8" if "fp8" in name else "bf16"
+    kv, _ = gc.gpu_pool(smla, lay, c.rows, fmt)
+    qt = gc.q_tensor(c.q, c.q_dtype)
+    T, H = c.q.shape[0], c.q.shape[1]
+    args = (_t(c.idx), _t(c.valid), _t(c.tok_req), _t(lay.page_table), _t(lay.ctx), lay.page_size, c.scale)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = smla.new_workspace(smla.smla_sparse_decode_workspace(qt, kv, args[0], args[1], 1, c.scale), "cuda")
+
+    def step():
+        smla.smla_sparse_decode_topk(qt, kv, *args, out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+        step()
+    for _ in range(4):
+        out.fill_(float("nan"))
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+        assert int(ws[:256 * 1024].count_nonzero()) == 0, "merge counters not returned to zero by a replay"
+
+
 @pytest.mark.parametrize("name", ["decode_bf16_b32", "decode_ragged_b128", "decode_fp8_b64"])
 def test_topk_fused_equals_resolve_then_decode(name):
     """smla_sparse_decode_topk (resolution inside stage 1) is bitwise smla_resolve_slots followed
