@@ -114,3 +114,46 @@ def test_prefill_grouped_q8192_sampled():
     gc.assert_close(o, o_ref, 2e-2, 1e-2, "prefill_grouped_q8192 out")
     gc.assert_lse(lse[torch.from_numpy(sample).cuda()].cpu().numpy(), l_ref, 1e-3, "prefill_grouped_q8192 lse")
     assert gc.rel_l2(o, o_ref) <= 1e-2
+
+
+@pytest.mark.parametrize("Q,H,G", [(9, 64, 2), (13, 16, 8)])
+def test_prefill_graph_replay(Q, H, G):
+    """Union build + grouped prefill captured into a HIP graph: every replay, with eager work and
+    synchronisation between replays, gives the eager union, lengths and outputs bit for bit."""
+    q, slots, valid, kv, pool, ns = _small(40 + Q + G, Q, H, G)
+    st, vt, qt = _t(slots), _t(valid), gc.q_tensor(q, "bf16")
+    ng = -(-Q // G)
+    enc = torch.empty((ng, G * slots.shape[1]), dtype=torch.int32, device="cuda")
+    lens = torch.empty((ng,), dtype=torch.int32, device="cuda")
+    out = torch.empty((Q, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Q, H), dtype=torch.float32, device="cuda")
+
+    def step():
+        smla.smla_build_group_union(st, vt, G, ns, enc=enc, lens=lens)
+        smla.smla_grouped_prefill(qt, kv, enc, lens, G, 0.0625, out=out, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [lens.clone(), out.clone(), lse.clone()]
+    ref_enc = [enc[g, :int(ref[0][g])].clone() for g in range(ng)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        enc.fill_(-7)
+        lens.fill_(-1)
+        out.fill_(float("nan"))
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lens, ref[0]) and torch.equal(out, ref[1]) and torch.equal(lse, ref[2])
+        for k in range(ng):
+            assert torch.equal(enc[k, :int(ref[0][k])], ref_enc[k])
+    enc_o, lens_o = oracle.group_union(slots, valid, G, ns)
+    assert np.array_equal(lens.cpu().numpy(), lens_o)
