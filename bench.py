@@ -587,8 +587,8 @@ def main():
                          "readings give the scale for the decode kernels' FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (decode shards by request with no "
-              "exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: libsmla has no multi-GPU path (decode would shard by request, with no "
+              "exchange between GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

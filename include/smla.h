@@ -56,7 +56,7 @@ typedef enum {
   SMLA_ERR_NULL = 1,        /* a required pointer is NULL */
   SMLA_ERR_SHAPE = 2,       /* a size or stride is negative, zero where it must not be, or inconsistent */
   SMLA_ERR_ALIGN = 3,       /* a pointer or stride breaks the alignment stated for it */
-  SMLA_ERR_UNSUPPORTED = 4, /* a dtype, head count, group size or page size this build does not implement */
+  SMLA_ERR_UNSUPPORTED = 4, /* a dtype, head count, group size or page size the library does not implement */
   SMLA_ERR_RANGE = 5,       /* a size exceeds a documented limit */
   SMLA_ERR_WORKSPACE = 6,   /* the workspace is NULL or smaller than the size the query function gave */
   SMLA_ERR_DEVICE = 7       /* a HIP call or kernel launch failed */

@@ -3,8 +3,8 @@
     python -m sparse_mla_attention_resolve_amd.build [--verbose] [--resource-usage]
 
 Compiles every csrc/*.hip to an object in csrc/_build/ and links them into
-sparse_mla_attention_resolve_amd/libsmla.so. Always recompiles (the build check of
-this repository is that this succeeds from a clean tree).
+sparse_mla_attention_resolve_amd/libsmla.so. Always recompiles, also where a built
+library is already present.
 """
 from __future__ import annotations
 
