@@ -14,6 +14,7 @@ LATENT = 512
 ROPE = 64
 ROW = LATENT + ROPE
 ROW_BITS = 24            # union entries keep the row in bits 0..23, membership above
+INT32_MAX = 2 ** 31 - 1  # slots are 32-bit integers
 
 KV_F32 = "f32"
 KV_BF16 = "bf16"
@@ -36,7 +37,8 @@ def resolve_slots(idx, valid, tok_req, page_table, seq_lens, page_size):
     An entry resolves to -1 when it is padding or out of range: j >= valid[t] (the
     per-token count of valid entries), a token whose request is not a row of the page
     table, a negative index, an index at or past the request's context length, past the
-    page-table row, or on a page whose id is < 0.
+    page-table row, on a page whose id is < 0, or when the slot itself is past 2^31 - 1
+    (slots are 32-bit integers, so no pool has such a row).
     """
     idx = np.asarray(idx, dtype=np.int64)
     T, W = idx.shape
@@ -51,7 +53,9 @@ def resolve_slots(idx, valid, tok_req, page_table, seq_lens, page_size):
     ok &= page_no < pt.shape[1]
     page = pt[req, np.minimum(page_no, pt.shape[1] - 1)]
     ok &= page >= 0
-    return np.where(ok, page * page_size + idx % page_size, -1).astype(np.int32)
+    slot = page * page_size + idx % page_size
+    ok &= slot <= INT32_MAX                  # a slot no int32 table can name (reading: masked)
+    return np.where(ok, slot, -1).astype(np.int32)
 
 
 def attended_slots(table_row, length, page_size):

@@ -41,6 +41,14 @@ bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 smla_status check_kv(const smla_kv& kv, const char* fn, bool for_write) {
   CHECK(kv.reserved0 == 0, SMLA_ERR_SHAPE, "%s: kv.reserved0 must be 0", fn);
   CHECK(kv.num_slots > 0, SMLA_ERR_SHAPE, "%s: kv.num_slots must be > 0 (got %lld)", fn, (long long)kv.num_slots);
+  // slots travel as int32 through every table of the ABI, so a larger pool has rows no table can name
+  CHECK(kv.num_slots <= INT32_MAX, SMLA_ERR_RANGE, "%s: kv.num_slots must be <= 2^31 - 1 (got %lld)", fn,
+        (long long)kv.num_slots);
+  // the kernels form slot * stride as a 32 x 32 -> 64-bit product, so a row stride must fit 32 bits; the
+  // limit is far above any real row (1152 bytes for bf16, 656 for the packed fp8 row)
+  CHECK(kv.row_stride < (1ll << 20) && kv.lat8_stride < (1ll << 20) && kv.rope16_stride < (1ll << 20) &&
+            kv.scale_stride < (1ll << 20),
+        SMLA_ERR_RANGE, "%s: kv row strides must be below 1 MiB", fn);
   if (kv.dtype == SMLA_F32 || kv.dtype == SMLA_BF16) {
     const int64_t row_bytes = kv.dtype == SMLA_F32 ? 4 * SMLA_ROW : 2 * SMLA_ROW;
     CHECK(kv.rows != nullptr, SMLA_ERR_NULL, "%s: kv.rows is NULL", fn);
@@ -171,9 +179,6 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   if (a->lse) CHECK(a->lse_tok_stride >= a->H, SMLA_ERR_SHAPE, "%s: lse_tok_stride < H", fn);
   smla_status st = check_kv(a->kv, fn, false);
   if (st != SMLA_OK) return st;
-  CHECK(a->kv.row_stride < (1ll << 20) && a->kv.lat8_stride < (1ll << 20) && a->kv.rope16_stride < (1ll << 20) &&
-            a->kv.scale_stride < (1ll << 20),
-        SMLA_ERR_RANGE, "%s: kv row strides must be below 1 MiB", fn);
   if (need_ptrs && a->T > 0) {
     CHECK(a->q && a->table && a->lens && a->out, SMLA_ERR_NULL, "%s: q, table, lens and out are required", fn);
     CHECK(aligned(a->q, bf16 ? 16 : 4) && aligned(a->out, 16) && aligned(a->table, 4) && aligned(a->lens, 4) &&

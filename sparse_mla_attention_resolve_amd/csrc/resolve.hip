@@ -7,7 +7,8 @@
 
 namespace smla {
 
-// One thread per (token, entry); page_size is a power of two, so / and % are shifts.
+// One thread per (token, entry); page_size is a power of two, so / and % are shifts. The slot is
+// formed in 64 bits: one that does not fit int32 resolves to -1, as a pool cannot hold it.
 __global__ void __launch_bounds__(256) resolve_kernel(
     const int32_t* __restrict__ idx, int64_t idx_stride, const int32_t* __restrict__ valid,
     const int32_t* __restrict__ tok_req, int32_t R, const int32_t* __restrict__ page_table,
@@ -26,7 +27,9 @@ __global__ void __launch_bounds__(256) resolve_kernel(
       const int32_t page_no = i >> log2_page;
       if (page_no < pt_width) {
         const int32_t page = page_table[(int64_t)r * pt_stride + page_no];
-        if (page >= 0) out = (int32_t)(((int64_t)page << log2_page) + (i & ((1 << log2_page) - 1)));
+        // a slot past the int32 range (page id * P >= 2^31) names no row any table can hold: masked
+        const int64_t s = ((int64_t)page << log2_page) + (i & ((1 << log2_page) - 1));
+        if (page >= 0 && s <= INT32_MAX) out = (int32_t)s;
       }
     }
   }

@@ -403,7 +403,9 @@ def check_kv_write_fp8(ref, seed=14):
     rows = pool.rows(sm[live])
     err = np.abs(rows[:, :512] - src[live, :512])
     assert np.all(err <= np.abs(src[live, :512]) * 2.0 ** -4 + amax[:, None] / 448 * 2.0 ** -10)
-    assert np.all(np.isnan(pool.rows(np.array([sm[3] if sm[3] >= 0 else 0]))) | True)
+    # the skipped row (slot -1) wrote nothing: every slot outside the written ones still reads NaN
+    unwritten = np.setdiff1d(np.arange(100), sm[live])
+    assert len(unwritten) == 51 and np.all(np.isnan(pool.rows(unwritten)))
 
 
 def check_kv_write_bf16(ref, seed=15):

@@ -112,6 +112,9 @@ def test_decode_checks_and_workspace():
     assert _ws(_decode_args(num_splits=300))[0] == RANGE
     assert _ws(_decode_args(kv_row_stride=1000))[0] == SHAPE
     assert _ws(_decode_args(kv_row_stride=1160))[0] == ALIGN
+    assert _ws(_decode_args(kv_row_stride=1 << 20))[0] == RANGE                       # stride past 1 MiB
+    assert _ws(_decode_args(kv_num_slots=(1 << 31) - 1))[0] == OK
+    assert _ws(_decode_args(kv_num_slots=1 << 31))[0] == RANGE                        # slots are int32
     assert _ws(_decode_args(kv_dtype=7))[0] == UNSUP
     assert _ws(_decode_args(scale=float("nan")))[0] == SHAPE
     assert _ws(_decode_args(table_width=1 << 20, table_stride=1 << 20, page_size=1 << 11))[0] == RANGE
@@ -180,6 +183,9 @@ def test_prefill_checks():
     assert p(enc_width=5000) == SHAPE
     assert p(q=None) == NULL
     assert p(Q=0) == OK
+    # the same cache limits as decode: strides form 32-bit products in the kernel, slots are int32
+    assert p(kv_row_stride=1 << 32) == RANGE
+    assert p(kv_num_slots=1 << 31) == RANGE
 
 
 def test_kv_write_checks():

@@ -292,6 +292,39 @@ def test_topk_fused_masks(splits):
 
 
 
+def test_topk_slots_past_int32():
+    """Page ids whose slots pass the int32 range (page size 2^20; page id 4096 gives 2^32 + offset,
+    which a 32-bit slot would wrap onto a slot inside the pool): smla_resolve_slots masks them
+    as the oracle does, the fused path masks them too, and the two forms agree bitwise."""
+    rng = np.random.default_rng(23)
+    T, W, P, num_slots = 3, 512, 1 << 20, 1 << 16
+    page_table = np.array([[0, 4096, 2048]], np.int32)
+    seq_lens = np.array([3 * P], np.int32)
+    tok_req = np.zeros(T, np.int32)
+    idx = np.stack([np.concatenate([rng.choice(num_slots, W // 2, replace=False),
+                                    P + rng.choice(num_slots, W // 4, replace=False),
+                                    2 * P + rng.choice(num_slots, W // 4, replace=False)])
+                    for _ in range(T)]).astype(np.int32)
+    for t in range(T):
+        rng.shuffle(idx[t])
+    valid = np.full(T, W, np.int32)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((T, 64, 576)).astype(np.float32) * 0.5)
+    live = np.arange(num_slots, dtype=np.int32)
+    vals = rng.standard_normal((num_slots, 576)).astype(np.float32) * 0.5
+    kv, pool = _pools(live, vals, num_slots, "bf16")
+    qt = gc.q_tensor(q, "bf16")
+    args = (_t(idx), _t(valid), _t(tok_req), _t(page_table), _t(seq_lens))
+    slots = smla.smla_resolve_slots(*args, P)
+    oslots = oracle.resolve_slots(idx, valid, tok_req, page_table, seq_lens, P)
+    assert np.array_equal(slots.cpu().numpy(), oslots)
+    assert int((oslots >= 0).sum()) == T * W // 2               # only the page-0 positions resolve
+    a = smla.smla_sparse_decode(qt, kv, slots, _t(valid), 1, 1 / 16)
+    b = smla.smla_sparse_decode_topk(qt, kv, *args, P, 1 / 16)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, oslots, valid, 1, 1 / 16)
+    _check(b[0], b[1], o_ref, l_ref, BF16_ATOL, BF16_RTOL, "slots past int32")
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 def test_topk_long_page_table_row(kv_dtype):
     """A page-table row longer than the staging the fused path gives it in LDS (page size 1

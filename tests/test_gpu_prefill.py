@@ -50,6 +50,13 @@ def test_prefill_small(Q, H, G):
         bad[:, :] &= ~np.uint32(1 << 25)
         ob, _ = oracle.grouped_prefill(q, pool, bad, lens_o, G, 0.0625, queries=[1])
         assert gc.rel_l2(o[1], ob[0]) > 0.05
+    # the last query (the short last group's tail when Q % G != 0) dropped from its group
+    tail, gl, m = Q - 1, (Q - 1) // G, (Q - 1) % G
+    bad = enc_o.copy()
+    bad[gl, :] &= ~np.uint32(1 << (24 + m))
+    ob, lb = oracle.grouped_prefill(q, pool, bad, lens_o, G, 0.0625, queries=[tail])
+    assert np.all(ob[0] == 0) and np.all(np.isneginf(lb[0]))
+    assert gc.rel_l2(o[tail], ob[0]) > 0.05 and np.all(np.isfinite(lse[tail].cpu().numpy()))
 
 
 def _fp8_pool(vals, live, ns):
@@ -106,7 +113,8 @@ def test_prefill_grouped_q8192_sampled():
     enc, lens = smla.smla_build_group_union(slots, _t(c.valid), c.G, lay.num_slots)
     out, lse = smla.smla_grouped_prefill(gc.q_tensor(c.q, "bf16"), kv, enc, lens, c.G, c.scale)
     rng = np.random.default_rng(44)
-    sample = np.sort(np.concatenate([rng.choice(len(c.idx), size=254, replace=False), [0, len(c.idx) - 1]]))
+    sample = np.sort(np.concatenate([rng.choice(np.arange(1, len(c.idx) - 1), size=1022, replace=False),
+                                     [0, len(c.idx) - 1]]))
     enc_o, lens_o = oracle.group_union(oslots, c.valid, c.G, lay.num_slots)
     assert np.array_equal(lens.cpu().numpy(), lens_o)
     o_ref, l_ref = oracle.grouped_prefill(c.q, pool, enc_o, lens_o, c.G, c.scale, queries=sample)

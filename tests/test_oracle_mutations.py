@@ -22,6 +22,7 @@ MUTATIONS = [
     ("reference.py", "ok = req_ok & (j < n) &", "ok = req_ok & (j <= n) &"),                 # valid off by one
     ("reference.py", "ok = req_ok & (j < n) &", "ok = (j < n) &"),                          # unknown request kept
     ("reference.py", "(idx < np.asarray(seq_lens, dtype=np.int64)[req])", "(idx <= np.asarray(seq_lens, dtype=np.int64)[req])"),
+    ("reference.py", "ok &= slot <= INT32_MAX", "ok &= slot <= INT32_MAX + 1"),             # int32 slot range off by one
     ("reference.py", "page[keep] * page_size + p[keep] % page_size", "page[keep] * page_size + p[keep] % (page_size - 1)"),
     ("reference.py", "sel = row[:min(n, len(row))]", "sel = row[:len(row)]"),               # lens ignored
     ("reference.py", "mask |= np.isin(union, lst).astype(np.int64) << i", "mask |= np.isin(union, lst).astype(np.int64) << (G - 1 - i)"),
