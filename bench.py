@@ -334,6 +334,15 @@ def time_decode(c, smla, torch, steps, warmup, flush):
     e1.record()
     torch.cuda.synchronize()
     stream_ms = e0.elapsed_time(e1) / steps
+    # the same back-to-back loop again with an event after every step, for the spread of the
+    # per-step times (the events sit between launches, so this run is reported beside the first)
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evb[0].record()
+    for k in range(steps):
+        rot[k % BATCHES]()
+        evb[k + 1].record()
+    torch.cuda.synchronize()
+    per_step_ms = np.array([evb[k].elapsed_time(evb[k + 1]) for k in range(steps)])
 
     # warm steps: back to back, no flush
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -368,7 +377,7 @@ def time_decode(c, smla, torch, steps, warmup, flush):
     except Exception as ex:  # graph capture is a report-only extra
         log(f"graph capture skipped: {ex}")
     return {"step_ms": step_ms, "two_kernel": two, "warm_ms": warm_ms, "graph_ms": graph_ms, "wall_s": wall,
-            "splits": fused.splits, "stream_ms": stream_ms}
+            "splits": fused.splits, "stream_ms": stream_ms, "per_step_ms": per_step_ms}
 
 
 def time_ragged(c, smla, torch, steps, warmup, flush):
@@ -454,13 +463,101 @@ def time_kv_write(smla, torch, steps, warmup, flush, rows=1 << 20):
     return res
 
 
+def gather_ceiling(torch, flush, steps, rows=1 << 16, pool_rows=1 << 20):
+    """Context for the decode's HBM figures, measured on this GPU with torch's own kernels (not
+    libsmla): torch.index_select of `rows` random 1,152-byte rows out of a pool of `pool_rows`
+    (each row read once and written once), and a plain copy of 1 GiB, both cold (a 1 GiB read
+    before each), as GB/s of bytes read + written."""
+    pool = torch.zeros((pool_rows, 576), dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    idx = torch.rand(pool_rows, device="cuda", generator=g).argsort()[:rows]
+    out = torch.empty((rows, 576), dtype=torch.bfloat16, device="cuda")
+    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def cold(fn):
+        for _ in range(2):
+            flush.sum()
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for k in range(steps):
+            flush.sum()
+            ev[k][0].record()
+            fn()
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+
+    tg = cold(lambda: torch.index_select(pool, 0, idx, out=out))
+    tc = cold(lambda: dst.copy_(src))
+    gb = 2 * rows * 1152
+    res = {"what": "torch kernels on this GPU, cold, median: index_select of 65,536 random 1,152-byte rows of a 2^20-row "
+                   "pool (read + write), and a 1 GiB device copy (read + write); context for the HBM fractions, "
+                   "not the roofline peak",
+           "index_select_rows_gbs": gb / (tg / 1e3) / 1e9, "copy_gbs": 2 * (1 << 30) / (tc / 1e3) / 1e9}
+    del pool, out, src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_decode_h128(smla, torch, steps, warmup, T=32, W=2048, n=1 << 20):
+    """Decode with 128 heads per token (two blocks of 64 head slots), batch T, top-k W, over a
+    bf16 pool of n random rows: the index lists are fresh unique draws, back to back over 8
+    batches in rotation (a batch's rows return after ~530 MB of other rows)."""
+    kv = smla.KvCache.empty(smla.SMLA_BF16, n, device="cuda", poison=False)
+    kv.storage.normal_(0.0, 0.5)
+    g = torch.Generator(device="cuda").manual_seed(128)
+    q = (torch.randn(T, 128, 576, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    out = torch.empty((T, 128, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, 128), dtype=torch.float32, device="cuda")
+    lens = torch.full((T,), W, dtype=torch.int32, device="cuda")
+    tables = [torch.rand(T, n, device="cuda", generator=g).argsort(dim=1)[:, :W].to(torch.int32).contiguous()
+              for _ in range(BATCHES)]
+    calls = [smla.DecodeCall(q, kv, tables[0], lens, 1, 1 / 16, out, lse)]
+    calls += [smla.DecodeCall(q, kv, tb, lens, 1, 1 / 16, out, lse, workspace=calls[0].workspace) for tb in tables[1:]]
+    for k in range(warmup):
+        calls[k % BATCHES]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(steps):
+        calls[k % BATCHES]()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = T * W * 1152 + T * 128 * (576 + 512) * 2 + T * 128 * 4 + T * W * 4
+    del kv, tables
+    torch.cuda.empty_cache()
+    return {"workload": f"sparse MLA decode, bf16, batch {T}, 128 heads (two blocks of 64 head slots), top-k {W}, "
+                        f"{n}-slot pool, resolved slot tables, 8 rotating batches back to back",
+            "queries_per_s": T / (ms / 1e3), "ms_per_step": ms, "algorithmic_bytes_step": alg,
+            "hbm_gbs_step": alg / (ms / 1e3) / 1e9, "hbm_frac_step": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "splits": calls[0].splits}
+
+
+def prefill_flop_done(enc, lens, G, H):
+    """FLOP the grouped-prefill kernel issues: its workgroups each serve 64 / H members of a group
+    (64 head slots) and walk the group's union entries that name one of them, 2 * (576 + 512)
+    FLOP per (entry, head slot)."""
+    enc = enc.cpu().numpy().view(np.uint32)
+    lens = lens.cpu().numpy()
+    mpw = 64 // H
+    total = 0
+    for g in range(len(lens)):
+        bits = enc[g, :int(lens[g])] >> 24
+        for m0 in range(0, G, mpw):
+            total += int(np.count_nonzero(bits & (((1 << mpw) - 1) << m0)))
+    return float(total) * 64 * 2 * (576 + 512)
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_KERNEL = {"bf16": "decode_stage1_mfma<bf16, union>", "fp8": "decode_stage1_mfma<fp8, union>"}
 
 
-def time_prefill(c, smla, torch, steps, warmup, flush, cpu_seconds):
-    """Grouped sparse prefill (union build + grouped attention) on case `c`: cold steps (the
-    flush before each), each kernel alone and the two together, against the bf16 MFMA peak;
-    the oracle on a bounded sample of groups."""
+def time_prefill(c, smla, torch, steps, warmup, flush, cpu_seconds, kv_dtype="bf16"):
+    """Grouped sparse prefill (union build + grouped attention) on case `c`, over a bf16 or an fp8
+    cache written from the case's rows: cold steps (the flush before each), each kernel alone and
+    the two together, against the bf16 MFMA peak; the oracle on a bounded sample of groups."""
     dev = "cuda"
 
     def t(a):
@@ -468,7 +565,7 @@ def time_prefill(c, smla, torch, steps, warmup, flush, cpu_seconds):
 
     lay = c.layout
     Q, H = c.q.shape[0], c.q.shape[1]
-    kv = smla.KvCache.empty(smla.SMLA_BF16, lay.num_slots, device=dev)
+    kv = smla.KvCache.empty(smla.SMLA_BF16 if kv_dtype == "bf16" else smla.SMLA_FP8_E4M3, lay.num_slots, device=dev)
     smap = smla.smla_resolve_slots(t(c.rows.pos[:, None]), None, t(c.rows.req), t(lay.page_table), t(lay.ctx),
                                    lay.page_size)[:, 0].contiguous()
     smla.smla_kv_write(t(c.rows.values.view(np.int16)).view(torch.bfloat16), smap, kv)
@@ -505,17 +602,20 @@ def time_prefill(c, smla, torch, steps, warmup, flush, cpu_seconds):
     both = np.array([e[0].elapsed_time(e[2]) for e in ev])
     n_union = int(lens.sum().item())
     flop_alg = float(c.valid.astype(np.int64).sum()) * H * 2 * (576 + 512)
-    flop_done = float(n_union) * c.G * H * 2 * (576 + 512)
+    flop_done = prefill_flop_done(enc, lens, c.G, H)
     p_mean = float(p_ms.mean())
-    res = {"workload": f"{c.name}: union build + grouped attention; KV pool {lay.num_slots} slots (cache-resident)",
-           "queries": Q, "group": c.G, "union_rows": n_union, "union_over_topk": n_union / float(c.valid.sum()) * c.G,
+    res = {"workload": f"{c.name}: union build + grouped attention; {kv_dtype} KV pool of {lay.num_slots} slots "
+                       f"(cache-resident)",
+           "queries": Q, "group": c.G, "kv_dtype": kv_dtype, "union_rows": n_union,
+           "union_over_topk": n_union / float(c.valid.sum()) * c.G,
            "step_ms": float(both.mean()), "union_us": float(u_ms.mean()) * 1e3, "prefill_ms": p_mean,
+           "prefill_p10_ms": float(np.percentile(p_ms, 10)), "prefill_p90_ms": float(np.percentile(p_ms, 90)),
            "tokens_per_s": Q / (float(both.mean()) / 1e3),
-           "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": flop_alg / (p_mean / 1e3) / 1e12,
+           "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL[kv_dtype], "achieved": flop_alg / (p_mean / 1e3) / 1e12,
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": flop_alg / (p_mean / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                        "algorithmic_flop_per_launch": flop_alg, "computed_flop_per_launch": flop_done,
-                        "computed_tflops": flop_done / (p_mean / 1e3) / 1e12, "avg_launch_us": p_mean * 1e3}}
+                        "algorithmic_flop_per_launch": flop_alg, "issued_flop_per_launch": flop_done,
+                        "issued_tflops": flop_done / (p_mean / 1e3) / 1e12, "avg_launch_us": p_mean * 1e3}}
     if cpu_seconds > 0:
         import oracle
         pool = oracle.Pool(lay.num_slots, "bf16")
@@ -538,30 +638,108 @@ def time_prefill(c, smla, torch, steps, warmup, flush, cpu_seconds):
     return res
 
 
-def cpu_baseline(c, seconds: float) -> dict:
-    import oracle
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu reports it)."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    lay = c.layout
-    pool = oracle.Pool(lay.num_slots, c.kv_dtype)
-    osl = oracle.resolve_slots(c.rows.pos[:, None], None, c.rows.req, lay.page_table, lay.ctx, lay.page_size)[:, 0]
-    oracle.kv_write(pool, c.rows.values, "bf16" if c.rows.values.dtype == np.uint16 else "f32", osl)
-    T = c.q.shape[0]
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_threads() -> int:
+    """Cores this process may run on, capped at the 16 host cores one GPU's share of the box has."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_decode_queries(d: str, tokens, seconds: float, start_at: float):
+    """One oracle process: resolve + fp64 attention of the given tokens, one token at a time,
+    for `seconds` from the wall-clock time `start_at`, with one BLAS thread. The workload's
+    arrays come memory-mapped from directory d. Returns the number of queries done."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    a = {k[:-4]: np.load(os.path.join(d, k), mmap_mode="r") for k in os.listdir(d) if k.endswith(".npy")}
+    meta = json.load(open(os.path.join(d, "meta.json")))
+    # the cache the oracle's own kv_write stored (written once, by the parent)
+    pool = oracle.Pool(meta["num_slots"], meta["kv_dtype"])
+    pool.store(a["pool_slots"], {k[6:]: np.asarray(v) for k, v in a.items() if k.startswith("plane_")})
     done = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        t = done % T
-        sl = oracle.resolve_slots(c.idx[t:t + 1], c.valid[t:t + 1], c.tok_req[t:t + 1], lay.page_table, lay.ctx,
-                                  lay.page_size)
-        oracle.sparse_decode(c.q[t:t + 1], c.q_dtype, pool, sl, c.valid[t:t + 1], 1, c.scale)
-        done += 1
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} decode queries of the same workload (token t mod {T}, resolve + fp64 attention), "
-                      f"{el:.1f} s wall on the host"}
+    with threadpool_limits(1):
+        while time.time() < start_at:
+            time.sleep(0.005)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            t = int(tokens[done % len(tokens)])
+            sl = oracle.resolve_slots(a["idx"][t:t + 1], a["valid"][t:t + 1], a["tok_req"][t:t + 1], a["page_table"],
+                                      a["ctx"], meta["page_size"])
+            oracle.sparse_decode(np.asarray(a["q"][t:t + 1]), meta["q_dtype"], pool, sl, a["valid"][t:t + 1], 1,
+                                 meta["scale"])
+            done += 1
+    return done
+
+
+def cpu_baseline(c, seconds: float) -> dict:
+    """The oracle (plain numpy fp64, as it stands) on the host: decode queries of the workload
+    (resolve + attention per token). Two rates: one core (one process, one BLAS thread) for a
+    third of `seconds`, and all cores (one process per core, each one BLAS thread, over its
+    share of the tokens) for the rest. Runs before anything touches the GPU, so that the worker
+    processes start from a process without GPU state."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    lay = c.layout
+    d = tempfile.mkdtemp(prefix="smla_oracle_")
+    try:
+        import oracle
+        pool = oracle.Pool(lay.num_slots, c.kv_dtype)
+        osl = oracle.resolve_slots(c.rows.pos[:, None], None, c.rows.req, lay.page_table, lay.ctx, lay.page_size)[:, 0]
+        oracle.kv_write(pool, c.rows.values, "bf16" if c.rows.values.dtype == np.uint16 else "f32", osl)
+        written = np.unique(osl[osl >= 0])
+        arrays = {"pool_slots": written, "page_table": lay.page_table, "ctx": lay.ctx, "idx": c.idx,
+                  "valid": c.valid, "tok_req": c.tok_req, "q": c.q}
+        arrays.update({"plane_" + k: v for k, v in pool.stored(written).items()})
+        del pool
+        for k, v in arrays.items():
+            np.save(os.path.join(d, k + ".npy"), np.ascontiguousarray(v))
+        json.dump({"num_slots": int(lay.num_slots), "kv_dtype": c.kv_dtype, "page_size": int(lay.page_size),
+                   "q_dtype": c.q_dtype, "scale": float(c.scale)}, open(os.path.join(d, "meta.json"), "w"))
+        T = c.q.shape[0]
+        s1 = seconds / 3
+        n1 = _oracle_decode_queries(d, np.arange(T), s1, time.time())
+        n = host_threads()
+        s2 = seconds - s1
+        env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+        for k in env:
+            os.environ[k] = "1"
+        try:
+            with cf.ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn")) as ex:
+                start_at = time.time() + 5.0                  # every worker has started and loaded by then
+                futs = [ex.submit(_oracle_decode_queries, d, np.arange(i, T, n) if i < T else np.arange(T), s2,
+                                  start_at) for i in range(n)]
+                counts = [f.result() for f in futs]
+        finally:
+            for k, v in env.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    rate_all = sum(counts) / s2
+    return {"value": rate_all, "unit": "queries/s", "cores": n, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{sum(counts)} decode queries of the same workload (resolve + fp64 attention per token, "
+                      f"tokens dealt over {n} processes of one BLAS thread each), {s2:.1f} s wall on the host",
+            "single_core": {"value": n1 / s1, "unit": "queries/s", "cores": 1,
+                            "sample": f"{n1} decode queries, one process, one BLAS thread, {s1:.1f} s wall"}}
 
 
 def main():
@@ -575,6 +753,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-kv-write", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the context rows: 128-head decode, fp8 grouped prefill, dense paged decode, gather ceiling")
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--overlap-sweep", action="store_true",
                     help="only time grouped prefill against per-query decode for G = 2 / 4 / 8 over list "
@@ -585,14 +765,33 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three plain 256 MiB fp32 copy kernels (y = x * 1), whose HBM counter "
                          "readings give the scale for the decode kernels' FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--summarize-profile", nargs="+", metavar=("KIND", "DIR"),
+                    help="no GPU work: reduce rocprofv3 output directories into a profiles/ table. KIND trace DIR | "
+                         "traffic FETCH_DIR WRITE_DIR | sq DIR_A DIR_B")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: libsmla has no multi-GPU path (decode would shard by request, with no "
               "exchange between GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import torch
     import workloads as wl
+    sweeping = args.split_sweep or args.overlap_sweep
+    c2 = None
+    cpu = None
+    if not sweeping:
+        log("generating the bf16 decode workload (batch 32, top-k 2048)")
+        c2 = wl.decode_bf16_b32()
+        if not args.no_cpu_baseline:
+            # before anything touches the GPU: the oracle's worker processes start from this one
+            log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
+            cpu = cpu_baseline(c2, args.cpu_seconds)
+            log(f"oracle: {cpu['single_core']['value']:.0f} queries/s on one core, {cpu['value']:.0f} on "
+                f"{cpu['cores']} ({cpu['cpu_model']})")
+
+    import torch
     import sparse_mla_attention_resolve_amd as smla
 
     if not os.path.exists(smla.LIB_PATH):
@@ -606,8 +805,6 @@ def main():
         overlap_sweep(smla, torch, flush, max(3, args.steps // 10))
         return
 
-    log("generating the bf16 decode workload (batch 32, top-k 2048)")
-    c2 = wl.decode_bf16_b32()
     ab = algorithmic_bytes(c2, "bf16")
     log("timing bf16 decode")
     r = time_decode(c2, smla, torch, args.steps, args.warmup, flush)
@@ -617,10 +814,13 @@ def main():
     step_gbs = ab["step"] / (step_ms / 1e3) / 1e9
     iso_ms = float(r["step_ms"].mean())
     two = r["two_kernel"]
+    ps = r["per_step_ms"]
     log(f"step {step_ms*1e3:.1f} us back to back over {BATCHES} rotating batches (one kernel: {step_gbs:.0f} GB/s "
-        f"of algorithmic bytes); one isolated cold launch {iso_ms*1e3:.1f} us; warm {r['warm_ms']*1e3:.1f} us; "
-        f"graph {(r['graph_ms'] or 0)*1e3:.1f} us. Two-kernel form: {two['step_ms'].mean()*1e3:.1f} us (resolve "
-        f"{two['resolve_ms'].mean()*1e3:.1f}, decode {two['decode_ms'].mean()*1e3:.1f})")
+        f"of algorithmic bytes; per-step p10/p50/p90 {np.percentile(ps, 10)*1e3:.1f}/{np.median(ps)*1e3:.1f}/"
+        f"{np.percentile(ps, 90)*1e3:.1f} us); one isolated cold launch {iso_ms*1e3:.1f} us; warm "
+        f"{r['warm_ms']*1e3:.1f} us; graph {(r['graph_ms'] or 0)*1e3:.1f} us. Two-kernel form: "
+        f"{two['step_ms'].mean()*1e3:.1f} us (resolve {two['resolve_ms'].mean()*1e3:.1f}, decode "
+        f"{two['decode_ms'].mean()*1e3:.1f})")
 
     def us(a):
         return float(np.mean(a)) * 1e3
@@ -638,6 +838,10 @@ def main():
         "hbm_gbs_step": step_gbs, "hbm_frac_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_step": ab["step"],
         "timing_us": {"step_back_to_back": step_ms * 1e3,
+                      "per_step_events": {"what": "the back-to-back loop rerun with an event recorded after every "
+                                                  "step; the events between launches lengthen each step a little",
+                                          "p10": float(np.percentile(ps, 10)) * 1e3, "p50": float(np.median(ps)) * 1e3,
+                                          "p90": float(np.percentile(ps, 90)) * 1e3, "mean": float(ps.mean()) * 1e3},
                       "isolated_cold_launch_mean": iso_ms * 1e3,
                       "isolated_cold_launch_median": float(np.median(r["step_ms"])) * 1e3,
                       "isolated_cold_launch_p10": float(np.percentile(r["step_ms"], 10)) * 1e3,
@@ -662,19 +866,25 @@ def main():
         ms5 = r5["stream_ms"]
         two5 = r5["two_kernel"]
         gbs5 = ab5["step"] / (ms5 / 1e3) / 1e9
+        ps5 = r5["per_step_ms"]
         line["fp8_kv_decode"] = {
             "workload": "batch 64, 64 heads, fp8 e4m3 latent + bf16 rope + fp32 scale per row, context 64K, top-k 2048",
             "queries_per_s": c5.q.shape[0] / (ms5 / 1e3), "ms_per_step": ms5,
             "hbm_gbs_step": gbs5, "hbm_frac_step": gbs5 / HBM_PEAK_GBS,
             "algorithmic_bytes_step": ab5["step"],
+            "per_step_us_p10_p50_p90": [float(np.percentile(ps5, 10)) * 1e3, float(np.median(ps5)) * 1e3,
+                                        float(np.percentile(ps5, 90)) * 1e3],
             "isolated_cold_launch_us": float(np.mean(r5["step_ms"])) * 1e3,
             "warm_step_us": r5["warm_ms"] * 1e3, "splits": r5["splits"],
-            "traffic": measured_traffic("decode_stage1_mfma<fp8>", "fp8_batch_64"),
+            "roofline": {"bound": "hbm", "kernel": "decode_stage1_mfma<fp8>", "achieved": gbs5, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs5 / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": ab5["step"],
+                         "avg_launch_us": ms5 * 1e3,
+                         "traffic": measured_traffic("decode_stage1_mfma<fp8>", "fp8_batch_64")},
             "two_kernel_form_us": {"step": us(two5["step_ms"]), "resolve": us(two5["resolve_ms"]),
                                    "decode": us(two5["decode_ms"])}}
         log(f"fp8: step {ms5*1e3:.1f} us back to back (isolated cold launch {np.mean(r5['step_ms'])*1e3:.1f}; "
-            f"{gbs5:.0f} GB/s); "
-            f"two-kernel form {us(two5['step_ms']):.1f} us")
+            f"{gbs5:.0f} GB/s); two-kernel form {us(two5['step_ms']):.1f} us")
+        del c5
 
     if not args.no_ragged:
         log("generating the ragged decode workload (batch 128, 13 dense requests)")
@@ -692,7 +902,24 @@ def main():
                           0.0 if args.no_cpu_baseline else min(5.0, args.cpu_seconds))
         line["grouped_prefill"] = pr
         log(f"grouped prefill: union {pr['union_us']:.0f} us + attention {pr['prefill_ms']:.2f} ms "
-            f"({pr['roofline']['achieved']:.0f} TFLOP/s algorithmic, {pr['roofline']['computed_tflops']:.0f} computed)")
+            f"({pr['roofline']['achieved']:.0f} TFLOP/s algorithmic, {pr['roofline']['issued_tflops']:.0f} issued)")
+        if not args.no_extra:
+            log("timing grouped prefill over an fp8 cache")
+            pf = time_prefill(c4, smla, torch, max(3, args.steps // 5), 2, flush, 0.0, kv_dtype="fp8")
+            line["grouped_prefill_fp8"] = pf
+            log(f"grouped prefill (fp8 cache): union {pf['union_us']:.0f} us + attention {pf['prefill_ms']:.2f} ms "
+                f"({pf['roofline']['achieved']:.0f} TFLOP/s algorithmic)")
+        del c4
+
+    if not args.no_extra:
+        log("timing 128-head decode (batch 32, top-k 2048)")
+        h1 = time_decode_h128(smla, torch, args.steps, args.warmup)
+        line["decode_h128"] = h1
+        log(f"128 heads: step {h1['ms_per_step']*1e3:.1f} us ({h1['hbm_gbs_step']:.0f} GB/s)")
+        log("measuring the gather and copy ceilings (torch kernels)")
+        line["context_ceilings"] = gather_ceiling(torch, flush, max(5, args.steps // 5))
+        log(f"index_select of random rows {line['context_ceilings']['index_select_rows_gbs']:.0f} GB/s, "
+            f"copy {line['context_ceilings']['copy_gbs']:.0f} GB/s")
 
     if not args.no_kv_write:
         log("timing smla_kv_write (1M rows)")
@@ -701,9 +928,8 @@ def main():
         log(f"kv_write: bf16 {kw['bf16']['us']:.0f} us ({kw['bf16']['hbm_gbs']:.0f} GB/s), fp8 {kw['fp8']['us']:.0f} us "
             f"({kw['fp8']['hbm_gbs']:.0f} GB/s)")
 
-    if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
-        line["cpu_baseline"] = cpu_baseline(c2, args.cpu_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     if args.copy_calibration:
         x = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         y = torch.empty_like(x)
@@ -713,6 +939,10 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x (read 256 MiB, write 256 MiB)")
     print(json.dumps(line), flush=True)
+
+
+def summarize_profile(argv):
+    raise SystemExit("--summarize-profile: not available yet")
 
 
 if __name__ == "__main__":
