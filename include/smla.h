@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 3
+#define SMLA_ABI_VERSION 4
 
 #define SMLA_LATENT 512          /* latent (value) columns of a cache row */
 #define SMLA_ROPE 64             /* rotary columns of a cache row */
@@ -246,6 +246,33 @@ smla_status smla_sparse_decode_topk(const smla_decode_args* args, const smla_pag
                                     size_t workspace_bytes, void* stream);
 smla_status smla_sparse_decode_topk_stage1(const smla_decode_args* args, const smla_page_map* map,
                                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Decode without allocation, for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).
+ *
+ * The full decode of smla_sparse_decode (map == NULL) or of smla_sparse_decode_topk (map
+ * != NULL, same page-map contract), with the same validation, kernels, split plan and
+ * results, but its workspace is a static device array inside the library instead of caller
+ * memory: 34 MiB (35,651,584 bytes) on every GPU the library runs on, held from the
+ * library's load until the process ends. The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine); the caller still passes inputs and outputs.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents:
+ * calls that overlap in time on one GPU (two streams, two threads) race and give wrong
+ * results; calls on one stream, one after another, are safe. The merge words at the head of
+ * the array are cleared by a fill kernel on `stream` at the first call on each device (and
+ * every decode leaves them zero); a first call made under graph capture clears them inside
+ * the graph and again at the next call that is not captured.
+ *
+ * Errors: as smla_sparse_decode / smla_sparse_decode_topk; SMLA_ERR_RANGE when the call
+ * needs more workspace than the array holds (smla_sparse_decode_workspace reports the need:
+ * 64 KiB per (token, 64-head block, split) plus 256 KiB, e.g. 16.6 MiB for batch 32 x 8
+ * splits at 64 heads); SMLA_ERR_DEVICE when the device or the array's address cannot be
+ * obtained.
+ * ------------------------------------------------------------------------------- */
+smla_status smla_sparse_decode_noalloc(const smla_decode_args* args, const smla_page_map* map, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * Group top-k union with per-query membership bits.

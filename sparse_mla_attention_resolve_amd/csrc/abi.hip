@@ -337,6 +337,36 @@ static smla_status decode_stages(const smla_decode_args* args, void* workspace, 
                        "smla_sparse_decode");
 }
 
+}  // extern "C"
+
+// Shared with the allocation-free entry point (noalloc.hip), which owns its workspace.
+namespace smla {
+
+smla_status decode_workspace_bytes(const smla_decode_args* args, const smla_page_map* map, size_t* bytes) {
+  smla::DecodePlan plan;
+  smla_status st = check_decode(args, &plan, true);
+  if (st != SMLA_OK) return st;
+  if (map) {
+    st = check_page_map(args, map);
+    if (st != SMLA_OK) return st;
+  }
+  *bytes = args->T == 0 ? 0 : plan.ws_bytes;
+  return ok();
+}
+
+smla_status decode_enqueue(const smla_decode_args* args, const smla_page_map* map, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  return decode_stages(args, workspace, workspace_bytes, stream, 3, map);
+}
+
+smla_status report(smla_status st, const char* msg) { return fail(st, "%s", msg); }
+
+smla_status report_device(hipError_t e, const char* what) { return device_status(e, what); }
+
+}  // namespace smla
+
+extern "C" {
+
 smla_status smla_sparse_decode(const smla_decode_args* args, void* workspace, size_t workspace_bytes,
                                void* stream) {
   return decode_stages(args, workspace, workspace_bytes, stream, 3);

@@ -68,4 +68,14 @@ hipError_t launch_union_decode(const smla_prefill_args& a, hipStream_t stream);
 // Zero-fill bytes / 16 16-byte words at p (a kernel, so it may be captured in a graph).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 
+// Decode validation and enqueue for callers that own the workspace (abi.hip): the bytes a full
+// decode (both stages; map may be NULL) needs, and the enqueue itself. Both validate exactly as
+// smla_sparse_decode / smla_sparse_decode_topk do and leave the same messages.
+smla_status decode_workspace_bytes(const smla_decode_args* args, const smla_page_map* map, size_t* bytes);
+smla_status decode_enqueue(const smla_decode_args* args, const smla_page_map* map, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+// Record a failure for smla_last_error() and return its status.
+smla_status report(smla_status st, const char* msg);
+smla_status report_device(hipError_t e, const char* what);
+
 }  // namespace smla

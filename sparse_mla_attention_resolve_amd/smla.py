@@ -28,7 +28,7 @@ STATUS_CODES = {v: k for k, v in STATUS.items()}
 EXPORTS = ["smla_resolve_slots", "smla_sparse_decode_workspace", "smla_sparse_decode_workspace_init",
            "smla_sparse_decode_splits",
            "smla_sparse_decode", "smla_sparse_decode_stage1", "smla_sparse_decode_stage2",
-           "smla_sparse_decode_topk", "smla_sparse_decode_topk_stage1",
+           "smla_sparse_decode_topk", "smla_sparse_decode_topk_stage1", "smla_sparse_decode_noalloc",
            "smla_build_group_union", "smla_grouped_prefill", "smla_kv_write",
            "smla_status_str", "smla_last_error", "smla_abi_version", "smla_sizeof_kv",
            "smla_sizeof_decode_args", "smla_sizeof_prefill_args", "smla_sizeof_page_map"]
@@ -91,6 +91,7 @@ _sig = {
     "smla_sparse_decode_topk": [ctypes.POINTER(smla_decode_args), ctypes.POINTER(smla_page_map), c_p, c_sz, c_p],
     "smla_sparse_decode_topk_stage1": [ctypes.POINTER(smla_decode_args), ctypes.POINTER(smla_page_map), c_p, c_sz,
                                        c_p],
+    "smla_sparse_decode_noalloc": [ctypes.POINTER(smla_decode_args), ctypes.POINTER(smla_page_map), c_p],
     "smla_build_group_union": [c_p, c_i64, c_p, c_i32, c_i32, c_i32, c_i64, c_p, c_i64, c_p, c_p],
     "smla_grouped_prefill": [ctypes.POINTER(smla_prefill_args), c_p],
     "smla_kv_write": [c_p, c_i32, c_i64, c_p, c_i32, ctypes.POINTER(smla_kv), c_p],
@@ -317,6 +318,23 @@ def smla_sparse_decode_topk(q, kv: KvCache, idx, valid, tok_req, page_table, seq
         workspace = new_workspace(need.value, q.device)
     _check(_lib.smla_sparse_decode_topk(ctypes.byref(a), ctypes.byref(m), _ptr(workspace), workspace.numel(),
                                         _stream(stream)))
+    return out, lse
+
+
+def smla_sparse_decode_noalloc(q, kv: KvCache, table, lens, page_size: int, scale: float,
+                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                               want_lse: bool = True, num_splits: int = 0, page_map=None, stream=None):
+    """The decode with the library's static workspace (no workspace argument, nothing allocated
+    by the library). page_map=(tok_req, page_table, seq_lens, page_size) makes `table` logical
+    top-k indices resolved inside stage 1, as smla_sparse_decode_topk. Returns (out, lse)."""
+    T, H, _ = q.shape
+    if out is None:
+        out = torch.empty((T, H, LATENT), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    a = _decode_args(q, kv, table, lens, page_size, scale, out, lse, num_splits)
+    m = None if page_map is None else ctypes.byref(_page_map(*page_map))
+    _check(_lib.smla_sparse_decode_noalloc(ctypes.byref(a), m, _stream(stream)))
     return out, lse
 
 

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_struct_sizes_and_version():
     lib = S.lib()
-    assert lib.smla_abi_version() == 3
+    assert lib.smla_abi_version() == 4
     assert lib.smla_sizeof_page_map() == ctypes.sizeof(S.smla_page_map) == 48
     assert lib.smla_sizeof_kv() == ctypes.sizeof(S.smla_kv) == 80
     assert lib.smla_sizeof_decode_args() == ctypes.sizeof(S.smla_decode_args)
@@ -228,3 +228,19 @@ def test_decode_topk_checks():
     # a valid map reaches the workspace check, which precedes any launch
     assert f(ctypes.byref(a), ctypes.byref(_map()), None, 0, None) == S.STATUS_CODES["SMLA_ERR_WORKSPACE"]
     assert S.lib().smla_sparse_decode_topk_stage1(ctypes.byref(a), None, None, 0, None) == NULL
+
+
+def test_decode_noalloc_checks():
+    """The allocation-free decode validates like the other decode entry points and refuses, before
+    touching the device, a call whose workspace would not fit its static scratch (34 MiB)."""
+    f = S.lib().smla_sparse_decode_noalloc
+    assert f(None, None, None) == NULL
+    assert f(ctypes.byref(_decode_args(page_size=3)), None, None) == UNSUP
+    assert f(ctypes.byref(_decode_args(q=None)), None, None) == NULL
+    assert f(ctypes.byref(_decode_args(T=0)), None, None) == OK
+    # 1,024 tokens of one split each: 1,024 partials of 64 KiB, past the scratch
+    big = _decode_args(T=1024)
+    assert _ws(big)[1] > (34 << 20)
+    assert f(ctypes.byref(big), None, None) == RANGE
+    assert b"static scratch" in S.lib().smla_last_error()
+    assert f(ctypes.byref(_decode_args(page_size=64)), ctypes.byref(_map()), None) == UNSUP   # map needs page_size 1
