@@ -646,9 +646,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int hq = w & 3, x = w >> 2;
   const int h0 = 16 * hq;
-  // waves issuing kLoadsHi copies per chunk (the others kLoadsLo): the first kHiWaves, and for
-  // fp8 also the last wave, whose extra copy is the chunk's row scales
-  const bool hi = w < kHiWaves || (kFp8 && w == kS1Waves - 1);
+  // waves issuing kLoadsHi copies per chunk (the others kLoadsLo): the first kHiWaves
+  const bool hi = w < kHiWaves;
 
   // ---- prologue. What the first gathers need goes out as early as it can:
   //   - at once (it needs only the kernel's arguments): the split's table entries
@@ -659,7 +658,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   //     load) and its page-table row, into ring slot 1 when the row fits there.
   // All of it lands before the slots are built, so that building them touches LDS only (a
   // register that a global load may still be writing would make the compiler wait for
-  // every copy in flight, since it does not see them). q follows with the first chunks.
+  // every copy in flight, since it does not see them). Decode issues q right behind it and
+  // leaves q in flight meanwhile; union mode issues q first.
   const int lp = a.log2_page;
   const int r0 = s * rps;
   const bool mapped = a.mapped != 0;
@@ -728,7 +728,15 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
         }
       }
     }
-    wait_vmcnt<0>();
+    if constexpr (!UNION) {
+      // decode: q goes out right behind the entries (it depends on the token alone) and stays
+      // in flight while the slots are built: the wait below covers the entries only, the
+      // copies issued before q
+      copy_q();
+      wait_vmcnt<kQLoads / 2>();
+    } else {
+      wait_vmcnt<0>();
+    }
   }
   if (r0 >= len) {                              // inactive split: no merge reads it
     wait_vmcnt<0>();                            // no copy may land after the workgroup is gone
@@ -779,31 +787,15 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   struct Copies {
     int32_t slot[kLoadsHi];                     // -1: masked row, copied from the zero row
   };
-  // fp8: the last wave, which has fewer row copies, copies the chunk's 32 row scales as its
-  // copy kLoadsLo (lanes 0 .. 31), next to the rows' own gathers (the scale shares a cache line
-  // with the row's rotary part)
-  const bool row_hi = w < kHiWaves;
-  const bool scale_wave = kFp8 && w == kS1Waves - 1;
-  static_assert(!kFp8 || (kHiWaves < kS1Waves && kLoadsHi == kLoadsLo + 1), "the scale copy fills a short wave");
   auto src_of = [&](int ci) {
     Copies cp;
     const int32_t* srow = slot_s + ci * kChunk;
 #pragma unroll
-    for (int k = 0; k < kLoadsHi; ++k)
-      cp.slot[k] = (k < kLoadsLo || row_hi) ? srow[lpos[k] & 0xff] : scale_wave ? srow[lane & (kChunk - 1)] : -1;
+    for (int k = 0; k < kLoadsHi; ++k) cp.slot[k] = (k < kLoadsLo || hi) ? srow[lpos[k] & 0xff] : -1;
     return cp;
   };
   auto fire = [&](const Copies& cp, int ci, int k) {
-    if (!(k < kLoadsLo || row_hi)) {
-      if constexpr (kFp8) {
-        if (scale_wave && lane < kChunk) {
-          const int32_t sl = umode && cp.slot[k] >= 0 ? cp.slot[k] & ((1 << SMLA_UNION_ROW_BITS) - 1) : cp.slot[k];
-          dma4(sl >= 0 ? (const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride : (const char*)kZeroRow,
-               (char*)(scale_s + ci * kChunk));
-        }
-      }
-      return;
-    }
+    if (!(k < kLoadsLo || hi)) return;
     const int32_t sl = umode && cp.slot[k] >= 0 ? cp.slot[k] & ((1 << SMLA_UNION_ROW_BITS) - 1) : cp.slot[k];
     const int unit = lpos[k] >> 8;
     const bool live = sl >= 0;
@@ -1043,12 +1035,25 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     }
     lds_barrier();
     const int nchunks = (nrows + kChunk - 1) / kChunk;
+    if constexpr (kFp8) {
+      // the segment's row scales, copied once before its first rows: one 4-byte copy per row
+      // into scale_s (masked rows read 0 from the zero row). A per-chunk scale copy inside the
+      // loop held each chunk's row gathers up behind it (the fp8 loop took 2.3 instead of 1.3 us
+      // per chunk), so the scales go out here, ahead of q and the first chunks, and land before
+      // them.
+      for (int k = w; k * 64 < nchunks * kChunk; k += kS1Waves) {
+        const int32_t e = slot_s[k * 64 + lane];
+        const int32_t sl = umode && e >= 0 ? e & ((1 << SMLA_UNION_ROW_BITS) - 1) : e;
+        dma4(sl >= 0 && k * 64 + lane < nchunks * kChunk ? (const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride
+                                                          : (const char*)kZeroRow,
+             (char*)(scale_s + k * 64));
+      }
+    }
 
     if constexpr (!UNION) {
-      // decode (one segment): q goes out now, followed by chunks 0 and 1; once q has landed
-      // every wave moves its quarter to registers, and the slots it held take the next
-      // chunks (q follows the slots so that the first gathers are not held up by it)
-      copy_q();
+      // decode (one segment): chunks 0 and 1 go out; once q (issued in the prologue) has
+      // landed every wave moves its quarter to registers, and the slots it held take the
+      // next chunks
       for (int ci = 0; ci < 2 && ci < nchunks; ++ci) issue(ci);
       wait_chunks_w<2, kLoadsHi, kLoadsLo>(hi, min(2, nchunks));   // q, issued before them, has landed
       lds_barrier();
