@@ -535,6 +535,51 @@ def time_decode_h128(smla, torch, steps, warmup, T=32, W=2048, n=1 << 20):
             "splits": calls[0].splits}
 
 
+def time_dense_paged(smla, torch, steps, warmup, flush, T=64, lo=32768, hi=65536, page=64):
+    """Dense paged decode (the block-table case, page size 64, length = context) of T tokens with
+    contexts uniform in [lo, hi], bf16, over a page-permuted pool holding exactly their pages: the
+    splits are planned on the device from the lengths. Cold steps (the flush before each)."""
+    rng = np.random.default_rng(64)
+    ctx = rng.integers(lo, hi + 1, size=T).astype(np.int32)
+    npages = -(-ctx // page)
+    width = int(npages.max())
+    total = int(npages.sum())
+    perm = rng.permutation(total).astype(np.int32)
+    table = np.full((T, width), -1, np.int32)
+    off = 0
+    for t in range(T):
+        table[t, :npages[t]] = perm[off:off + npages[t]]
+        off += npages[t]
+    kv = smla.KvCache.empty(smla.SMLA_BF16, total * page, device="cuda", poison=False)
+    kv.storage.normal_(0.0, 0.5)
+    g = torch.Generator(device="cuda").manual_seed(65)
+    q = (torch.randn(T, 64, 576, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, 64), dtype=torch.float32, device="cuda")
+    call = smla.DecodeCall(q, kv, torch.from_numpy(table).cuda(), torch.from_numpy(ctx).cuda(), page, 1 / 16, out, lse)
+    for _ in range(warmup):
+        flush.sum()
+        call()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(steps):
+        flush.sum()
+        ev[k][0].record()
+        call()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    rows = int(ctx.sum())
+    alg = rows * 1152 + T * (73728 + 65536 + 256) + int(npages.sum()) * 4
+    m = float(np.median(ms))
+    del kv
+    torch.cuda.empty_cache()
+    return {"workload": f"dense paged decode, bf16, {T} tokens, contexts U[{lo}, {hi}], page {page}, splits planned on "
+                        f"the device from the lengths; cold (1 GiB read before each step)",
+            "rows": rows, "step_median_us": m * 1e3, "step_p10_us": float(np.percentile(ms, 10)) * 1e3,
+            "step_p90_us": float(np.percentile(ms, 90)) * 1e3, "algorithmic_bytes_step": alg,
+            "hbm_gbs_step": alg / (m / 1e3) / 1e9, "hbm_frac_step": alg / (m / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+
 def prefill_flop_done(enc, lens, G, H):
     """FLOP the grouped-prefill kernel issues: its workgroups each serve 64 / H members of a group
     (64 head slots) and walk the group's union entries that name one of them, 2 * (576 + 512)
@@ -936,6 +981,10 @@ def main():
         del c4
 
     if not args.no_extra:
+        log("timing dense paged decode (64 tokens, contexts 32K-64K)")
+        dp = time_dense_paged(smla, torch, max(5, args.steps // 2), 3, flush)
+        line["dense_paged_decode"] = dp
+        log(f"dense paged: {dp['step_median_us']:.1f} us over {dp['rows']} rows ({dp['hbm_gbs_step']:.0f} GB/s)")
         log("timing 128-head decode (batch 32, top-k 2048)")
         h1 = time_decode_h128(smla, torch, args.steps, args.warmup)
         line["decode_h128"] = h1

@@ -217,8 +217,11 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   // the head of the workspace; a workgroup waits for its block's other splits (at most
   // 10 us) only when the whole grid is resident at once
   plan->sync_bytes = bf16 ? smla::kSyncBytes : 0;
-  plan->fused = bf16 && tv <= smla::kSyncTokens;
-  plan->wait_ticks = (plan->balanced || tv * plan->S <= device_cus()) ? wall_ticks(10) : 0;
+  // A balanced plan whose grid may exceed the device merges in stage 2 instead: its splits
+  // cannot all run at once, and the last arrival of a token with tens of splits would merge
+  // them all by itself.
+  plan->fused = bf16 && tv <= smla::kSyncTokens && !(plan->balanced && items > plan->cus);
+  plan->wait_ticks = tv * plan->S <= plan->cus || (plan->balanced && items <= plan->cus) ? wall_ticks(10) : 0;
   plan->ws_bytes = plan->sync_bytes + (plan->part_o_bytes + plan->part_lse_bytes + 255) / 256 * 256;
   return SMLA_OK;
 }

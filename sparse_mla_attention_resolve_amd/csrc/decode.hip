@@ -190,7 +190,41 @@ constexpr int kAhead = 4;                   // LDS operand reads kept in flight 
 #endif
 constexpr int kPvA = SMLA_PV_IN_A;          // P V tiles of chunk ci computed with the scores of chunk ci + 1
 
-// Workgroup id -> (token, split). Workgroups are dispatched to the 8 XCDs round robin;
+// The balanced plan of a dense paged decode of tv <= 64 virtual tokens (64-head blocks; virtual
+// token v is block v / T of token v % T), computed by one wave from the lengths alone, lane v for
+// token v: rows per split r from the launch's total rows, so that every token's splits fit the
+// compute units at once (at least min_rows, at most kMaxSplitRows, whole chunks); token v gets
+// n = max(1, ceil(len_v / r)) splits, numbered consecutively in token order from base. Stage 1
+// and stage 2 compute the same plan. Returns the total number of splits (wave-uniform).
+struct BalancedPlan {
+  int r, base, n, total;
+};
+__device__ __forceinline__ BalancedPlan balanced_plan(const int32_t* lens, int T, int hblocks, int max_len, int cus,
+                                                      int min_rows, int v) {
+  const int tv = T * hblocks;
+  int ln = 0;
+  if (v < tv) {
+    const int l = lens[v % T];
+    ln = l < 0 ? 0 : (l > max_len ? max_len : l);
+  }
+  int tot = ln;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
+  const int room = cus - tv;                               // splits beyond one per token
+  int r = (tot + room - 1) / room;
+  r = (r + kChunk - 1) / kChunk * kChunk;
+  r = r < min_rows ? min_rows : (r > kMaxSplitRows ? kMaxSplitRows : r);
+  const int n = v < tv ? max(1, (ln + r - 1) / r) : 0;
+  int incl = n;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (v >= o) incl += y;
+  }
+  return BalancedPlan{r, incl - n, n, __shfl(incl, 63, 64)};
+}
+
+// Workgroup id -> (token, split).// Workgroup id -> (token, split). Workgroups are dispatched to the 8 XCDs round robin;
 // when T is a multiple of 8 every split of a token runs on one XCD, so the token's partial
 // results stay in that XCD's L2 for stage 2, which uses the same token -> XCD rule.
 __device__ __forceinline__ void stage1_coords(int b, int T, int S, int& t, int& s) {
@@ -591,42 +625,21 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     // empty token's output); workgroup b takes the b-th split in token order, or leaves past
     // the last. Wave 0 plans, lane v for token v.
     __shared__ int bplan[5];
-    const int tv = a.T * a.hblocks;
     if (threadIdx.x < 64) {
-      const int v = threadIdx.x;
-      int ln = 0;
-      if (v < tv) {
-        const int l = a.lens[v % a.T];
-        ln = l < 0 ? 0 : (l > a.max_len ? a.max_len : l);
-      }
-      int tot = ln;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
-      const int room = a.cus - tv;                         // splits beyond one per token
-      int r = (tot + room - 1) / room;
-      r = (r + kChunk - 1) / kChunk * kChunk;
-      r = r < a.min_rows ? a.min_rows : (r > kMaxSplitRows ? kMaxSplitRows : r);
-      const int n = v < tv ? max(1, (ln + r - 1) / r) : 0;
-      int incl = n;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (v >= o) incl += y;
-      }
-      const int base = incl - n, b = blockIdx.x;
-      const bool mine = v < tv && b >= base && b < base + n;
+      const int v = threadIdx.x, b = blockIdx.x;
+      const BalancedPlan bp = balanced_plan(a.lens, a.T, a.hblocks, a.max_len, a.cus, a.min_rows, v);
+      const bool mine = bp.n > 0 && b >= bp.base && b < bp.base + bp.n;
       const uint64_t m = __ballot(mine);
-      const int total = __shfl(incl, 63, 64);              // splits of all tokens
       if (v == 0) {
         bplan[0] = m ? __builtin_ffsll((long long)m) - 1 : -1;
-        bplan[2] = r;
+        bplan[2] = bp.r;
         // the splits are the launch's first `total` workgroups, dispatched before the ones that
         // leave at once: only when they fit the compute units together may one wait for another
-        bplan[4] = total <= a.cus ? a.wait_ticks : 0;
+        bplan[4] = bp.total <= a.cus ? a.wait_ticks : 0;
       }
       if (mine) {
-        bplan[1] = b - base;
-        bplan[3] = base;
+        bplan[1] = b - bp.base;
+        bplan[3] = bp.base;
       }
     }
     __syncthreads();
@@ -1228,6 +1241,9 @@ struct Stage2Args {
   int64_t lse_tok_stride;
   int32_t out_f32;
   int32_t hblocks;          // packed path: 64-head blocks per token, as in stage 1
+  // packed path: the splits were planned on the device from the lengths (balanced_plan, with
+  // these arguments), as stage 1 did
+  int32_t balanced, min_rows, cus;
 };
 
 // Thread = (token, head, 4 consecutive columns); a workgroup of 256 covers two heads. Every
@@ -1323,9 +1339,25 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2_packed(Stage2Args a)
   const int tr = t % a.T, hbk = t / a.T, hv = min(kHeads, a.H - kHeads * hbk);
   int len = a.lens[tr];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
-  if (len > 0 && len <= a.rows_per_split) return;      // one split: stage 1 wrote the output
-  const int nact = min(a.S, (len + a.rows_per_split - 1) / a.rows_per_split);
-  const int64_t base = (int64_t)t * a.S;
+  int rps = a.rows_per_split, smax = a.S;
+  int64_t base = (int64_t)t * a.S;
+  if (a.balanced) {
+    // the plan stage 1 made from the lengths: this token's rows per split and first partial
+    __shared__ int sp[2];
+    if (threadIdx.x < 64) {
+      const BalancedPlan bp = balanced_plan(a.lens, a.T, a.hblocks, a.max_len, a.cus, a.min_rows, threadIdx.x);
+      if (threadIdx.x == t) {
+        sp[0] = bp.r;
+        sp[1] = bp.base;
+      }
+    }
+    __syncthreads();
+    rps = sp[0];
+    base = sp[1];
+    smax = kMaxSplitRows;
+  }
+  if (len > 0 && len <= rps) return;                   // one split: stage 1 wrote the output
+  const int nact = min(smax, (len + rps - 1) / rps);
   const int64_t off = ((((hq * 2 + x) * 16 + nt) * 4 + g) * 16 + 4 * cq) * 4;   // bf16 elements
   const uint16_t* po = (const uint16_t*)a.part_o;
   float mx[4], wsum[4], acc[4][4];
@@ -1469,6 +1501,9 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   b.lse_tok_stride = d.lse_tok_stride;
   b.out_f32 = d.q_dtype == SMLA_F32;
   b.hblocks = plan.hblocks;
+  b.balanced = plan.balanced;
+  b.min_rows = plan.min_rows;
+  b.cus = plan.cus;
   if (d.q_dtype == SMLA_F32)
     hipLaunchKernelGGL(decode_stage2, dim3(d.T * ((d.H + 1) / 2)), dim3(kS2Threads), 0, stream, b);
   else
