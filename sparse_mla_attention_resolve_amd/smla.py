@@ -143,20 +143,29 @@ def _i32(t: torch.Tensor, name: str):
 
 # ---------------------------------------------------------------------------------- cache
 
+FP8_ALIGNED_ROW_BYTES = 640     # e4m3 codes (0..511) + bf16 rope (512..639): five aligned 128-byte lines
+
+
 class KvCache:
     """A latent KV pool in device memory (torch-allocated) and its smla_kv descriptor.
 
-    bf16 / f32: one [num_slots, 576] tensor. fp8: one packed uint8 [num_slots, 656] tensor
-    holding e4m3 codes (bytes 0..511), bf16 rope (512..639) and the fp32 scale (640..643).
+    bf16 / f32: one [num_slots, 576] tensor.
+    fp8, layout "aligned" (the default): uint8 [num_slots, 640] rows holding the e4m3 codes
+    (bytes 0..511) and the bf16 rope (512..639), each row five whole 128-byte lines, and a
+    separate fp32 [num_slots] scale plane.
+    fp8, layout "packed": one uint8 [num_slots, 656] tensor holding the codes (0..511), the rope
+    (512..639) and the scale (640..643), the SMLA_FP8_ROW_BYTES row of smla.h.
     """
 
-    def __init__(self, dtype: int, num_slots: int, storage: torch.Tensor):
+    def __init__(self, dtype: int, num_slots: int, storage: torch.Tensor, scale_plane: Optional[torch.Tensor] = None):
         self.dtype = dtype
         self.num_slots = num_slots
         self.storage = storage
+        self.scale_plane = scale_plane
 
     @staticmethod
-    def empty(dtype: int, num_slots: int, device="cuda", poison: bool = True) -> "KvCache":
+    def empty(dtype: int, num_slots: int, device="cuda", poison: bool = True, layout: str = "aligned") -> "KvCache":
+        sc = None
         if dtype == SMLA_BF16:
             st = torch.empty((num_slots, ROW), dtype=torch.bfloat16, device=device)
             if poison:
@@ -166,14 +175,22 @@ class KvCache:
             if poison:
                 st.fill_(float("nan"))
         elif dtype == SMLA_FP8_E4M3:
-            st = torch.empty((num_slots, FP8_ROW_BYTES), dtype=torch.uint8, device=device)
+            if layout not in ("aligned", "packed"):
+                raise ValueError(layout)
+            width = FP8_ALIGNED_ROW_BYTES if layout == "aligned" else FP8_ROW_BYTES
+            st = torch.empty((num_slots, width), dtype=torch.uint8, device=device)
+            if layout == "aligned":
+                sc = torch.empty((num_slots,), dtype=torch.float32, device=device)
             if poison:
                 st.fill_(0x7F)                                   # e4m3 NaN codes, NaN rope and scale
                 st[:, FP8_ROPE_OFFSET:FP8_SCALE_OFFSET].view(torch.int16).fill_(0x7FC0)
-                st[:, FP8_SCALE_OFFSET:FP8_SCALE_OFFSET + 4].view(torch.float32).fill_(float("nan"))
+                if sc is None:
+                    st[:, FP8_SCALE_OFFSET:FP8_SCALE_OFFSET + 4].view(torch.float32).fill_(float("nan"))
+                else:
+                    sc.fill_(float("nan"))
         else:
             raise ValueError(dtype)
-        return KvCache(dtype, num_slots, st)
+        return KvCache(dtype, num_slots, st, sc)
 
     def desc(self) -> smla_kv:
         d = smla_kv()
@@ -187,7 +204,10 @@ class KvCache:
             rs = self.storage.stride(0)
             d.lat8, d.lat8_stride = base, rs
             d.rope16, d.rope16_stride = base + FP8_ROPE_OFFSET, rs
-            d.scale, d.scale_stride = base + FP8_SCALE_OFFSET, rs
+            if self.scale_plane is None:
+                d.scale, d.scale_stride = base + FP8_SCALE_OFFSET, rs
+            else:
+                d.scale, d.scale_stride = self.scale_plane.data_ptr(), 4
         return d
 
     # views of the stored planes (for tests and for building inputs)
@@ -198,6 +218,8 @@ class KvCache:
         return self.storage[:, FP8_ROPE_OFFSET:FP8_SCALE_OFFSET].view(torch.int16)
 
     def scale(self):
+        if self.scale_plane is not None:
+            return self.scale_plane
         return self.storage[:, FP8_SCALE_OFFSET:FP8_SCALE_OFFSET + 4].view(torch.float32)[:, 0]
 
 

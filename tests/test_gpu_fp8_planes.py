@@ -44,7 +44,7 @@ class PlanarKv:
 
 
 def _pools(vals, live, ns):
-    packed = smla.KvCache.empty(smla.SMLA_FP8_E4M3, ns)
+    packed = smla.KvCache.empty(smla.SMLA_FP8_E4M3, ns, layout="packed")
     planar = PlanarKv(ns)
     src, sl = _t(vals[live]), _t(live)
     smla.smla_kv_write(src, sl, packed)
