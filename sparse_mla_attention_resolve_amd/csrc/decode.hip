@@ -13,9 +13,10 @@
 // The block table is either resolved slots (page size 1, the virtual block table of
 // The Virtual Block Table: Reusing Triton MLA for Sparse Attention on Blackwell GPUs,
 // "The Breakthrough") or page ids (page size P > 1, the dense paged walk of "The
-// Investigation"). fp8 caches are dequantised in the kernel: e4m3 codes convert to
-// bf16 exactly, the per-row scale multiplies the latent part of the score and the
-// softmax weight that meets the row's values.
+// Investigation"). fp8 caches are dequantised in the kernel: each gathered chunk's e4m3
+// codes convert to bf16 exactly, once per workgroup, into a staging tile that the bf16 MFMA
+// loop reads; the per-row scale multiplies the latent part of the score and the softmax
+// weight that meets the row's values.
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -99,16 +100,15 @@ __device__ __forceinline__ int token_len(const Stage1Args& a, int t) {
 }
 
 // Shared-memory layout of one gathered row: the row's 16-byte units, unit u stored at
-// position u ^ key(row), a permutation inside each aligned block of 8 units. The key spreads
-// the rows that one operand read touches over the 64 LDS banks without padding, so a 32-row
-// chunk is a whole number of 64-lane x 16-byte direct-to-LDS load instructions. Its form
-// depends on the row size; both were chosen with the LDS bank-conflict counter on gfx950:
-//   bf16 (1152-byte rows): key = row & 7, conflict-free for the 16-byte score reads (16
-//     consecutive rows at one unit) and the transposing value reads (rows 4g .. 4g+3 and
-//     16 + 4g .. +3 at two units);
-//   fp8 (640-byte rows): key = 2 ((row >> 1) & 3) + (((row >> 3) ^ (row >> 4)) & 1),
-//     conflict-free for the 8-byte latent score reads and the transposing value reads; the
-//     two 16-byte rotary reads per chunk meet a two-way conflict.
+// position u ^ key(row), a permutation inside each aligned block of 8 units, so that a 32-row
+// chunk is a whole number of 64-lane x 16-byte direct-to-LDS load instructions with no padding.
+//   bf16 (1152-byte rows, the rows the MFMA loop reads): key = row & 7 spreads the rows that
+//     one operand read touches over the 64 LDS banks: the 16-byte score reads (16 consecutive
+//     rows at one unit) and the transposing value reads (rows 4g .. 4g+3 and 16 + 4g .. +3 at
+//     two units) are conflict-free (checked with the LDS bank-conflict counter on gfx950);
+//   fp8 (640-byte rows of codes and rotary values): key = 0. Only the conversion into bf16
+//     rows reads them, 16 consecutive lanes over the 16 units of one row, which meets no
+//     conflict in any order.
 template <int KV>
 struct Lay;
 template <>
@@ -119,13 +119,13 @@ struct Lay<SMLA_BF16> {
 template <>
 struct Lay<SMLA_FP8_E4M3> {
   static constexpr int kUnits = 40;      // 512 e4m3 codes + 64 bf16 rotary values; scales live apart
-  static constexpr int kNBuf = 6;        // 7 queued ~20% more bytes at the start and was ~4% slower
+  static constexpr int kNBuf = 3;        // chunks in the LDS ring, beside two bf16 staging tiles
 };
 
 template <int KV>
 __device__ __forceinline__ int swz_key(int row) {
   if constexpr (KV == SMLA_BF16) return row & 7;
-  else return 2 * ((row >> 1) & 3) + (((row >> 3) ^ (row >> 4)) & 1);
+  else return 0;
 }
 template <int KV>
 __device__ __forceinline__ int swz(int row, int unit) { return unit ^ swz_key<KV>(row); }
@@ -189,6 +189,10 @@ constexpr int kAhead = 4;                   // LDS operand reads kept in flight 
 #define SMLA_PV_IN_A 4
 #endif
 constexpr int kPvA = SMLA_PV_IN_A;          // P V tiles of chunk ci computed with the scores of chunk ci + 1
+#ifndef SMLA_PV_FP8
+#define SMLA_PV_FP8 4
+#endif
+constexpr int kPvF = SMLA_PV_FP8;           // fp8: P V tiles of chunk ci computed while chunk ci + 1 is converted
 
 // The balanced plan of a dense paged decode of tv <= 64 virtual tokens (64-head blocks; virtual
 // token v is block v / T of token v % T), computed by one wave from the lengths alone, lane v for
@@ -224,7 +228,7 @@ __device__ __forceinline__ BalancedPlan balanced_plan(const int32_t* lens, int T
   return BalancedPlan{r, incl - n, n, __shfl(incl, 63, 64)};
 }
 
-// Workgroup id -> (token, split).// Workgroup id -> (token, split). Workgroups are dispatched to the 8 XCDs round robin;
+// Workgroup id -> (token, split). Workgroups are dispatched to the 8 XCDs round robin;
 // when T is a multiple of 8 every split of a token runs on one XCD, so the token's partial
 // results stay in that XCD's L2 for stage 2, which uses the same token -> XCD rule.
 __device__ __forceinline__ void stage1_coords(int b, int T, int S, int& t, int& s) {
@@ -262,93 +266,59 @@ __device__ __forceinline__ void wait_chunks_w(bool hi, int chunks) {
 }
 
 
-// Per-lane LDS byte offsets of wave (hq, x)'s operand reads (the same for every chunk).
-//   ka[m]: score operand A = K[chunk row 16x + c][dims 32ks + 8g .. +7]
-//     bf16: unit 4ks + g sits at 4(ks ^ (key >> 2)) + (g ^ (key & 3)): base m = ks & 1, plus 64 ks
-//     fp8:  8 bytes at unit 2ks + g/2, stored at 8(ks >> 2) + 2((ks & 3) ^ (key >> 1)) +
-//           ((g >> 1) ^ (key & 1)), + 8(g & 1): base m = ks & 3, plus 128 (ks >> 2)
-//   vo[m]: P V operand B = V[rows 4g .. 4g+3, then 16 + 4g .. +3][column c of tile 16x + nt]
-//     bf16: two transposed 16-bit reads (j = 0, 1); the group's lane c points at row
-//           16j + 4g + c/4, columns 16(16x + nt) + 4(c%4) .. +3: unit 32x + 2nt + (c%4)/2,
-//           stored at 32x + 8(nt >> 2) + 2((nt & 3) ^ (key >> 1)) + (((c%4)/2) ^ (key & 1)):
-//           base vo[4j + (nt & 3)], plus 128 (nt >> 2)
-//     fp8:  one transposed 8-bit read; lane c of the group points at row R(c/2), columns
-//           16(16x + nt) + 8(c%2) .. +7, with R(i) = 4g + i for i < 4 and 16 + 4g + i - 4
-//           after: unit 16x + nt, stored at 16x + 8(nt >> 3) + ((nt & 7) ^ key): base
-//           vo[nt & 7], plus 128 (nt >> 3)
-template <int KV>
+// Per-lane LDS byte offsets of wave (hq, x)'s operand reads in a chunk of bf16 rows (the same
+// for every chunk; fp8 chunks are dequantised into bf16 rows before the loop reads them).
+//   ka[m]: score operand A = K[chunk row 16x + c][dims 32ks + 8g .. +7]: unit 4ks + g sits at
+//          4(ks ^ (key >> 2)) + (g ^ (key & 3)): base m = ks & 1, plus 64 ks
+//   vo[m]: P V operand B = V[rows 4g .. 4g+3, then 16 + 4g .. +3][column c of tile 16x + nt],
+//          two transposed 16-bit reads (j = 0, 1); the group's lane c points at row
+//          16j + 4g + c/4, columns 16(16x + nt) + 4(c%4) .. +3: unit 32x + 2nt + (c%4)/2,
+//          stored at 32x + 8(nt >> 2) + 2((nt & 3) ^ (key >> 1)) + (((c%4)/2) ^ (key & 1)):
+//          base vo[4j + (nt & 3)], plus 128 (nt >> 2)
 struct Offsets {
-  int ka[4];
+  int ka[2];
   int vo[8];
   __device__ __forceinline__ Offsets(int x, int g, int c) {
-    constexpr int kRowBytes = Lay<KV>::kUnits * 16;
-    const int row = 16 * x + c, key = swz_key<KV>(row);
-    if constexpr (KV == SMLA_BF16) {
-      const int kh = (key >> 2) * 64;
-      ka[0] = row * kRowBytes + 16 * (g ^ (key & 3)) + kh;
-      ka[1] = row * kRowBytes + 16 * (g ^ (key & 3)) - kh;
-      ka[2] = ka[3] = 0;
-      const int b = (c & 3) >> 1;
+    constexpr int kRowBytes = Lay<SMLA_BF16>::kUnits * 16;
+    const int row = 16 * x + c, key = swz_key<SMLA_BF16>(row);
+    const int kh = (key >> 2) * 64;
+    ka[0] = row * kRowBytes + 16 * (g ^ (key & 3)) + kh;
+    ka[1] = row * kRowBytes + 16 * (g ^ (key & 3)) - kh;
+    const int b = (c & 3) >> 1;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = 16 * j + 4 * g + (c >> 2), k2 = swz_key<KV>(r);
+    for (int j = 0; j < 2; ++j) {
+      const int r = 16 * j + 4 * g + (c >> 2), k2 = swz_key<SMLA_BF16>(r);
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          vo[4 * j + m] = r * kRowBytes + 512 * x + 32 * (m ^ (k2 >> 1)) + 16 * (b ^ (k2 & 1)) + 8 * (c & 1);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) ka[m] = row * kRowBytes + 32 * (m ^ (key >> 1)) + 16 * ((g >> 1) ^ (key & 1)) + 8 * (g & 1);
-      const int i = c >> 1;
-      const int r = i < 4 ? 4 * g + i : 16 + 4 * g + i - 4, k2 = swz_key<KV>(r);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) vo[m] = r * kRowBytes + 256 * x + 16 * (m ^ k2) + 8 * (c & 1);
+      for (int m = 0; m < 4; ++m)
+        vo[4 * j + m] = r * kRowBytes + 512 * x + 32 * (m ^ (k2 >> 1)) + 16 * (b ^ (k2 & 1)) + 8 * (c & 1);
     }
   }
 };
 
-// One step of wave (hq, x): the scores of one chunk's rows 16x .. 16x+15 (S^T tile: lane
-// (g, c) gets rows 16x + 4g + v of head 16hq + c; 18 MFMAs on two accumulator chains)
-// and / or O += P V over another chunk's columns 256x .. 256x+255 (16 MFMAs, one per
-// 16-column tile), interleaved so that the matrix unit always has independent work while
-// the operand reads run kAhead steps ahead. sl receives the latent part of the scores, sr
-// the rotary part (fp8 only; bf16 sums both into sl). after_step(k) runs after step k's
-// MFMAs are issued (the caller spreads its gathers of a later chunk over the steps).
-template <int KV, bool DO_S, bool DO_PV, typename Hook, int PV0 = 0, int PV1 = 16>
-__device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, const Offsets<KV>& off, int x, int g,
-                                           int c, const bf16x8 (&qf)[kQLoads], f32x4& sl, f32x4& sr,
-                                           const bf16x8& pa, f32x4 (&oacc)[16], Hook&& after_step) {
-  constexpr bool kFp8 = KV == SMLA_FP8_E4M3;
-  constexpr int kRowBytes = Lay<KV>::kUnits * 16;
+// One step of wave (hq, x) over chunks of bf16 rows: the scores of one chunk's rows
+// 16x .. 16x+15 (S^T tile: lane (g, c) gets rows 16x + 4g + v of head 16hq + c; 18 MFMAs on two
+// accumulator chains) and / or O += P V over another chunk's columns 256x .. 256x+255 (16 MFMAs,
+// one per 16-column tile), interleaved so that the matrix unit always has independent work
+// while the operand reads run kAhead steps ahead. With ROPE_APART the scores' latent part
+// (dims 0 .. 511) goes to sl and the rotary part to sr (an fp8 cache scales the latent part
+// alone); otherwise sl holds both. after_step(k) runs after step k's MFMAs are issued (the
+// caller spreads its gathers of a later chunk over the steps).
+template <bool DO_S, bool DO_PV, bool ROPE_APART, typename Hook, int PV0 = 0, int PV1 = 16>
+__device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, const Offsets& off,
+                                           const bf16x8 (&qf)[kQLoads], f32x4& sl, f32x4& sr, const bf16x8& pa,
+                                           f32x4 (&oacc)[16], Hook&& after_step) {
   // P V tiles PV0 .. PV1 - 1 (at steps 0 .. PV1 - PV0 - 1)
   constexpr int kNPV = DO_PV ? PV1 - PV0 : 0;
   constexpr int kSteps = DO_S ? 18 : kNPV;
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  f32x4 racc = f32x4{0.f, 0.f, 0.f, 0.f};
-  // score step ks: bf16 k steps 0 .. 17; fp8 latent k steps 0 .. 15, then rotary 16, 17
-  auto kread = [&](int ks) -> uint4 {
-    if constexpr (!kFp8) {
-      return *(const uint4*)(kbS + off.ka[ks & 1] + 64 * ks);
-    } else if (ks < 16) {
-      const uint2 v = *(const uint2*)(kbS + off.ka[ks & 3] + 128 * (ks >> 2));
-      return make_uint4(v.x, v.y, 0u, 0u);
-    } else {
-      const int row = 16 * x + c;
-      return *(const uint4*)(kbS + row * kRowBytes + swz<KV>(row, 32 + (ks - 16) * 4 + g) * 16);
-    }
-  };
+  f32x4 acc[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                  f32x4{0.f, 0.f, 0.f, 0.f}};
+  auto kread = [&](int ks) -> uint4 { return *(const uint4*)(kbS + off.ka[ks & 1] + 64 * ks); };
   auto vread = [&](int nt) -> uint4 {
-    if constexpr (!kFp8) {
-      const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(kbV + off.vo[nt & 3] + 128 * (nt >> 2)));
-      const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(kbV + off.vo[4 + (nt & 3)] + 128 * (nt >> 2)));
-      return __builtin_bit_cast(uint4, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-    } else {
-      const i32x2 a = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (__attribute__((address_space(3))) i32x2*)(kbV + off.vo[nt & 7] + 128 * (nt >> 3)));
-      return make_uint4((uint32_t)a[0], (uint32_t)a[1], 0u, 0u);
-    }
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(kbV + off.vo[nt & 3] + 128 * (nt >> 2)));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(kbV + off.vo[4 + (nt & 3)] + 128 * (nt >> 2)));
+    return __builtin_bit_cast(uint4, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   uint4 kq[kAhead + 1], vq[kAhead + 1];
 #pragma unroll
@@ -360,21 +330,13 @@ __device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, con
   for (int k = 0; k < kSteps; ++k) {
     if constexpr (DO_S) {
       if (k + kAhead < 18) kq[(k + kAhead) % (kAhead + 1)] = kread(k + kAhead);
-      const uint4 kv = kq[k % (kAhead + 1)];
-      if constexpr (!kFp8) {
-        acc[k & 1] = mfma16x16x32(as_bf16x8(kv), qf[k], acc[k & 1]);
-      } else if (k < 16) {
-        acc[k & 1] = mfma16x16x32(e4m3x8_to_bf16x8(kv.x, kv.y), qf[k], acc[k & 1]);
-      } else {
-        racc = mfma16x16x32(as_bf16x8(kv), qf[k], racc);
-      }
+      const int ai = (ROPE_APART && k >= 16 ? 2 : 0) + (k & 1);
+      acc[ai] = mfma16x16x32(as_bf16x8(kq[k % (kAhead + 1)]), qf[k], acc[ai]);
     }
     if constexpr (DO_PV) {
       if (k < kNPV) {
         if (k + kAhead < kNPV) vq[(k + kAhead) % (kAhead + 1)] = vread(PV0 + k + kAhead);
-        const uint4 vv = vq[k % (kAhead + 1)];
-        const bf16x8 b = kFp8 ? e4m3x8_to_bf16x8(vv.x, vv.y) : as_bf16x8(vv);
-        oacc[PV0 + k] = mfma16x16x32(pa, b, oacc[PV0 + k]);
+        oacc[PV0 + k] = mfma16x16x32(pa, as_bf16x8(vq[k % (kAhead + 1)]), oacc[PV0 + k]);
       }
     }
     after_step(k);
@@ -382,7 +344,7 @@ __device__ __forceinline__ void chunk_step(const char* kbS, const char* kbV, con
   }
   if constexpr (DO_S) {
     sl = acc[0] + acc[1];
-    sr = racc;
+    if constexpr (ROPE_APART) sr = acc[2] + acc[3];
   }
 }
 
@@ -607,6 +569,9 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   constexpr int kNBuf = L::kNBuf;
   constexpr bool kFp8 = KV == SMLA_FP8_E4M3;
   __shared__ __attribute__((aligned(16))) char kvbuf[kNBuf][kChunkBytes];
+  // fp8: each chunk's rows converted to bf16 rows (the layout of a bf16 chunk), two chunks
+  constexpr int kStgBytes = kChunk * Lay<SMLA_BF16>::kUnits * 16;
+  __shared__ __attribute__((aligned(16))) char stg[kFp8 ? 2 : 1][kFp8 ? kStgBytes : 16];
   __shared__ __attribute__((aligned(16))) int32_t slot_s[kMaxSplitRows];
   __shared__ int32_t page_s[kMaxSplitRows / 2 + 64];     // page ids of a split (page size >= 2)
   __shared__ __attribute__((aligned(16))) float scale_s[kFp8 ? kMaxSplitRows : 4];
@@ -701,14 +666,16 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int32_t* trow = a.table + (int64_t)trow_id * a.table_stride;
   const int e0 = r0 >> lp;
   const int n_ent = lp == 0 ? min(rps, a.max_len - r0) : min((r0 + rps - 1) >> lp, a.table_width - 1) - e0 + 1;
-  static_assert((kNBuf - 2) * kChunkBytes >= 4 * kQLoads * 1024, "q must fit the ring slots from 2 on");
-  char* const qlds = kvbuf[2] + hq * (kQLoads * 1024);
+  // q's staging: bf16, ring slots 2 ..; fp8, the two staging tiles
+  static_assert(kFp8 ? 2 * kStgBytes >= 4 * kQLoads * 1024 : (kNBuf - 2) * kChunkBytes >= 4 * kQLoads * 1024,
+                "q must fit its staging");
+  char* const qlds = (kFp8 ? stg[0] : kvbuf[2]) + hq * (kQLoads * 1024);
   int32_t* const prow_lds = (int32_t*)kvbuf[1];
   const bool row_in_lds = a.map_pt_width <= kChunkBytes / 4;
   int32_t req = -1, seq = 0;
   // q, in the order the lanes read it back (head quarter hq: piece ks of lane (g, c) = head
-  // 16hq + c, dims 32ks + 8g .. +7) into ring slots 2.. (wave (hq, x) copies pieces 9x ..
-  // 9x+8 of quarter hq)
+  // 16hq + c, dims 32ks + 8g .. +7) into its staging (wave (hq, x) copies pieces 9x .. 9x+8
+  // of quarter hq)
   auto copy_q = [&]() {
     const int qt = min(tok_of(h0 + c), a.T - 1);       // a short group repeats its last query
     const uint16_t* qh = a.q + (int64_t)qt * a.q_tok_stride + (int64_t)head_of(h0 + c) * a.q_head_stride + 8 * g;
@@ -830,7 +797,52 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   };
   auto no_hook = [](int) {};
 
-  const Offsets<KV> off(x, g, c);
+  // fp8: chunk ci's rows converted to bf16 rows into staging tile ci % 2, exactly (every e4m3
+  // value is a bf16 value; the row scale is applied to the scores and the weights instead).
+  // Thread (r, j) = (tid / 16, tid % 16) converts latent units j and 16 + j of row r (16 codes
+  // each) into bf16 units 2j, 2j + 1 and 32 + 2j, 33 + 2j (stored at their swizzled positions);
+  // lanes j >= 8 write their two units in the other order, so that each 16-lane group of a
+  // store covers the 16 bank groups once. Threads 0 .. 255 copy the rotary units (row
+  // tid / 8, unit tid % 8: bf16 already). In three parts, so that the loop can place them
+  // between MFMAs: 0 reads, 1 and 2 convert and write.
+  uint4 su[2], srp;
+  auto stage_part = [&](int ci, int part) {
+    if constexpr (kFp8) {
+      const int r = tid >> 4, j = tid & 15, e = j >> 3, rr = tid >> 3;
+      if (part == 0) {
+        const char* src = kvbuf[ci % kNBuf];
+        su[0] = *(const uint4*)(src + r * kRowBytes + 16 * swz<SMLA_FP8_E4M3>(r, j));
+        su[1] = *(const uint4*)(src + r * kRowBytes + 16 * swz<SMLA_FP8_E4M3>(r, 16 + j));
+        if (tid < 256) srp = *(const uint4*)(src + rr * kRowBytes + 16 * swz<SMLA_FP8_E4M3>(rr, 32 + (tid & 7)));
+      } else {
+        char* dst = stg[ci & 1];
+        const uint4 u = su[part - 1];
+        const int b = 32 * (part - 1), kb = swz_key<SMLA_BF16>(r);
+        auto put = [&](int unit, uint32_t w0, uint32_t w1) {
+          *(bf16x8*)(dst + r * (kStgBytes / kChunk) + 16 * (unit ^ kb)) = e4m3x8_to_bf16x8(w0, w1);
+        };
+        put(b + 2 * j + e, e ? u.z : u.x, e ? u.w : u.y);
+        put(b + 2 * j + 1 - e, e ? u.x : u.z, e ? u.y : u.w);
+        if (part == 2 && tid < 256)
+          *(uint4*)(dst + rr * (kStgBytes / kChunk) + 16 * swz<SMLA_BF16>(rr, 64 + (tid & 7))) = srp;
+      }
+    }
+  };
+  auto stage = [&](int ci) {
+    stage_part(ci, 0);
+    stage_part(ci, 1);
+    stage_part(ci, 2);
+  };
+  // the rows the loop reads: bf16, the ring; fp8, the staging tiles
+  auto rows_of = [&](int ci) -> const char* { return kFp8 ? stg[ci & 1] : kvbuf[ci % kNBuf]; };
+
+  const Offsets off(x, g, c);
+  // P V tiles of chunk ci in iteration ci: fp8, tiles 0 .. kPv0 - 1 while chunk ci + 1 is
+  // converted, then (both) tiles kPv0 .. kPvS - 1 with the scores of chunk ci + 1, the rest
+  // with its softmax
+  constexpr int kPv0 = kFp8 ? kPvF : 0;
+  constexpr int kPvS = kFp8 ? kPvF : kPvA;
+  static_assert(!kFp8 || kPv0 >= 3, "the conversion takes three steps");
   f32x4 oacc[16];
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1063,27 +1075,44 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       }
     }
 
-    if constexpr (!UNION) {
-      // decode (one segment): chunks 0 and 1 go out; once q (issued in the prologue) has
-      // landed every wave moves its quarter to registers, and the slots it held take the
-      // next chunks
-      for (int ci = 0; ci < 2 && ci < nchunks; ++ci) issue(ci);
-      wait_chunks_w<2, kLoadsHi, kLoadsLo>(hi, min(2, nchunks));   // q, issued before them, has landed
+    if constexpr (kFp8) {
+      // the ring's chunks go out; once chunk 0 (and q and the scales, issued before it) has
+      // landed, decode moves q to registers, and chunk 0 is converted into staging tile 0,
+      // whose ring slot then takes chunk kNBuf
+      for (int ci = 0; ci < kNBuf && ci < nchunks; ++ci) issue(ci);
+      wait_chunks_w<kNBuf - 1, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 1, nchunks - 1));
       lds_barrier();
+      if constexpr (!UNION) {
 #pragma unroll
-      for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
+        for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
+        lds_barrier();
+      }
+      if (nchunks == 0) continue;
+      stage(0);
       lds_barrier();
-      for (int ci = 2; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+      if (kNBuf < nchunks) issue(kNBuf);
     } else {
-      for (int ci = 0; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+      if constexpr (!UNION) {
+        // decode (one segment): chunks 0 and 1 go out; once q (issued in the prologue) has
+        // landed every wave moves its quarter to registers, and the slots it held take the
+        // next chunks
+        for (int ci = 0; ci < 2 && ci < nchunks; ++ci) issue(ci);
+        wait_chunks_w<2, kLoadsHi, kLoadsLo>(hi, min(2, nchunks));   // q, issued before them, has landed
+        lds_barrier();
+#pragma unroll
+        for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
+        lds_barrier();
+        for (int ci = 2; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+      } else {
+        for (int ci = 0; ci < kNBuf - 1 && ci < nchunks; ++ci) issue(ci);
+      }
+      if (nchunks == 0) continue;
+      wait_chunks_w<kNBuf - 2, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 2, nchunks - 1));
+      lds_barrier();
     }
-    if (nchunks == 0) continue;
-
 
     // scores and weights of chunk 0
-    wait_chunks_w<kNBuf - 2, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 2, nchunks - 1));
-    lds_barrier();
-    chunk_step<KV, true, false>(kvbuf[0], kvbuf[0], off, x, g, c, qf, sl, sr, pa, oacc, no_hook);
+    chunk_step<true, false, kFp8>(rows_of(0), rows_of(0), off, qf, sl, sr, pa, oacc, no_hook);
     publish(0);
     lds_barrier();
 #pragma unroll
@@ -1091,32 +1120,48 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     finish();
 
     // iteration ci, in two phases between three barriers: the scores of chunk ci + 1 (phase
-    // A, with the gathers of chunk ci + kNBuf - 1 spread over its MFMAs), the exchange of
-    // score tiles, then O += P V over chunk ci with the softmax of chunk ci + 1 in between
-    // (phase C). The barrier at the top publishes chunk ci + 1 and tells that every wave is
-    // done with the ring slot of chunk ci - 1, which the iteration refills.
+    // A, with the gathers of a later chunk spread over its MFMAs), the exchange of score
+    // tiles, then O += P V over chunk ci with the softmax of chunk ci + 1 in between (phase C).
+    // bf16: the barrier at the top publishes chunk ci + 1 and tells that every wave is done
+    // with the ring slot of chunk ci - 1, which the iteration refills with chunk ci + kNBuf - 1.
+    // fp8: the barrier at the top publishes chunk ci + 1 and frees the staging tile of chunk
+    // ci - 1; chunk ci + 1 is converted into it between the first kPv0 P V MFMAs of chunk ci,
+    // and after a second barrier its ring slot takes chunk ci + 1 + kNBuf. (The conversion
+    // costs about 0.5 us per chunk of LDS and VALU work whether it runs between MFMAs or
+    // alone; it replaces a conversion of each MFMA operand, repeated by the four waves that
+    // share a row, which was slower.)
     for (int ci = 0; ci + 1 < nchunks; ++ci) {
-      wait_chunks_w<kNBuf - 3, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 3, nchunks - 2 - ci));
-      lds_barrier();
+      if constexpr (kFp8) {
+        wait_chunks_w<kNBuf - 1, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 1, nchunks - 2 - ci));
+        lds_barrier();
+        auto conv = [&](int k) {
+          if (k == 0) stage_part(ci + 1, 0);
+          else if (k >= kPv0 - 2) stage_part(ci + 1, k - kPv0 + 3);
+        };
+        chunk_step<false, true, true, decltype((conv)), 0, kPv0>(rows_of(ci), rows_of(ci), off, qf, sl, sr, pa, oacc, conv);
+        lds_barrier();
+      } else {
+        wait_chunks_w<kNBuf - 3, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 3, nchunks - 2 - ci));
+        lds_barrier();
+      }
       // a copy instruction can wait for room in the compute unit's memory queue: one at a
       // time among the MFMAs, the matrix unit keeps busy meanwhile
-      const int cn = ci + kNBuf - 1;
+      const int cn = kFp8 ? ci + 1 + kNBuf : ci + kNBuf - 1;
       const bool refill = cn < nchunks;
       const Copies cp = src_of(refill ? cn : ci);   // (ci: a valid chunk whose slots go unused)
       auto gathers = [&](int k) {
         if (refill && (k & 3) == 1 && (k >> 2) < kLoadsHi) fire(cp, cn, k >> 2);
       };
-      chunk_step<KV, true, (kPvA > 0), decltype((gathers)), 0, kPvA>(kvbuf[(ci + 1) % kNBuf], kvbuf[ci % kNBuf], off, x,
-                                                                    g, c, qf, sl, sr, pa, oacc, gathers);
+      chunk_step<true, (kPvS > kPv0), kFp8, decltype((gathers)), kPv0, kPvS>(rows_of(ci + 1), rows_of(ci), off, qf, sl, sr,
+                                                                            pa, oacc, gathers);
       publish(ci + 1);
       lds_barrier();
       auto pieces = [&](int k) { piece(ci + 1, k); };
-      chunk_step<KV, false, true, decltype((pieces)), kPvA, 16>(kvbuf[ci % kNBuf], kvbuf[ci % kNBuf], off, x, g, c, qf, sl,
-                                                              sr, pa, oacc, pieces);
+      chunk_step<false, true, kFp8, decltype((pieces)), kPvS, 16>(rows_of(ci), rows_of(ci), off, qf, sl, sr, pa, oacc,
+                                                                 pieces);
       finish();
     }
-    chunk_step<KV, false, true>(kvbuf[(nchunks - 1) % kNBuf], kvbuf[(nchunks - 1) % kNBuf], off, x, g, c, qf, sl, sr,
-                                pa, oacc, no_hook);
+    chunk_step<false, true, kFp8>(rows_of(nchunks - 1), rows_of(nchunks - 1), off, qf, sl, sr, pa, oacc, no_hook);
   }
 
   // ---- normalise. A token whose rows fit one split is finished here; the others leave
