@@ -18,9 +18,14 @@ Prints exactly one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import csv
 import gc
+import hashlib
 import json
 import os
+import re
+import statistics
 import sys
 import time
 
@@ -35,6 +40,26 @@ HBM_PEAK_GBS = 8000.0
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+@contextlib.contextmanager
+def section(torch, name):
+    """A named range in the marker trace of a profiler (torch's NVTX ranges are roctx ranges on
+    ROCm; rocprofv3 --marker-trace records them), with the device drained on both sides so that
+    the range holds exactly the kernels launched inside it. --summarize-profile trace labels
+    each dispatch with its innermost "workload:" and "form:" ranges."""
+    torch.cuda.synchronize()
+    pushed = True
+    try:
+        torch.cuda.nvtx.range_push(name)
+    except Exception:                      # no marker library: the ranges are only labels
+        pushed = False
+    try:
+        yield
+    finally:
+        torch.cuda.synchronize()
+        if pushed:
+            torch.cuda.nvtx.range_pop()
 
 
 KERNEL_SOURCES = ["sparse_mla_attention_resolve_amd/csrc/decode.hip", "sparse_mla_attention_resolve_amd/csrc/smla_device.h",
@@ -283,13 +308,13 @@ def time_decode(c, smla, torch, steps, warmup, flush):
     def step():
         fused()
 
-    for _ in range(warmup):
-        flush.sum()
-        step()
-        flush.sum()
-        resolve()
-        call()
-    torch.cuda.synchronize()
+    with section(torch, "form: warm-up"):
+        for _ in range(warmup):
+            flush.sum()
+            step()
+            flush.sum()
+            resolve()
+            call()
 
     # cold steps: the flush runs between steps, outside the events, on the same stream as the
     # decode kernel, so the event pair brackets exactly its one launch. Python's collector is
@@ -298,24 +323,26 @@ def time_decode(c, smla, torch, steps, warmup, flush):
     ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     gc.disable()
-    wall0 = time.perf_counter()
-    for k in range(steps):
-        flush.sum()                       # reads 1 GiB: evicts the caches, leaves nothing dirty
-        e = evs[k]
-        e[0].record()
-        step()
-        e[1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    for k in range(steps):
-        flush.sum()
-        e = ev2[k]
-        e[0].record()
-        resolve()
-        e[1].record()
-        call()
-        e[2].record()
-    torch.cuda.synchronize()
+    with section(torch, "form: fused, cold (isolated launches)"):
+        wall0 = time.perf_counter()
+        for k in range(steps):
+            flush.sum()                       # reads 1 GiB: evicts the caches, leaves nothing dirty
+            e = evs[k]
+            e[0].record()
+            step()
+            e[1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+    with section(torch, "form: two kernels, cold (resolve, then decode over slots)"):
+        for k in range(steps):
+            flush.sum()
+            e = ev2[k]
+            e[0].record()
+            resolve()
+            e[1].record()
+            call()
+            e[2].record()
+        torch.cuda.synchronize()
     gc.enable()
     step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     two = {"step_ms": np.array([e[0].elapsed_time(e[2]) for e in ev2]),
@@ -324,33 +351,36 @@ def time_decode(c, smla, torch, steps, warmup, flush):
 
     # the headline form: `steps` steps back to back over the rotating batches, one pair of events
     # around all of them (a barrier and a device synchronise on both sides)
-    for k in range(warmup):
-        rot[k % BATCHES]()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for k in range(steps):
-        rot[k % BATCHES]()
-    e1.record()
-    torch.cuda.synchronize()
+    with section(torch, "form: warm-up"):
+        for k in range(warmup):
+            rot[k % BATCHES]()
+    with section(torch, "form: fused, back to back over rotating batches (the headline)"):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(steps):
+            rot[k % BATCHES]()
+        e1.record()
+        torch.cuda.synchronize()
     stream_ms = e0.elapsed_time(e1) / steps
     # the same back-to-back loop again with an event after every step, for the spread of the
     # per-step times (the events sit between launches, so this run is reported beside the first)
-    evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    evb[0].record()
-    for k in range(steps):
-        rot[k % BATCHES]()
-        evb[k + 1].record()
-    torch.cuda.synchronize()
+    with section(torch, "form: fused, back to back, an event after every step"):
+        evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evb[0].record()
+        for k in range(steps):
+            rot[k % BATCHES]()
+            evb[k + 1].record()
+        torch.cuda.synchronize()
     per_step_ms = np.array([evb[k].elapsed_time(evb[k + 1]) for k in range(steps)])
 
     # warm steps: back to back, no flush
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
+    with section(torch, "form: fused, warm (one batch, back to back)"):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
     warm_ms = e0.elapsed_time(e1) / steps
 
     # GRAPH_STEPS steps back to back captured in one HIP graph and replayed (warm): a layer
@@ -368,11 +398,12 @@ def time_decode(c, smla, torch, steps, warmup, flush):
                 step()
         g.replay()
         torch.cuda.synchronize()
-        e0.record()
-        for _ in range(steps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
+        with section(torch, "form: fused, graph replay (warm)"):
+            e0.record()
+            for _ in range(steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
         graph_ms = e0.elapsed_time(e1) / (steps * GRAPH_STEPS)
     except Exception as ex:  # graph capture is a report-only extra
         log(f"graph capture skipped: {ex}")
@@ -412,17 +443,18 @@ def time_ragged(c, smla, torch, steps, warmup, flush):
         fs()
         fd()
 
-    for _ in range(warmup):
-        flush.sum()
-        step()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for k in range(steps):
-        flush.sum()
-        ev[k][0].record()
-        step()
-        ev[k][1].record()
-    torch.cuda.synchronize()
+    with section(torch, "form: warm-up"):
+        for _ in range(warmup):
+            flush.sum()
+            step()
+    with section(torch, "form: cold (isolated steps)"):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for k in range(steps):
+            flush.sum()
+            ev[k][0].record()
+            step()
+            ev[k][1].record()
+        torch.cuda.synchronize()
     ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     rows = int(c.valid[sparse].sum()) + int(lay.ctx[c.tok_req[dense]].sum())
     alg = rows * 1152 + T * (73728 + 65536 + 256 + 8192)
@@ -446,15 +478,16 @@ def time_kv_write(smla, torch, steps, warmup, flush, rows=1 << 20):
     res = {"workload": f"{rows} bf16 rows of 576, slots in 64-slot pages dealt in random order"}
     for name, code, row_out in (("bf16", smla.SMLA_BF16, 1152), ("fp8", smla.SMLA_FP8_E4M3, 644)):
         kv = smla.KvCache.empty(code, rows, device="cuda", poison=False)
-        for _ in range(warmup):
-            smla.smla_kv_write(src, smap, kv)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-        for k in range(steps):
-            flush.sum()
-            ev[k][0].record()
-            smla.smla_kv_write(src, smap, kv)
-            ev[k][1].record()
-        torch.cuda.synchronize()
+        with section(torch, f"form: {name} pool"):
+            for _ in range(warmup):
+                smla.smla_kv_write(src, smap, kv)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+            for k in range(steps):
+                flush.sum()
+                ev[k][0].record()
+                smla.smla_kv_write(src, smap, kv)
+                ev[k][1].record()
+            torch.cuda.synchronize()
         ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))   # median: a first touch can stall one step
         alg = rows * (1152 + 4 + row_out)                  # source row + slot index + stored payload
         res[name] = {"us": ms * 1e3, "algorithmic_bytes": alg, "hbm_gbs": alg / (ms / 1e3) / 1e9,
@@ -488,8 +521,10 @@ def gather_ceiling(torch, flush, steps, rows=1 << 16, pool_rows=1 << 20):
         torch.cuda.synchronize()
         return float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
 
-    tg = cold(lambda: torch.index_select(pool, 0, idx, out=out))
-    tc = cold(lambda: dst.copy_(src))
+    with section(torch, "form: index_select of random rows"):
+        tg = cold(lambda: torch.index_select(pool, 0, idx, out=out))
+    with section(torch, "form: 1 GiB copy"):
+        tc = cold(lambda: dst.copy_(src))
     gb = 2 * rows * 1152
     res = {"what": "torch kernels on this GPU, cold, median: index_select of 65,536 random 1,152-byte rows of a 2^20-row "
                    "pool (read + write), and a 1 GiB device copy (read + write); context for the HBM fractions, "
@@ -515,15 +550,16 @@ def time_decode_h128(smla, torch, steps, warmup, T=32, W=2048, n=1 << 20):
               for _ in range(BATCHES)]
     calls = [smla.DecodeCall(q, kv, tables[0], lens, 1, 1 / 16, out, lse)]
     calls += [smla.DecodeCall(q, kv, tb, lens, 1, 1 / 16, out, lse, workspace=calls[0].workspace) for tb in tables[1:]]
-    for k in range(warmup):
-        calls[k % BATCHES]()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for k in range(steps):
-        calls[k % BATCHES]()
-    e1.record()
-    torch.cuda.synchronize()
+    with section(torch, "form: warm-up"):
+        for k in range(warmup):
+            calls[k % BATCHES]()
+    with section(torch, "form: back to back over rotating batches"):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(steps):
+            calls[k % BATCHES]()
+        e1.record()
+        torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     alg = T * W * 1152 + T * 128 * (576 + 512) * 2 + T * 128 * 4 + T * W * 4
     del kv, tables
@@ -557,16 +593,18 @@ def time_dense_paged(smla, torch, steps, warmup, flush, T=64, lo=32768, hi=65536
     out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((T, 64), dtype=torch.float32, device="cuda")
     call = smla.DecodeCall(q, kv, torch.from_numpy(table).cuda(), torch.from_numpy(ctx).cuda(), page, 1 / 16, out, lse)
-    for _ in range(warmup):
-        flush.sum()
-        call()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for k in range(steps):
-        flush.sum()
-        ev[k][0].record()
-        call()
-        ev[k][1].record()
-    torch.cuda.synchronize()
+    with section(torch, "form: warm-up"):
+        for _ in range(warmup):
+            flush.sum()
+            call()
+    with section(torch, "form: cold (isolated launches)"):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for k in range(steps):
+            flush.sum()
+            ev[k][0].record()
+            call()
+            ev[k][1].record()
+        torch.cuda.synchronize()
     ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     rows = int(ctx.sum())
     alg = rows * 1152 + T * (73728 + 65536 + 256) + int(npages.sum()) * 4
@@ -628,20 +666,21 @@ def time_prefill(c, smla, torch, steps, warmup, flush, cpu_seconds, kv_dtype="bf
     def prefill():
         smla.smla_grouped_prefill(q, kv, enc, lens, c.G, c.scale, out=out, lse=lse)
 
-    for _ in range(warmup):
-        flush.sum()
-        union()
-        prefill()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for k in range(steps):
-        flush.sum()
-        ev[k][0].record()
-        union()
-        ev[k][1].record()
-        prefill()
-        ev[k][2].record()
-    torch.cuda.synchronize()
+    with section(torch, "form: warm-up"):
+        for _ in range(warmup):
+            flush.sum()
+            union()
+            prefill()
+    with section(torch, f"form: union over the {lay.num_slots}-slot pool, then attention, cold"):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for k in range(steps):
+            flush.sum()
+            ev[k][0].record()
+            union()
+            ev[k][1].record()
+            prefill()
+            ev[k][2].record()
+        torch.cuda.synchronize()
     u_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     p_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     both = np.array([e[0].elapsed_time(e[2]) for e in ev])
@@ -653,17 +692,18 @@ def time_prefill(c, smla, torch, steps, warmup, flush, cpu_seconds, kv_dtype="bf
         gen = torch.Generator(device="cuda").manual_seed(11)
         remap = torch.sort(torch.randperm(big, device="cuda", generator=gen)[:lay.num_slots])[0].to(torch.int32)
         slots_big = torch.where(slots >= 0, remap[slots.clamp(min=0).long()], slots).contiguous()
-        enc_b, lens_b = smla.smla_build_group_union(slots_big, valid, c.G, big)
         ub = []
-        for k in range(steps + 2):
-            flush.sum()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            smla.smla_build_group_union(slots_big, valid, c.G, big, enc=enc_b, lens=lens_b)
-            e1.record()
-            torch.cuda.synchronize()
-            if k >= 2:
-                ub.append(e0.elapsed_time(e1))
+        with section(torch, "form: union over a 2^20-slot pool, cold"):
+            enc_b, lens_b = smla.smla_build_group_union(slots_big, valid, c.G, big)
+            for k in range(steps + 2):
+                flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                smla.smla_build_group_union(slots_big, valid, c.G, big, enc=enc_b, lens=lens_b)
+                e1.record()
+                torch.cuda.synchronize()
+                if k >= 2:
+                    ub.append(e0.elapsed_time(e1))
         assert torch.equal(lens_b, lens)                   # the same union sizes as over the small pool
         union_big = float(np.median(ub)) * 1e3
         del slots_big, enc_b, lens_b, remap
@@ -826,10 +866,10 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--overlap-sweep", action="store_true",
                     help="only time grouped prefill against per-query decode for G = 2 / 4 / 8 over list "
-                         "overlaps 0 .. 1 and print the table; no JSON line")
+                         "overlaps 0 .. 1 and print the table (markdown); no JSON line")
     ap.add_argument("--split-sweep", action="store_true",
                     help="only time the decode against its split count for batches 1 .. 128 (bf16 and fp8, "
-                         "top-k 2048) and print the table; no JSON line")
+                         "top-k 2048) and print the table (markdown); no JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three plain 256 MiB fp32 copy kernels (y = x * 1), whose HBM counter "
                          "readings give the scale for the decode kernels' FETCH_SIZE / WRITE_SIZE")
@@ -867,15 +907,17 @@ def main():
     torch.cuda.set_device(0)
     flush = torch.ones((args.flush_mib << 20) // 4, dtype=torch.float32, device="cuda")
     if args.split_sweep:
-        split_sweep(smla, torch, flush, max(5, args.steps // 2))
+        print(split_sweep_markdown(split_sweep(smla, torch, flush, max(5, args.steps // 2))), end="", flush=True)
         return
     if args.overlap_sweep:
-        overlap_sweep(smla, torch, flush, max(3, args.steps // 10))
+        n = max(3, args.steps // 10)
+        print(overlap_sweep_markdown(overlap_sweep(smla, torch, flush, n), n), end="", flush=True)
         return
 
     ab = algorithmic_bytes(c2, "bf16")
     log("timing bf16 decode")
-    r = time_decode(c2, smla, torch, args.steps, args.warmup, flush)
+    with section(torch, "workload: bf16 decode, batch 32"):
+        r = time_decode(c2, smla, torch, args.steps, args.warmup, flush)
     T = c2.q.shape[0]
     step_ms = r["stream_ms"]
     value = T / (step_ms / 1e3)
@@ -930,7 +972,8 @@ def main():
         c5 = wl.decode_fp8_b64()
         ab5 = algorithmic_bytes(c5, "fp8")
         log("timing fp8-KV decode")
-        r5 = time_decode(c5, smla, torch, args.steps, args.warmup, flush)
+        with section(torch, "workload: fp8 decode, batch 64"):
+            r5 = time_decode(c5, smla, torch, args.steps, args.warmup, flush)
         ms5 = r5["stream_ms"]
         two5 = r5["two_kernel"]
         gbs5 = ab5["step"] / (ms5 / 1e3) / 1e9
@@ -958,7 +1001,8 @@ def main():
         log("generating the ragged decode workload (batch 128, 13 dense requests)")
         c3 = wl.decode_ragged_b128()
         log("timing ragged decode")
-        rg = time_ragged(c3, smla, torch, args.steps, args.warmup, flush)
+        with section(torch, "workload: ragged decode, batch 128"):
+            rg = time_ragged(c3, smla, torch, args.steps, args.warmup, flush)
         line["ragged_decode"] = rg
         log(f"ragged: step {rg['ms_per_step']*1e3:.1f} us ({rg['hbm_gbs_step']:.0f} GB/s over {rg['rows']} rows)")
 
@@ -966,15 +1010,17 @@ def main():
         log("generating the grouped-prefill workload (8192 queries on 16384 cached, G = 2)")
         c4 = wl.prefill_grouped_q8192()
         log("timing grouped prefill")
-        pr = time_prefill(c4, smla, torch, max(3, args.steps // 5), 2, flush,
-                          0.0 if args.no_cpu_baseline else min(5.0, args.cpu_seconds))
+        with section(torch, "workload: grouped prefill, bf16 cache"):
+            pr = time_prefill(c4, smla, torch, max(3, args.steps // 5), 2, flush,
+                              0.0 if args.no_cpu_baseline else min(5.0, args.cpu_seconds))
         line["grouped_prefill"] = pr
         log(f"grouped prefill: union {pr['union_us']:.0f} us ({pr['union_us_pool_2e20']:.0f} us over a 2^20-slot pool) "
             f"+ attention {pr['prefill_ms']:.2f} ms "
             f"({pr['roofline']['achieved']:.0f} TFLOP/s algorithmic, {pr['roofline']['issued_tflops']:.0f} issued)")
         if not args.no_extra:
             log("timing grouped prefill over an fp8 cache")
-            pf = time_prefill(c4, smla, torch, max(3, args.steps // 5), 2, flush, 0.0, kv_dtype="fp8")
+            with section(torch, "workload: grouped prefill, fp8 cache"):
+                pf = time_prefill(c4, smla, torch, max(3, args.steps // 5), 2, flush, 0.0, kv_dtype="fp8")
             line["grouped_prefill_fp8"] = pf
             log(f"grouped prefill (fp8 cache): union {pf['union_us']:.0f} us + attention {pf['prefill_ms']:.2f} ms "
                 f"({pf['roofline']['achieved']:.0f} TFLOP/s algorithmic)")
@@ -982,21 +1028,25 @@ def main():
 
     if not args.no_extra:
         log("timing dense paged decode (64 tokens, contexts 32K-64K)")
-        dp = time_dense_paged(smla, torch, max(5, args.steps // 2), 3, flush)
+        with section(torch, "workload: dense paged decode, 64 tokens of 32K-64K"):
+            dp = time_dense_paged(smla, torch, max(5, args.steps // 2), 3, flush)
         line["dense_paged_decode"] = dp
         log(f"dense paged: {dp['step_median_us']:.1f} us over {dp['rows']} rows ({dp['hbm_gbs_step']:.0f} GB/s)")
         log("timing 128-head decode (batch 32, top-k 2048)")
-        h1 = time_decode_h128(smla, torch, args.steps, args.warmup)
+        with section(torch, "workload: bf16 decode, 128 heads, batch 32"):
+            h1 = time_decode_h128(smla, torch, args.steps, args.warmup)
         line["decode_h128"] = h1
         log(f"128 heads: step {h1['ms_per_step']*1e3:.1f} us ({h1['hbm_gbs_step']:.0f} GB/s)")
         log("measuring the gather and copy ceilings (torch kernels)")
-        line["context_ceilings"] = gather_ceiling(torch, flush, max(5, args.steps // 5))
+        with section(torch, "workload: gather and copy ceilings (torch kernels)"):
+            line["context_ceilings"] = gather_ceiling(torch, flush, max(5, args.steps // 5))
         log(f"index_select of random rows {line['context_ceilings']['index_select_rows_gbs']:.0f} GB/s, "
             f"copy {line['context_ceilings']['copy_gbs']:.0f} GB/s")
 
     if not args.no_kv_write:
         log("timing smla_kv_write (1M rows)")
-        kw = time_kv_write(smla, torch, max(5, args.steps // 5), 3, flush)
+        with section(torch, "workload: kv_write, 1M rows"):
+            kw = time_kv_write(smla, torch, max(5, args.steps // 5), 3, flush)
         line["kv_write"] = kw
         log(f"kv_write: bf16 {kw['bf16']['us']:.0f} us ({kw['bf16']['hbm_gbs']:.0f} GB/s), fp8 {kw['fp8']['us']:.0f} us "
             f"({kw['fp8']['hbm_gbs']:.0f} GB/s)")
@@ -1006,16 +1056,374 @@ def main():
     if args.copy_calibration:
         x = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         y = torch.empty_like(x)
-        for _ in range(3):
-            flush.sum()
-            torch.mul(x, 1.0, out=y)
-        torch.cuda.synchronize()
+        with section(torch, "workload: copy calibration"):
+            for _ in range(3):
+                flush.sum()
+                torch.mul(x, 1.0, out=y)
         log("copy calibration: 3 x (read 256 MiB, write 256 MiB)")
     print(json.dumps(line), flush=True)
 
 
-def summarize_profile(argv):
-    raise SystemExit("--summarize-profile: not available yet")
+# ---- profile summaries (no GPU work): rocprofv3 CSV output -> the tables under profiles/
+
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+CSRC = "sparse_mla_attention_resolve_amd/csrc/"
+ALL_KERNEL_SOURCES = [CSRC + f for f in ("decode.hip", "union.hip", "resolve.hip", "kv_write.hip", "prefill.hip",
+                                          "abi.hip", "smla_device.h", "smla_internal.h")] + ["include/smla.h"]
+# the commands whose output the summaries reduce (run from the repository root); the summary
+# documents quote them
+BENCH_TRACE = "python3 bench.py --steps 30 --warmup 5 --no-cpu-baseline"
+BENCH_PMC = ("python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-ragged --no-prefill --no-extra "
+             "--no-kv-write --copy-calibration")
+BENCH_SQ = "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-ragged --no-extra --no-kv-write"
+SQ_PASSES = {"A": "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_LDS_ADDR_CONFLICT SQ_LDS_DATA_FIFO_FULL SQ_INSTS_LDS "
+                  "SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVE_CYCLES",
+             "B": "SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS SQ_INST_LEVEL_LDS SQ_BUSY_CYCLES "
+                  "SQ_ACTIVE_INST_VALU SQ_INSTS_VALU_MFMA_MOPS_BF16"}
+
+
+def profile_commands(kind: str, dirs) -> list:
+    """The shell commands that produce and reduce one kind of profile, with `dirs` its output
+    directories (relative to the repository root)."""
+    if kind == "trace":
+        d = dirs[0]
+        return [f"mkdir -p {d}",
+                f"rocprofv3 --kernel-trace --marker-trace --stats --output-format csv -d {d} -o run -- "
+                f"{BENCH_TRACE} > {d}/bench.json 2> {d}/bench.err",
+                f"python3 bench.py --summarize-profile trace {d}"]
+    if kind == "traffic":
+        fd, wd = dirs
+        return [f"mkdir -p {fd} {wd}",
+                f"rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d {fd} -o run -- {BENCH_PMC} "
+                f"> {fd}/bench.json 2> {fd}/bench.err",
+                f"rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d {wd} -o run -- {BENCH_PMC} "
+                f"> {wd}/bench.json 2> {wd}/bench.err",
+                f"python3 bench.py --summarize-profile traffic {fd} {wd}"]
+    if kind == "sq":
+        da, db = dirs
+        return [f"mkdir -p {da} {db}"] + [
+            f"rocprofv3 --pmc {SQ_PASSES[p]} --kernel-trace --output-format csv -d {d} -o run -- {BENCH_SQ} "
+            f"> {d}/bench.json 2> {d}/bench.err" for p, d in (("A", da), ("B", db))] + [
+            f"python3 bench.py --summarize-profile sq {da} {db}"]
+    raise ValueError(kind)
+
+
+def sources_sha256(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+_KV_NAMES = {"1": "bf16", "2": "fp8"}
+_KERNEL_RULES = [
+    (re.compile(r"decode_stage1_mfma<(\d+), (true|false)>"),
+     lambda m: f"decode_stage1_mfma<{_KV_NAMES.get(m.group(1), m.group(1))}{', union' if m.group(2) == 'true' else ''}>"),
+    (re.compile(r"decode_stage1_f32\b"), lambda m: "decode_stage1_f32"),
+    (re.compile(r"decode_stage2_packed\b"), lambda m: "decode_stage2_packed"),
+    (re.compile(r"decode_stage2\b"), lambda m: "decode_stage2"),
+    (re.compile(r"resolve_kernel\b"), lambda m: "resolve_kernel"),
+    (re.compile(r"union_map_kernel\b"), lambda m: "union_map_kernel"),
+    (re.compile(r"union_sort_kernel<(\d+), (\d+)>"), lambda m: f"union_sort_kernel<{m.group(1)}, {m.group(2)}>"),
+    (re.compile(r"kv_write_kernel\b"), lambda m: "kv_write_kernel"),
+    (re.compile(r"zero_kernel\b"), lambda m: "zero_kernel"),
+]
+
+
+def kernel_label(name: str):
+    """Short name of a libsmla kernel from its demangled name; None for any other kernel."""
+    for rx, f in _KERNEL_RULES:
+        m = rx.search(name)
+        if m:
+            return f(m)
+    return None
+
+
+def torch_label(name: str) -> str:
+    """'torch <kernel>' for another library's kernel: its function name without scope or
+    template arguments."""
+    base = re.split(r"[<(]", name.replace("(anonymous namespace)::", ""), maxsplit=1)[0].strip()
+    return "torch " + (base.split("::")[-1].split() or ["?"])[-1]
+
+
+def _read_csv(path):
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _grid(r) -> int:
+    if "Grid_Size" in r:
+        return int(r["Grid_Size"])
+    return int(r.get("Grid_Size_X", 0)) * int(r.get("Grid_Size_Y", 1)) * int(r.get("Grid_Size_Z", 1))
+
+
+def _bench_line(d):
+    """The JSON line that the profiled bench run printed (d/bench.json), or None."""
+    try:
+        for ln in open(os.path.join(d, "bench.json")):
+            if ln.startswith("{"):
+                return json.loads(ln)
+    except OSError:
+        pass
+    return None
+
+
+def _write_profile(name: str, lines) -> None:
+    path = os.path.join(PROFILE_DIR, name)
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {os.path.relpath(path, ROOT)}")
+
+
+def _fmt_cmds(kind, dirs):
+    return ["```"] + profile_commands(kind, dirs) + ["```", ""]
+
+
+def summarize_trace(d: str) -> None:
+    """profiles/decode_prefill_kernels_trace.md from a kernel + marker trace of the full bench:
+    every libsmla dispatch (and the torch kernels of the ceiling and calibration sections)
+    labelled with the bench section (workload) and form it ran in."""
+    kt = sorted(_read_csv(os.path.join(d, "run_kernel_trace.csv")), key=lambda r: int(r["Start_Timestamp"]))
+    mpath = os.path.join(d, "run_marker_api_trace.csv")
+    ranges = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Function"]) for r in _read_csv(mpath)] \
+        if os.path.exists(mpath) else []
+
+    def inner(ts, prefix):
+        best = None
+        for a, b, n in ranges:
+            if n.startswith(prefix) and a <= ts <= b and (best is None or a > best[0]):
+                best = (a, n[len(prefix):])
+        return best[1] if best else None
+
+    groups = {}
+    for r in kt:
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        wl = inner(t0, "workload: ")
+        lab = kernel_label(r["Kernel_Name"])
+        if lab is None:
+            if wl is None or not (wl.startswith("gather") or wl.startswith("copy")):
+                continue                      # the 1 GiB flush reads and other torch work
+            lab = torch_label(r["Kernel_Name"])
+        key = (lab, wl or "(outside every section)", inner(t0, "form: ") or "set-up (outside the timed forms)")
+        groups.setdefault(key, []).append((t1 - t0) / 1e3)
+    sha = sources_sha256(ALL_KERNEL_SOURCES)
+    L = ["# libsmla kernels in the bench: rocprofv3 kernel trace", "",
+         "Every kernel dispatch of one full bench run, labelled with the bench section it ran in (a marker range per "
+         "workload and per timing form; the device is drained at each range's ends). Workloads are the bench's: "
+         "sparse MLA decode at top-k 2048 (bf16 batch 32 over a 2^20-slot pool of 64-slot pages; fp8 e4m3 batch 64; "
+         "the ragged bf16 batch of 128 with 13 dense requests; 128 heads), grouped sparse prefill (8,192 queries on "
+         "16,384 cached tokens, G = 2, bf16 and fp8 caches), dense paged decode and kv_write. Durations in "
+         "microseconds. From the repository root:", ""]
+    L += _fmt_cmds("trace", [d])
+    L += [f"Kernel source sha256 ({', '.join(os.path.basename(f) for f in ALL_KERNEL_SOURCES)}): `{sha}`", ""]
+    L += ["| kernel | workload | form | dispatches | mean | median | min | max |", "|---|---|---|---|---|---|---|---|"]
+    for (lab, wl, form), v in groups.items():
+        L.append(f"| {lab} | {wl} | {form} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | "
+                 f"{min(v):.2f} | {max(v):.2f} |")
+    L.append("")
+    bl = _bench_line(d)
+    head = groups.get(("decode_stage1_mfma<bf16>", "bf16 decode, batch 32",
+                       "fused, back to back over rotating batches (the headline)"))
+    if bl and head:
+        L.append(f"The profiled run's bench line gives {bl['ms_per_step'] * 1e3:.2f} us per headline step (one pair of "
+                 f"events around {bl['steps']} back-to-back steps); the trace's mean duration of those "
+                 f"{len(head)} dispatches is {statistics.mean(head):.2f} us. Its roofline figure divides the step's "
+                 f"{bl['algorithmic_bytes_step']:,} algorithmic bytes by the step time: "
+                 f"{bl['roofline']['achieved']:.0f} GB/s, {bl['roofline']['frac']:.3f} of 8 TB/s.")
+        L.append("")
+    spath = os.path.join(d, "run_kernel_stats.csv")
+    if os.path.exists(spath):
+        rows = [r for r in _read_csv(spath) if kernel_label(r["Name"])]
+        rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+        L += ["rocprofv3 --stats over the whole run (libsmla kernels):", "",
+              "| kernel | calls | total ms | mean us | min us | max us |", "|---|---|---|---|---|---|"]
+        for r in rows:
+            L.append(f"| {kernel_label(r['Name'])} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        L.append("")
+    _write_profile("decode_prefill_kernels_trace.md", L)
+
+
+def _pmc(d: str, counters):
+    """Per-dispatch sums of `counters` from d/run_counter_collection.csv, averaged per kernel label;
+    the calibration copy (torch's x * 1 over 64M floats: an elementwise kernel of a tensor and a
+    scalar, not the fill that creates x) is labelled "copy"."""
+    per = {}
+    dur = {}
+    for r in _read_csv(os.path.join(d, "run_counter_collection.csv")):
+        if r["Counter_Name"] not in counters:
+            continue
+        lab = kernel_label(r["Kernel_Name"])
+        if lab is None:
+            if "AUnaryFunctor" in r["Kernel_Name"] and _grid(r) == (64 << 20) // 4:
+                lab = "copy"
+            else:
+                continue
+        key = (lab, r["Dispatch_Id"])
+        per.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+        per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        if "Start_Timestamp" in r and r.get("End_Timestamp"):
+            dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out, n, du = {}, {}, {}
+    for (lab, _), cs in per.items():
+        for c, v in cs.items():
+            out.setdefault(lab, {}).setdefault(c, []).append(v)
+    for lab, cs in out.items():
+        n[lab] = max(len(v) for v in cs.values())
+        out[lab] = {c: statistics.mean(v) for c, v in cs.items()}
+        ds = [v for (l2, _), v in dur.items() if l2 == lab]
+        du[lab] = statistics.mean(ds) if ds else float("nan")
+    return out, n, du
+
+
+def summarize_traffic(fd: str, wd: str) -> None:
+    """profiles/decode_kernels_hbm_traffic.md: HBM bytes per launch of the decode kernels from
+    FETCH_SIZE and WRITE_SIZE, each scaled by the copy kernel's reading of a known size."""
+    fe, nf, _ = _pmc(fd, {"FETCH_SIZE"})
+    wr, nw, _ = _pmc(wd, {"WRITE_SIZE"})
+    copy_kib = (256 << 20) / 1024.0
+    sf, sw = copy_kib / fe["copy"]["FETCH_SIZE"], copy_kib / wr["copy"]["WRITE_SIZE"]
+    sha = sources_sha256(KERNEL_SOURCES)
+    bl = _bench_line(fd) or {}
+    alg = {"decode_stage1_mfma<bf16>": bl.get("algorithmic_bytes_step"),
+           "decode_stage1_mfma<fp8>": (bl.get("fp8_kv_decode") or {}).get("algorithmic_bytes_step")}
+    L = ["# Decode kernels: HBM traffic from rocprofv3 counters", "",
+         "Two counter passes over the same bench command (bf16 decode batch 32, fp8 decode batch 64, then a plain "
+         "copy y = x * 1 over 256 MiB of fp32: 262,144 KiB read and 262,144 KiB written, which calibrates each "
+         "counter). From the repository root:", ""]
+    L += _fmt_cmds("traffic", [fd, wd])
+    L += [f"Kernel source sha256 (decode.hip + smla_device.h + smla_internal.h): `{sha}`", "",
+          f"Calibration: FETCH_SIZE reads {fe['copy']['FETCH_SIZE']:.1f} KiB for the copy's 262,144 KiB of reads "
+          f"(scale {sf:.4f}); WRITE_SIZE reads {wr['copy']['WRITE_SIZE']:.1f} KiB for its 262,144 KiB of writes "
+          f"(scale {sw:.4f}).", "",
+          "| kernel | workload | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes (scaled) | written bytes "
+          "(scaled) | traffic bytes | algorithmic bytes | traffic / algorithmic |",
+          "|---|---|---|---|---|---|---|---|---|---|"]
+    mach = []
+    for k, wk in (("decode_stage1_mfma<bf16>", "bf16_batch_32"), ("decode_stage1_mfma<fp8>", "fp8_batch_64"),
+                  ("resolve_kernel", "both")):
+        if k not in fe or k not in wr:
+            continue
+        rb, wb = fe[k]["FETCH_SIZE"] * sf * 1024, wr[k]["WRITE_SIZE"] * sw * 1024
+        a = alg.get(k)
+        L.append(f"| {k} | {wk.replace('_', ' ')} | {nf[k]} | {fe[k]['FETCH_SIZE']:.1f} | {wr[k]['WRITE_SIZE']:.1f} | "
+                 f"{rb:,.0f} | {wb:,.0f} | {rb + wb:,.0f} | {f'{a:,}' if a else '-'} | "
+                 f"{f'{(rb + wb) / a:.3f}' if a else '-'} |")
+        if k != "resolve_kernel":
+            mach.append(f"traffic_bytes_per_launch {k} {wk} {rb + wb:.0f} read {rb:.0f} write {wb:.0f}")
+    L += ["", "Each decode's launches in every timed form (fused resolution, over resolved slots, back to back, graph "
+          "replay) are averaged together: they move the same cache rows. The algorithmic bytes are the bench's: cache "
+          "rows gathered once, q, the index table, the output and LSE, the split partials written and read back once.",
+          "", "Machine-readable lines (bench.py reports `roofline.traffic` from these while the kernel source hash "
+          "matches):", "", "```"] + mach + [f"source_sha256 {sha}", "```"]
+    _write_profile("decode_kernels_hbm_traffic.md", L)
+
+
+SQ_CLOCK_HZ = 2.1e9          # shader clock over the decode loop, measured with s_memtime on this GPU
+
+
+def summarize_sq(da: str, db: str) -> None:
+    """profiles/decode_prefill_sq_counters.md from the two SQ counter passes."""
+    cols = [("decode bf16", "decode_stage1_mfma<bf16>"), ("decode fp8", "decode_stage1_mfma<fp8>"),
+            ("union (prefill)", "decode_stage1_mfma<bf16, union>")]
+    pa, na, dura = _pmc(da, set(SQ_PASSES["A"].split()))
+    pb, nb, _ = _pmc(db, set(SQ_PASSES["B"].split()))
+    mean = {c: {**pa.get(k, {}), **pb.get(k, {})} for c, k in cols}
+    dur = {c: dura.get(k, float("nan")) for c, k in cols}
+    names = sorted({n for c, _ in cols for n in mean[c]})
+    sha = sources_sha256(KERNEL_SOURCES)
+    L = ["# Shader-sequencer counters: bf16 and fp8 decode, grouped prefill (MI355X)", "",
+         "Two counter passes (eight SQ counters each) over the same short bench run. From the repository root:", ""]
+    L += _fmt_cmds("sq", [da, db])
+    L += [f"Kernel source sha256 (decode.hip + smla_device.h + smla_internal.h): `{sha}`", "",
+          "Per-dispatch means: `decode bf16` = `decode_stage1_mfma<bf16>` on bf16 batch 32 (every form the bench runs); "
+          "`decode fp8` = `decode_stage1_mfma<fp8>` on fp8 batch 64; `union (prefill)` = "
+          "`decode_stage1_mfma<bf16, union>` on grouped prefill Q 8192 (G 2, 64 heads). Counter values are the device "
+          "totals rocprofv3 reports; the derived rows divide them by 256 compute units (or 1,024 SIMDs) and by the "
+          f"dispatch's cycles at {SQ_CLOCK_HZ / 1e9:.1f} GHz (the shader clock measured over the decode loop with "
+          "s_memtime). Durations under counter collection run longer than in the kernel trace.", "",
+          "| counter | " + " | ".join(c for c, _ in cols) + " |", "|---" * (len(cols) + 1) + "|"]
+    for n in names:
+        L.append(f"| {n} | " + " | ".join(f"{mean[c].get(n, float('nan')):.4g}" for c, _ in cols) + " |")
+    L.append("| dispatches (pass A / B) | " + " | ".join(f"{na.get(k, 0)} / {nb.get(k, 0)}" for _, k in cols) + " |")
+    L.append("| mean duration us (pass A) | " + " | ".join(f"{dur[c]:.1f}" for c, _ in cols) + " |")
+    derived = [
+        ("LDS bank-conflict stall cycles per CU-cycle", lambda m, cy: m["SQ_LDS_BANK_CONFLICT"] / (256 * cy)),
+        ("LDS busy (indexed) cycles per CU-cycle", lambda m, cy: m["SQ_LDS_IDX_ACTIVE"] / (256 * cy)),
+        ("MFMA busy cycles per SIMD-cycle", lambda m, cy: m["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cy)),
+        ("wave-cycles waiting (any) / wave-cycles", lambda m, cy: m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]),
+        ("wave-cycles waiting to issue / wave-cycles", lambda m, cy: m["SQ_WAIT_INST_ANY"] / m["SQ_WAVE_CYCLES"]),
+        ("wave-cycles waiting to issue LDS / wave-cycles", lambda m, cy: m["SQ_WAIT_INST_LDS"] / m["SQ_WAVE_CYCLES"]),
+        ("MFMA FLOP per dispatch (BF16 MOPS x 512)", lambda m, cy: m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512),
+        ("MFMA TFLOP/s over the dispatch (pass A duration)",
+         lambda m, cy: m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (cy / SQ_CLOCK_HZ) / 1e12),
+    ]
+    L += ["", "Derived:", "", "| quantity | " + " | ".join(c for c, _ in cols) + " |", "|---" * (len(cols) + 1) + "|"]
+    val = {}
+    for label, f in derived:
+        cells = []
+        for c, _ in cols:
+            try:
+                v = f(mean[c], dur[c] * 1e-6 * SQ_CLOCK_HZ)
+            except (KeyError, ZeroDivisionError):
+                v = float("nan")
+            val[(label, c)] = v
+            cells.append(f"{v:.4g}")
+        L.append(f"| {label} | " + " | ".join(cells) + " |")
+    mf = [val[("MFMA busy cycles per SIMD-cycle", c)] for c, _ in cols]
+    ld = [val[("LDS busy (indexed) cycles per CU-cycle", c)] for c, _ in cols]
+    wt = [val[("wave-cycles waiting (any) / wave-cycles", c)] for c, _ in cols]
+    L += ["", f"Over the three kernels the matrix unit is busy {min(mf):.2f}-{max(mf):.2f} of the SIMD cycles, the LDS "
+              f"{min(ld):.2f}-{max(ld):.2f} of the CU cycles, and the waves wait {min(wt):.2f}-{max(wt):.2f} of "
+              "theirs: no unit is saturated, so the loops are bound by latency (operand reads, accumulation chains, "
+              "barriers) and, in decode, by the row gathers."]
+    _write_profile("decode_prefill_sq_counters.md", L)
+
+
+def summarize_profile(argv) -> None:
+    kind, dirs = argv[0], argv[1:]
+    need = {"trace": 1, "traffic": 2, "sq": 2}
+    if kind not in need or len(dirs) != need[kind]:
+        raise SystemExit("--summarize-profile: trace DIR | traffic FETCH_DIR WRITE_DIR | sq DIR_A DIR_B")
+    {"trace": summarize_trace, "traffic": summarize_traffic, "sq": summarize_sq}[kind](*dirs)
+
+
+def split_sweep_markdown(res) -> str:
+    cols = sorted({S for v in res.values() for S in v["us"]})
+    sha = sources_sha256([CSRC + f for f in ("decode.hip", "smla_device.h", "smla_internal.h", "abi.hip")])
+    L = ["# Decode step against the split count (MI355X, one GPU)", "",
+         "Cold steps (1 GiB read before each, median) of `smla_sparse_decode` at top-k 2048, 64 heads, over a "
+         "2^20-slot pool of random rows, for each batch size and cache format, at every split count from the fewest "
+         "(a split holds at most 1,024 rows) to one 32-row chunk per split. From the repository root:", "",
+         "```", "python3 bench.py --split-sweep > profiles/decode_split_sweep.md", "```", "",
+         f"Source sha256 (decode.hip + smla_device.h + smla_internal.h + abi.hip): `{sha}`", "",
+         "`auto` is the split count the library picks when `num_splits` is 0. Step time in microseconds.", "",
+         "| cache | T | auto S | auto us | best S | best us | " + " | ".join(f"S={S}" for S in cols) + " |",
+         "|---" * (6 + len(cols)) + "|"]
+    for (dt, T), v in res.items():
+        cells = " | ".join(f"{v['us'][S]:.1f}" if S in v["us"] else "-" for S in cols)
+        L.append(f"| {dt} | {T} | {v['auto']} | {v['us'][v['auto']]:.1f} | {v['best']} | {v['us'][v['best']]:.1f} | "
+                 f"{cells} |")
+    return "\n".join(L) + "\n"
+
+
+def overlap_sweep_markdown(res, steps) -> str:
+    sha = sources_sha256([CSRC + f for f in ("decode.hip", "union.hip", "smla_device.h", "smla_internal.h")])
+    L = ["# Grouped prefill against per-query decode, by list overlap (MI355X, one GPU)", "",
+         "4,096 queries with lists of 2,048 slots over a 24,576-slot bf16 cache of random rows (the grouped-prefill "
+         "configuration's pool). Queries come in groups of G with H = 128 / G heads; a fraction `overlap` of each list "
+         "is shared by the group's members and the rest is disjoint (so the union holds exactly "
+         f"(overlap + G (1 - overlap)) x 2,048 rows). Cold steps (1 GiB read before each, median of {steps}):", "",
+         "- grouped: `smla_build_group_union` + `smla_grouped_prefill`;",
+         "- alone: `smla_sparse_decode` over the same lists (page size 1), every query attending its own rows.", "",
+         "From the repository root:", "", "```", "python3 bench.py --overlap-sweep > profiles/grouped_prefill_overlap_sweep.md",
+         "```", "", f"Source sha256 (decode.hip + union.hip + smla_device.h + smla_internal.h): `{sha}`", "",
+         "| G | H | overlap | union rows / W | grouped us | alone us | speedup |", "|---|---|---|---|---|---|---|"]
+    for (G, ov), v in res.items():
+        L.append(f"| {G} | {128 // G} | {ov:.2f} | {v['union_per_list']:.2f} | {v['grouped_us']:.0f} | "
+                 f"{v['alone_us']:.0f} | {v['alone_us'] / v['grouped_us']:.2f}x |")
+    return "\n".join(L) + "\n"
 
 
 if __name__ == "__main__":
