@@ -685,7 +685,7 @@ def time_prefill(c, smla, torch, steps, warmup, flush, cpu_seconds, kv_dtype="bf
     p_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     both = np.array([e[0].elapsed_time(e[2]) for e in ev])
     # the same lists over a 2^20-slot pool (the slots mapped one to one onto a random subset of
-    # it, in order): the union builder then takes its sort path instead of the row map
+    # it, in order): the union builder's bit map then spans 2^20 rows
     union_big = None
     if kv_dtype == "bf16":
         big = 1 << 20
@@ -1124,7 +1124,7 @@ _KERNEL_RULES = [
     (re.compile(r"decode_stage2_packed\b"), lambda m: "decode_stage2_packed"),
     (re.compile(r"decode_stage2\b"), lambda m: "decode_stage2"),
     (re.compile(r"resolve_kernel\b"), lambda m: "resolve_kernel"),
-    (re.compile(r"union_map_kernel\b"), lambda m: "union_map_kernel"),
+    (re.compile(r"union_bitmap_kernel<(\d+)>"), lambda m: f"union_bitmap_kernel<{m.group(1)}>"),
     (re.compile(r"union_sort_kernel<(\d+), (\d+)>"), lambda m: f"union_sort_kernel<{m.group(1)}, {m.group(2)}>"),
     (re.compile(r"kv_write_kernel\b"), lambda m: "kv_write_kernel"),
     (re.compile(r"zero_kernel\b"), lambda m: "zero_kernel"),

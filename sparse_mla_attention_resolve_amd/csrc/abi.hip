@@ -412,7 +412,7 @@ smla_status smla_build_group_union(const int32_t* slots, int64_t slots_stride, c
   CHECK(aligned(slots, 4) && aligned(enc, 4) && aligned(lens, 4) && (!valid || aligned(valid, 4)), SMLA_ERR_ALIGN,
         "%s: arrays must be 4-byte aligned", fn);
   return device_status(smla::launch_union(slots, slots_stride, valid, Q, W, G, num_slots, enc, enc_stride, lens,
-                                          (hipStream_t)stream),
+                                          device_cus(), (hipStream_t)stream),
                        fn);
 }
 

@@ -55,9 +55,10 @@ hipError_t launch_kv_write(const void* src, int32_t src_dtype, int64_t src_strid
 hipError_t launch_decode(const smla_decode_args& a, const DecodePlan& plan, void* ws,
                          hipStream_t stream, int stages = 3, const smla_page_map* map = nullptr);
 
+// cus: the device's compute units (the bit-map builder sizes its persistent grid with it)
 hipError_t launch_union(const int32_t* slots, int64_t slots_stride, const int32_t* valid,
                         int32_t Q, int32_t W, int32_t G, int64_t num_slots, uint32_t* enc,
-                        int64_t enc_stride, int32_t* lens, hipStream_t stream);
+                        int64_t enc_stride, int32_t* lens, int32_t cus, hipStream_t stream);
 
 hipError_t launch_prefill(const smla_prefill_args& a, hipStream_t stream);
 

@@ -2,87 +2,231 @@
 // cases, "Changes" for unions of consecutive queries whose rows keep a bit per member,
 // "Details" for gathering the union once per 128-row tile).
 //
-// One workgroup per group, two builders with the same result (the ascending union, each row
-// once with the OR of its members' bits):
-//   - pools of up to kMapSlots rows: a map of one byte per pool row in LDS;
-//   - larger pools: every listed (row, member) pair becomes the key row * 8 + member (padding,
-//     negative rows and rows past the pool become 0xffffffff), the keys are sorted by a
-//     bitonic network held in registers, each run of one row is folded into a single entry,
-//     and a block-wide prefix count of run heads gives every entry its place.
+// Two builders with the same result (the ascending union, each row once with the OR of its
+// members' bits):
+//   - pools of up to kBitmapSlots (2^20) rows (below 2^18 when a group lists more than 8,192
+//     entries), when the map fits LDS: a bit per pool row in LDS, counted per block to place
+//     each row; persistent workgroups build one group after another;
+//   - larger pools, one workgroup per group: every listed (row, member) pair becomes the key
+//     row * 8 + member (padding, negative rows and rows past the pool become 0xffffffff), the
+//     keys are sorted by a bitonic network held in registers, each run of one row is folded
+//     into a single entry, and a block-wide prefix count of run heads gives every entry its
+//     place.
 #include "smla_device.h"
 #include "smla_internal.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace smla {
 
 namespace {
 
-constexpr int kUnionThreads = 1024;
 constexpr uint32_t kEmpty = 0xffffffffu;
 
-// Pools of at most kMapSlots rows: the group marks its members in a map of one byte per
-// pool row in LDS (bit m of row r's byte = member m lists r; an atomic OR per listed entry),
-// then walks the map in ascending row order: thread i owns rows [i * per, (i + 1) * per), and
-// a block-wide prefix count of the marked rows gives every entry its place. No sort, and the
-// result is the same ascending union with the same bits.
-constexpr int kMapSlots = 49152;
-
-__global__ void __launch_bounds__(kUnionThreads) union_map_kernel(
-    const int32_t* __restrict__ slots, int64_t slots_stride, const int32_t* __restrict__ valid,
-    int32_t Q, int32_t W, int32_t G, int32_t num_slots, int32_t per,
-    uint32_t* __restrict__ enc, int64_t enc_stride, int32_t* __restrict__ lens) {
-  extern __shared__ uint32_t map[];                      // (num_slots + 3) / 4 words
-  __shared__ int32_t wave_tot[kUnionThreads / 64];
-  const int g = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int nwords = (num_slots + 3) >> 2;
-  for (int i = tid; i < nwords; i += kUnionThreads) map[i] = 0u;
-  __syncthreads();
-  for (int m = 0; m < G; ++m) {
-    const int q = g * G + m;
-    if (q >= Q) break;
-    const int cnt = valid ? min(max(valid[q], 0), W) : W;
-    const int32_t* row = slots + (int64_t)q * slots_stride;
-    for (int j = tid; j < cnt; j += kUnionThreads) {
-      const int32_t r = row[j];
-      if (r >= 0 && r < num_slots) atomicOr(&map[r >> 2], (1u << m) << (8 * (r & 3)));
-    }
-  }
-  __syncthreads();
-  // this thread's rows: per is a multiple of 4, so they are whole words
-  const int r0 = tid * per, r1 = min(r0 + per, num_slots);
-  int heads = 0;
-  for (int r = r0; r < r1; r += 4) {
-    const uint32_t v = map[r >> 2];
-    heads += ((v & 0xffu) != 0) + ((v & 0xff00u) != 0) + ((v & 0xff0000u) != 0) + ((v >> 24) != 0);
-  }
-  const int lane = tid & 63, wv = tid >> 6;
-  int incl = heads;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) wave_tot[wv] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int k2 = 0; k2 < kUnionThreads / 64; ++k2) {
-    before += k2 < wv ? wave_tot[k2] : 0;
-    total += wave_tot[k2];
-  }
-  int pos = before + incl - heads;
-  uint32_t* out = enc + (int64_t)g * enc_stride;
-  for (int r = r0; r < r1; r += 4) {
-    const uint32_t v = map[r >> 2];
-    if (v == 0u) continue;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t mask = (v >> (8 * b)) & 0xffu;
-      if (mask != 0u) out[pos++] = (uint32_t)(r + b) | (mask << SMLA_UNION_ROW_BITS);
-    }
-  }
-  if (tid == 0) lens[g] = total;
+// e / W for 0 <= e < 2^15 and W >= 1, with rw = 1 / W in fp32: the product is within 2^-8 of
+// the true quotient, so its truncation is off by at most one, which one step corrects.
+__device__ __forceinline__ int div_w(int e, int W, float rw) {
+  int m = (int)((float)e * rw);
+  m -= m * W > e ? 1 : 0;
+  m += (m + 1) * W <= e ? 1 : 0;
+  return m;
 }
 
-// Pools too large for the row map: the group's keys (row << 3 | member, empty = 0xffffffff)
+// Workgroup barrier that waits for this wave's LDS operations only: global loads issued ahead
+// (the next group's list entries) and the output stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no LDS): shifts by 1,
+// 2, 4 and 8 lanes inside each row of 16, then the last lane of row 0 added to rows 1 and 3,
+// and the last lane of row 1 (by then the sum of rows 0 and 1) added to rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x = dpp_add<0x111, 0xf>(x);                          // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);                          // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);                          // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);                          // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);                          // row_bcast:15 into rows 1, 3
+  x = dpp_add<0x143, 0xc>(x);                          // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Exclusive prefix of x over the P threads of the workgroup (in thread order); `tot` receives
+// the sum. wave_tot holds P / 64 words; it is free again after the caller's next barrier.
+template <int P>
+__device__ __forceinline__ int block_exclusive_sum(int x, int32_t* wave_tot, int& tot) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int incl = wave_inclusive_sum(x);
+  if (lane == 63) wave_tot[wv] = incl;
+  lds_barrier();
+  int before = 0;
+  tot = 0;
+#pragma unroll
+  for (int k = 0; k < P / 64; ++k) {
+    before += k < wv ? wave_tot[k] : 0;
+    tot += wave_tot[k];
+  }
+  return before + incl - x;
+}
+
+// Pools of at most kBitmapSlots rows: a bit per pool row in LDS, in blocks of 128 rows (four
+// words). The group's listed rows set their bits (an atomic OR each). Each wave counts the set
+// bits of a contiguous range of blocks, 64 blocks at a time (one 16-byte read per lane, so a
+// wave's reads cover every bank once) with a prefix inside the wave, and one block-wide sum of
+// the waves' totals turns the counts into the number of union rows before each block. A row's
+// place in the ascending union is then its block's count plus the set bits before it in the
+// block (one 16-byte read). Each listed entry ORs its member's bit into its place's byte, the
+// union's rows are written over the bit map in place order, and one coalesced pass writes the
+// entries. Cost per group: the map's size (cleared and counted once) plus a few LDS reads per
+// listed entry; no sort.
+// A workgroup builds groups blockIdx.x, + gridDim.x, ... (as many workgroups as fit the compute
+// units at once): the next group's list entries are loaded while the current one is built.
+constexpr int kBitmapSlots = 1 << 20;
+constexpr int kBitmapThreads = 1024;
+
+template <int K>
+__global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
+    const int32_t* __restrict__ slots, int64_t slots_stride, const int32_t* __restrict__ valid,
+    int32_t Q, int32_t W, int32_t G, int32_t num_slots, int32_t groups,
+    uint32_t* __restrict__ enc, int64_t enc_stride, int32_t* __restrict__ lens) {
+  constexpr int P = kBitmapThreads, kWaves = P / 64;
+  extern __shared__ uint32_t lds[];
+  __shared__ int32_t wave_tot[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = G * W;                                 // list entries of a group
+  const int nblocks = (num_slots + 127) >> 7;          // 128-row blocks
+  const int per_wave = (nblocks + kWaves - 1) / kWaves;   // blocks counted by each wave
+  const int area = max(4 * nblocks, n);
+  uint4* const bm = (uint4*)lds;                       // the bit map (a block per uint4), then the union's rows
+  uint32_t* const ubits = lds + area;                  // byte r: member bits of union entry r
+  uint16_t* const pre = (uint16_t*)(ubits + ((n + 3) >> 2));   // union rows before each block
+  // entry e = i * P + tid of the members' lists laid end to end: member m = e / W and position
+  // j = e - m W, the same for every group (as m << 16 | j, or -1 past the lists)
+  const float rw = 1.0f / (float)W;
+  auto entry = [&](int i) -> int32_t {
+    const int e = i * P + tid;
+    const int m = div_w(e, W, rw);
+    return e < n ? (m << 16) | (e - m * W) : -1;
+  };
+  // the row loads' addresses are in range whatever the data (entries past the lists read the
+  // last member's row and are masked), so all of them are in flight at once; the members'
+  // counts are the same for every thread (scalar loads)
+  int32_t raw[K], cnt_lane;                            // cnt_lane: member `lane`'s count (lanes < 8)
+  auto load = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const int32_t mj = entry(i);
+      const int m = mj >> 16, j = mj & 0xffff;
+      const int q = min(g * G + min(max(m, 0), G - 1), Q - 1);
+      raw[i] = mj >= 0 ? slots[(int64_t)q * slots_stride + j] : -1;
+    }
+    // a vector load (a scalar one would be waited for at the next LDS barrier)
+    const bool member = lane < G && g * G + lane < Q;
+    cnt_lane = member ? (valid ? valid[g * G + lane] : W) : 0;
+  };
+  // with 16 entries per thread the next group's rows are not loaded ahead (registers)
+  constexpr bool kAhead = K <= 8;
+  int g = blockIdx.x;
+  if (kAhead && g < groups) load(g);
+  for (; g < groups; g += gridDim.x) {
+    if (!kAhead) load(g);
+    int32_t key[K];                                    // listed row | member << 24, or -1
+    const int cnt_c = min(max(cnt_lane, 0), W);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const int32_t mj = entry(i);
+      const int m = mj >> 16, j = mj & 0xffff;
+      const int lim = __shfl(cnt_c, m & 7, 64);
+      key[i] = mj >= 0 && j < lim && raw[i] >= 0 && raw[i] < num_slots ? raw[i] | (m << 24) : -1;
+    }
+    if (kAhead && g + (int)gridDim.x < groups) load(g + gridDim.x);   // lands while this group is built
+    for (int b = tid; b < nblocks; b += P) bm[b] = make_uint4(0u, 0u, 0u, 0u);
+    for (int w = tid; w < ((n + 3) >> 2); w += P) ubits[w] = 0u;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (key[i] >= 0) atomicOr(&lds[(key[i] & 0xffffff) >> 5], 1u << (key[i] & 31));
+    lds_barrier();
+    // set bits per block, and their prefix inside the wave's range: round k covers blocks
+    // b_lo + 64k + lane (at most 8 rounds: 2^20 rows are 8,192 blocks over 16 waves); the
+    // rounds' reads all go out first and their scans are independent
+    const int b_lo = wv * per_wave, b_hi = min(b_lo + per_wave, nblocks);
+    int c[8], incl[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int b = b_lo + 64 * k + lane;
+      c[k] = 0;
+      if (b < b_hi) {
+        const uint4 x = bm[b];
+        c[k] = __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+      }
+    }
+    int run = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      incl[k] = wave_inclusive_sum(c[k]) + run;
+      run = __builtin_amdgcn_readlane(incl[k], 63);
+    }
+    if (lane == 0) wave_tot[wv] = run;
+    lds_barrier();
+    int off = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      off += k < wv ? wave_tot[k] : 0;
+      total += wave_tot[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int b = b_lo + 64 * k + lane;
+      if (b < b_hi) pre[b] = (uint16_t)(off + incl[k] - c[k]);
+    }
+    lds_barrier();
+    // each listed entry's place in the union (its block's count, plus the set bits before it in
+    // the block), and its member's bit there
+    // (with 16 entries per thread the place replaces the member in the key, row | place << 18,
+    // which holds for pools of fewer than 2^18 rows: the row's 18 bits are never all ones, so a
+    // packed key is never -1; fewer entries keep the places apart)
+    constexpr bool kPack = K >= 16;
+    int place[kPack ? 1 : K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if constexpr (!kPack) place[i] = -1;
+      if (key[i] >= 0) {
+        const int r = key[i] & 0xffffff, b = r >> 7, wi = (r >> 5) & 3;
+        const uint4 x = bm[b];
+        const uint32_t below = (1u << (r & 31)) - 1u;
+        int pl = pre[b];
+        pl += wi > 0 ? __popc(x.x) : __popc(x.x & below);
+        pl += wi > 1 ? __popc(x.y) : (wi == 1 ? __popc(x.y & below) : 0);
+        pl += wi > 2 ? __popc(x.z) : (wi == 2 ? __popc(x.z & below) : 0);
+        pl += wi == 3 ? __popc(x.w & below) : 0;
+        atomicOr(&ubits[pl >> 2], (1u << (key[i] >> 24)) << (8 * (pl & 3)));
+        if constexpr (kPack) key[i] = r | (pl << 18);
+        else place[i] = pl;
+      }
+    }
+    lds_barrier();                                   // the bit map is read: it takes the rows
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if constexpr (kPack) {
+        if (key[i] != -1) lds[(uint32_t)key[i] >> 18] = (uint32_t)key[i] & 0x3ffffu;
+      } else {
+        if (place[i] >= 0) lds[place[i]] = (uint32_t)(key[i] & 0xffffff);
+      }
+    }
+    lds_barrier();
+    uint32_t* out = enc + (int64_t)g * enc_stride;
+    for (int r = tid; r < total; r += P)
+      out[r] = lds[r] | (((ubits[r >> 2] >> (8 * (r & 3))) & 0xffu) << SMLA_UNION_ROW_BITS);
+    if (tid == 0) lens[g] = total;
+    lds_barrier();                                   // before the next group clears the map
+  }
+}
+
+// Pools too large for the bit map: the group's keys (row << 3 | member, empty = 0xffffffff)
 // are sorted by a bitonic network whose data stays in registers, unrolled at compile time.
 // Thread t holds keys t*K .. t*K + K - 1 of the n = P * K (a power of two); a compare-exchange
 // of stride j pairs key p with key p ^ j, which is
@@ -159,24 +303,30 @@ __global__ void __launch_bounds__(P) union_sort_kernel(
   __shared__ uint32_t keys[n];
   __shared__ int32_t wave_tot[P / 64];
   const int g = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int t = threadIdx.x;
   uint32_t v[K];
   // the thread's keys before the sort: entries t, t + P, t + 2P, ... of the members' lists laid
-  // end to end (any assignment sorts the same; this one makes each load instruction contiguous)
+  // end to end (any assignment sorts the same; this one makes each load instruction contiguous).
+  // Entry e is position j = e - m W of member m = e / W. Every load address is in range
+  // whatever the data (entries past the group's lists read the last member's row and are
+  // masked afterwards), so all the loads are in flight at once.
+  const float rw = 1.0f / (float)W;
+  int32_t raw[K], lim[K], mj[K];
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     const int e = i * P + t;
-    const int m = e / W, j = e - m * W;
-    uint32_t key = kEmpty;
-    const int q = g * G + m;
-    if (m < G && q < Q) {
-      const int cnt = valid ? min(max(valid[q], 0), W) : W;
-      if (j < cnt) {
-        const int32_t r = slots[(int64_t)q * slots_stride + j];
-        if (r >= 0 && r < num_slots) key = ((uint32_t)r << 3) | (uint32_t)m;
-      }
-    }
-    v[i] = key;
+    const int m = div_w(e, W, rw), j = e - m * W;
+    const int q = min(g * G + min(m, G - 1), Q - 1);
+    raw[i] = slots[(int64_t)q * slots_stride + j];
+    lim[i] = valid ? valid[q] : W;
+    mj[i] = m < G && g * G + m < Q ? (m << 16) | j : -1;    // member and position, or not listed
+  }
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const int m = mj[i] >> 16, j = mj[i] & 0xffff;
+    const int32_t r = raw[i];
+    v[i] = mj[i] >= 0 && j < min(max(lim[i], 0), W) && r >= 0 && r < num_slots ? ((uint32_t)r << 3) | (uint32_t)m
+                                                                                 : kEmpty;
   }
   sort_all<P, K, 2>(v, keys, t);
   __syncthreads();
@@ -190,19 +340,8 @@ __global__ void __launch_bounds__(P) union_sort_kernel(
     const int p = t * K + i;
     if (v[i] != kEmpty && (p == 0 || (keys[p - 1] >> 3) != (v[i] >> 3))) ++heads;
   }
-  int incl = heads;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) wave_tot[wv] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int k2 = 0; k2 < P / 64; ++k2) {
-    before += k2 < wv ? wave_tot[k2] : 0;
-    total += wave_tot[k2];
-  }
-  int pos = before + incl - heads;
+  int total;
+  int pos = block_exclusive_sum<P>(heads, wave_tot, total);
   uint32_t* out = enc + (int64_t)g * enc_stride;
 #pragma unroll
   for (int i = 0; i < K; ++i) {
@@ -217,26 +356,65 @@ __global__ void __launch_bounds__(P) union_sort_kernel(
   if (t == 0) lens[g] = total;
 }
 
+// A kernel's dynamic LDS limit, raised to `bytes` when a launch needs more than the limit set
+// so far on the current device (each device keeps its own function attributes). Racing first
+// calls may both set it; the larger value stays.
+std::atomic<int32_t> lds_limit[5][64];
+
+hipError_t allow_dynamic_lds(const void* kernel, int k, size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::atomic<int32_t>* lim = dev >= 0 && dev < 64 ? &lds_limit[k][dev] : nullptr;
+  if (lim && lim->load(std::memory_order_relaxed) >= (int32_t)bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && lim) {
+    int32_t cur = lim->load(std::memory_order_relaxed);
+    while (cur < (int32_t)bytes && !lim->compare_exchange_weak(cur, (int32_t)bytes, std::memory_order_relaxed)) {
+    }
+  }
+  return e;
+}
+
 }  // namespace
 
 hipError_t launch_union(const int32_t* slots, int64_t slots_stride, const int32_t* valid,
                         int32_t Q, int32_t W, int32_t G, int64_t num_slots, uint32_t* enc,
-                        int64_t enc_stride, int32_t* lens, hipStream_t stream) {
+                        int64_t enc_stride, int32_t* lens, int32_t cus, hipStream_t stream) {
   if (Q == 0) return hipSuccess;
   const int groups = (Q + G - 1) / G;
-  if (num_slots <= kMapSlots) {
-    const int per = ((int)((num_slots + kUnionThreads - 1) / kUnionThreads) + 3) / 4 * 4;
-    const size_t lds = (size_t)((num_slots + 3) / 4) * 4;
-    hipLaunchKernelGGL(union_map_kernel, dim3(groups), dim3(kUnionThreads), lds, stream, slots, slots_stride, valid,
-                       Q, W, G, (int32_t)num_slots, per, enc, enc_stride, lens);
+  const int n = G * W, nblocks = (int)((std::min<int64_t>(num_slots, kBitmapSlots) + 127) >> 7);
+  const size_t lds = (size_t)(std::max(4 * nblocks, n) + ((n + 3) >> 2)) * 4 + (size_t)nblocks * 2;
+  // the bit map, the member bytes and the block counts must fit one compute unit's LDS beside
+  // the kernel's own (a 2^20-row pool with 16,384 list entries per group does not: the sort)
+  if (num_slots <= (n > 8192 ? (1 << 18) - 1 : kBitmapSlots) && lds + 1024 <= 160u * 1024u) {
+    // as many workgroups as fit the compute units at once (registers and LDS decide)
+#define SMLA_UNION_BITMAP(K)                                                                                        \
+  do {                                                                                                              \
+    hipError_t e = allow_dynamic_lds((const void*)union_bitmap_kernel<K>, __builtin_ctz(K), lds);                  \
+    if (e != hipSuccess) return e;                                                                                  \
+    int per_cu = 0;                                                                                                 \
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)union_bitmap_kernel<K>, kBitmapThreads, \
+                                                     lds);                                                          \
+    if (e != hipSuccess) return e;                                                                                  \
+    const int grid = (int)std::min<int64_t>(groups, (int64_t)std::max(1, cus) * std::max(1, per_cu));               \
+    hipLaunchKernelGGL((union_bitmap_kernel<K>), dim3(grid), dim3(kBitmapThreads), lds, stream, slots, slots_stride, \
+                       valid, Q, W, G, (int32_t)num_slots, groups, enc, enc_stride, lens);                          \
+  } while (0)
+    if (n <= 1024) SMLA_UNION_BITMAP(1);
+    else if (n <= 2048) SMLA_UNION_BITMAP(2);
+    else if (n <= 4096) SMLA_UNION_BITMAP(4);
+    else if (n <= 8192) SMLA_UNION_BITMAP(8);
+    else SMLA_UNION_BITMAP(16);                  // 16384, the largest G * W the ABI accepts
+#undef SMLA_UNION_BITMAP
     return hipGetLastError();
   }
-  int n = 256;
-  while (n < G * W) n <<= 1;
+  int keys = 256;                                  // the sort's key count: G * W rounded up to a power of two
+  while (keys < G * W) keys <<= 1;
 #define SMLA_UNION_SORT(P, K)                                                                                        \
   hipLaunchKernelGGL((union_sort_kernel<P, K>), dim3(groups), dim3(P), 0, stream, slots, slots_stride, valid, Q, W, G, \
                      num_slots, enc, enc_stride, lens)
-  switch (n) {
+  switch (keys) {
     case 256: SMLA_UNION_SORT(256, 1); break;
     case 512: SMLA_UNION_SORT(256, 2); break;
     case 1024: SMLA_UNION_SORT(256, 4); break;

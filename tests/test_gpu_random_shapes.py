@@ -124,7 +124,8 @@ def test_random_decode_shape(seed):
 def test_random_prefill_shape(seed):
     """Union build + grouped prefill on random shapes: G in {2, 4, 8} (H = 128 / G), a query
     count that may leave the last group short, list widths, empty and partial lists, list
-    overlap, pools below and above the union row-map limit, and every cache format."""
+    overlap, pools of several sizes (the bit-map union builder; the sorting one is covered by the
+    union tests), and every cache format."""
     rng = np.random.default_rng(2000 + seed)
     G = int(rng.choice([2, 4, 8]))
     H = 128 // G

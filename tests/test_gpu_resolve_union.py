@@ -108,17 +108,20 @@ def test_union_golden():
 
 @pytest.mark.parametrize("G", [2, 4, 8])
 @pytest.mark.parametrize("Q", [1, 7, 64])
-@pytest.mark.parametrize("ns", [5000, 49152, 200000])
+@pytest.mark.parametrize("ns", [5000, 262143, 262144, 1 << 20, (1 << 20) + 1, 3000000])
 def test_union_random(G, Q, ns):
-    # pools up to 49152 rows take the row-map kernel, larger ones the sorting kernel
-    W = 2048 if G == 2 else (1024 if G == 4 else 300)
+    # pools of up to 2^20 rows take the bit-map kernel (with 16,384 entries per group, G = 8 here,
+    # only below 2^18 rows), larger ones the sorting kernel
+    W = 1024 if G == 4 else 2048
     slots, valid = wl.random_slot_lists(1000 + G * 10 + Q, Q, W, ns, overlap=0.6, G=G, pad_frac=0.3)
     rng = np.random.default_rng(Q)
-    # sprinkle negative rows, rows past the pool and in-list duplicates
+    # sprinkle negative rows, rows past the pool and in-list duplicates; every list holds the
+    # pool's last row
     m = rng.random(slots.shape)
     slots[m < 0.01] = -5
     slots[(m > 0.01) & (m < 0.02)] = ns + 3
     slots[:, 1] = slots[:, 0]
+    slots[:, 2] = ns - 1
     enc_g, lens_g = _union_gpu(slots, valid, G, ns)
     enc_o, lens_o = oracle.group_union(slots, valid, G, ns)
     _compare_union(enc_g, lens_g, enc_o, lens_o)
