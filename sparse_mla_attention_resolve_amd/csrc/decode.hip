@@ -17,69 +17,13 @@
 // codes convert to bf16 exactly, once per workgroup, into a staging tile that the bf16 MFMA
 // loop reads; the per-row scale multiplies the latent part of the score and the softmax
 // weight that meets the row's values.
-#include "smla_device.h"
-#include "smla_internal.h"
+#include "stage1_common.h"
 
 namespace smla {
 
 namespace {
 
-constexpr int kHeads = 64;
 constexpr int kThreads = 256;
-
-struct Stage1Args {
-  const uint16_t* q;
-  int64_t q_tok_stride, q_head_stride;
-  smla_kv kv;
-  const int32_t* table;
-  int64_t table_stride;
-  const int32_t* lens;
-  int32_t max_len;          // table_width * page size
-  int32_t table_width;
-  int32_t log2_page;
-  float scale_log2;         // softmax scale * log2(e): scores are kept in base 2
-  int32_t rows_per_split;
-  int32_t S;
-  int32_t H;
-  int32_t T;
-  float* part_o;            // fp32 path: [T][S][H][512]; bf16 path: bf16 in the packed order below
-  float* part_lse;          // [T][S][H], natural log
-  // page map: when `mapped` is set, the (page size 1) table holds request-relative
-  // positions, which the kernel resolves through the request's page-table row. map_req is
-  // always a valid [T] array (lens when unmapped), so its load needs no branch.
-  int32_t mapped;
-  const int32_t* map_req;
-  const int32_t* map_pt;
-  int64_t map_pt_stride;
-  const int32_t* map_seq;
-  int32_t map_R, map_pt_width, map_log2_page;
-  // outputs, written by stage 1 itself for a token whose rows fit one split (bf16 path)
-  void* out;
-  int64_t out_tok_stride, out_head_stride;
-  float* lse;
-  int64_t lse_tok_stride;
-  // merge inside stage 1 (bf16 q): the per-token words at the head of the workspace
-  // (nullptr: stage 2 merges), and how long a workgroup may wait for its token's other
-  // splits, in wall-clock ticks (0: never wait)
-  uint32_t* sync;
-  int32_t wait_ticks;
-  // union mode (grouped prefill), when > 0: the G = union_G queries of a group have H heads
-  // each (G * H = 128); workgroup t serves 64 / H of them (members m0 .. m0 + 64/H - 1 of
-  // group t / (G * H / 64)), its 64 heads being theirs in order. The table row and length are
-  // the group's union (entries = row | member bits << 24); the kernel keeps the entries that
-  // name one of its members, and each head attends only to its own member's. One split
-  // (S = 1); workgroups whose first member is past the last query do nothing.
-  int32_t union_G;
-  // decode, bf16 q: blocks of 64 heads per token (1, or 2 for H up to 128). Workgroups cover
-  // hblocks * T virtual tokens, block-major (virtual token b * T + t is block b of token t),
-  // each with 64 head slots; slots past the block's real heads read the block's last head
-  // and write nothing. Partials and merge words are per virtual token.
-  int32_t hblocks;
-  // dense paged decode of at most 64 (virtual) tokens, bf16 q: the workgroups plan the splits
-  // themselves from the tokens' lengths (balanced), with at least min_rows rows per split,
-  // for a device of `cus` compute units
-  int32_t balanced, min_rows, cus;
-};
 
 // Physical slot of position p of token t's table row, or -1 when masked.
 __device__ __forceinline__ int64_t slot_of(const Stage1Args& a, int t, int p) {
@@ -99,92 +43,11 @@ __device__ __forceinline__ int token_len(const Stage1Args& a, int t) {
   return n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
 }
 
-// Shared-memory layout of one gathered row: the row's 16-byte units, unit u stored at
-// position u ^ key(row), a permutation inside each aligned block of 8 units, so that a 32-row
-// chunk is a whole number of 64-lane x 16-byte direct-to-LDS load instructions with no padding.
-//   bf16 (1152-byte rows, the rows the MFMA loop reads): key = row & 7 spreads the rows that
-//     one operand read touches over the 64 LDS banks: the 16-byte score reads (16 consecutive
-//     rows at one unit) and the transposing value reads (rows 4g .. 4g+3 and 16 + 4g .. +3 at
-//     two units) are conflict-free (checked with the LDS bank-conflict counter on gfx950);
-//   fp8 (640-byte rows of codes and rotary values): key = 0. Only the conversion into bf16
-//     rows reads them, 16 consecutive lanes over the 16 units of one row, which meets no
-//     conflict in any order.
-template <int KV>
-struct Lay;
-template <>
-struct Lay<SMLA_BF16> {
-  static constexpr int kUnits = 72;      // 1152-byte row
-  static constexpr int kNBuf = 4;        // chunks in the LDS ring
-};
-template <>
-struct Lay<SMLA_FP8_E4M3> {
-  static constexpr int kUnits = 40;      // 512 e4m3 codes + 64 bf16 rotary values; scales live apart
-  static constexpr int kNBuf = 3;        // chunks in the LDS ring, beside two bf16 staging tiles
-};
-
-template <int KV>
-__device__ __forceinline__ int swz_key(int row) {
-  if constexpr (KV == SMLA_BF16) return row & 7;
-  else return 0;
-}
-template <int KV>
-__device__ __forceinline__ int swz(int row, int unit) { return unit ^ swz_key<KV>(row); }
-
-// Source of the gathers of masked rows (a row past the list's length, or a -1 entry):
-// the LDS tile then holds zeros there, so a zero softmax weight meets finite values.
-__device__ const uint4 kZeroRow[72] = {};
-
-// Workgroup barrier that waits for this wave's LDS operations only: the outstanding
-// direct-to-LDS gathers of later chunks stay in flight across it.
-__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Materialise v in a register here: the compiler otherwise sinks work whose result is only
-// needed later (past the MFMAs it is meant to run between).
-template <typename V>
-__device__ __forceinline__ void pin(V& v) { __asm__ volatile("" : "+v"(v)); }
-
-// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
-}
-// 16-byte direct-to-LDS gather: lane l's 16 bytes at `src` land at lds_wave_base + 16 l.
-// Issued through inline assembly on purpose: the compiler does not see a pending LDS
-// write, so it adds no wait for it before the LDS reads of other ring slots; the kernel
-// orders the ring itself (wait_chunks, then a barrier). M0 is set right here and nothing
-// else in these kernels reads it.
-__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base);
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
-}
-
-// 4-byte direct-to-LDS copy: lane l's word at `src` lands at lds_wave_base + 4 l.
-__device__ __forceinline__ void dma4(const void* src, char* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base);
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory");
-}
-
-// Wait until at most `chunks` chunks of `LOADS` gathers each are still in flight.
-template <int MAXC, int LOADS>
-__device__ __forceinline__ void wait_chunks(int chunks) {
-  if constexpr (MAXC > 0) {
-    if (chunks >= MAXC) { wait_vmcnt<MAXC * LOADS>(); return; }
-    wait_chunks<MAXC - 1, LOADS>(chunks);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
 // Stage 1 workgroup: 8 waves, two per SIMD. Wave w = (hq, x) with hq = w & 3, x = w >> 2
 // owns heads 16hq .. 16hq+15; for the scores it takes rows 16x .. 16x+15 of each chunk, for
 // the output it takes latent columns 256x .. 256x+255. Its partner w ^ 4 holds the other half.
 constexpr int kS1Waves = 8;
 constexpr int kS1Threads = 64 * kS1Waves;
-constexpr int kQLoads = 18;                 // 16-byte q pieces per lane: 16 heads x 72 units / 64 lanes
-constexpr int kAhead = 4;                   // LDS operand reads kept in flight ahead of the MFMAs
 #ifndef SMLA_PV_IN_A
 #define SMLA_PV_IN_A 4
 #endif
@@ -241,59 +104,6 @@ __device__ __forceinline__ void stage1_coords(int b, int T, int S, int& t, int& 
     s = b % S;
   }
 }
-
-// Max and sum over the four lanes c, 16 + c, 32 + c, 48 + c (the four 16-lane rows of the
-// wave): v_permlane16_swap exchanges rows 0 <-> 1 and 2 <-> 3 between its two operands,
-// v_permlane32_swap the two halves, so each returned pair holds both partners' values.
-__device__ __forceinline__ float max_rows(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_rows(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Wait until at most `chunks` chunks are in flight for this wave, which issues `hi` or `lo`
-// copies per chunk (a compile-time count either way; the choice is wave-uniform).
-template <int MAXC, int HI, int LO>
-__device__ __forceinline__ void wait_chunks_w(bool hi, int chunks) {
-  if (hi) wait_chunks<MAXC, HI>(chunks); else wait_chunks<MAXC, LO>(chunks);
-}
-
-
-// Per-lane LDS byte offsets of wave (hq, x)'s operand reads in a chunk of bf16 rows (the same
-// for every chunk; fp8 chunks are dequantised into bf16 rows before the loop reads them).
-//   ka[m]: score operand A = K[chunk row 16x + c][dims 32ks + 8g .. +7]: unit 4ks + g sits at
-//          4(ks ^ (key >> 2)) + (g ^ (key & 3)): base m = ks & 1, plus 64 ks
-//   vo[m]: P V operand B = V[rows 4g .. 4g+3, then 16 + 4g .. +3][column c of tile 16x + nt],
-//          two transposed 16-bit reads (j = 0, 1); the group's lane c points at row
-//          16j + 4g + c/4, columns 16(16x + nt) + 4(c%4) .. +3: unit 32x + 2nt + (c%4)/2,
-//          stored at 32x + 8(nt >> 2) + 2((nt & 3) ^ (key >> 1)) + (((c%4)/2) ^ (key & 1)):
-//          base vo[4j + (nt & 3)], plus 128 (nt >> 2)
-struct Offsets {
-  int ka[2];
-  int vo[8];
-  __device__ __forceinline__ Offsets(int x, int g, int c) {
-    constexpr int kRowBytes = Lay<SMLA_BF16>::kUnits * 16;
-    const int row = 16 * x + c, key = swz_key<SMLA_BF16>(row);
-    const int kh = (key >> 2) * 64;
-    ka[0] = row * kRowBytes + 16 * (g ^ (key & 3)) + kh;
-    ka[1] = row * kRowBytes + 16 * (g ^ (key & 3)) - kh;
-    const int b = (c & 3) >> 1;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = 16 * j + 4 * g + (c >> 2), k2 = swz_key<SMLA_BF16>(r);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        vo[4 * j + m] = r * kRowBytes + 512 * x + 32 * (m ^ (k2 >> 1)) + 16 * (b ^ (k2 & 1)) + 8 * (c & 1);
-    }
-  }
-};
 
 // One step of wave (hq, x) over chunks of bf16 rows: the scores of one chunk's rows
 // 16x .. 16x+15 (S^T tile: lane (g, c) gets rows 16x + 4g + v of head 16hq + c; 18 MFMAs on two
@@ -557,7 +367,7 @@ __device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int64_t
 // software pipelined: while it accumulates P V for chunk ci it computes the scores of
 // chunk ci + 1.
 
-template <int KV, bool UNION>
+template <int KV, bool UNION, bool BYIDX>
 __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a) {
   using L = Lay<KV>;
   constexpr int kRowBytes = L::kUnits * 16;
@@ -748,6 +558,14 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   // row strides fit 32 bits (a row is at most a few KB), so slot * stride is one 32x32->64 multiply
   const uint32_t lat8_stride32 = (uint32_t)a.kv.lat8_stride, rope16_stride32 = (uint32_t)a.kv.rope16_stride;
   const uint32_t row_stride32 = (uint32_t)a.kv.row_stride;
+  // BYIDX (a pool of at most 2^32 bytes whose gathered units sit in one row: bf16, or fp8
+  // with the rotary part right behind the codes in the same stride, as gathers_by_index
+  // decides): the rows are read by index through a buffer resource, so that a copy takes the
+  // slot as it is and a masked row (index -1) reads zeros. Otherwise each lane forms its
+  // 64-bit address.
+  const char* const rbase = kFp8 ? lat8 : (const char*)a.kv.rows;
+  const uint32_t rstride = kFp8 ? lat8_stride32 : row_stride32;
+  const u32x4 rrsrc = row_rsrc(rbase, rstride, (uint32_t)a.kv.num_slots);
 
   // gather chunk ci into ring slot ci % kNBuf: copy instruction i = 8k + w of a chunk puts
   // the chunk's 16-byte units 64i .. 64i+63 (row-major, unit positions swizzled) at bytes
@@ -758,7 +576,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   for (int k = 0; k < kLoadsHi; ++k) {
     const int pos = (k * kS1Waves + w) * 64 + lane;
     const int row = pos / L::kUnits, unit = swz<KV>(row, pos % L::kUnits);   // the swizzle is an involution
-    lpos[k] = row | (unit << 8);
+    lpos[k] = row | (unit << 12);                   // bits 8 and up: the unit's byte offset in the row
   }
   // a chunk's copies in two steps: src_of reads the slots and forms each copy's source
   // address (every slot is read before the first copy goes out: a copy's asm statement is
@@ -777,7 +595,11 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   auto fire = [&](const Copies& cp, int ci, int k) {
     if (!(k < kLoadsLo || hi)) return;
     const int32_t sl = umode && cp.slot[k] >= 0 ? cp.slot[k] & ((1 << SMLA_UNION_ROW_BITS) - 1) : cp.slot[k];
-    const int unit = lpos[k] >> 8;
+    if constexpr (BYIDX) {
+      dma16_row(rrsrc, (uint32_t)sl, (uint32_t)lpos[k] >> 8, kvbuf[ci % kNBuf] + (k * kS1Waves + w) * 1024);
+      return;
+    }
+    const int unit = lpos[k] >> 12;
     const bool live = sl >= 0;
     const uint32_t slot = live ? (uint32_t)sl : 0u;
     const char* src;
@@ -1465,6 +1287,26 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2_packed(Stage2Args a)
 
 }  // namespace
 
+namespace {
+// Whether stage 1 reads the pool's rows by index through a buffer resource (the BYIDX form):
+// a pool of at most 2^32 bytes, a row stride below 2^14 bytes, and for fp8 the rotary part
+// right behind the codes in the same row.
+bool gathers_by_index(const smla_kv& kv) {
+  const bool fp8 = kv.dtype == SMLA_FP8_E4M3;
+  const int64_t stride = fp8 ? kv.lat8_stride : kv.row_stride;
+  if (stride <= 0 || stride >= (1 << 14) || kv.num_slots > ((int64_t)1 << 32) / stride) return false;
+  return !fp8 || ((const char*)kv.rope16 == (const char*)kv.lat8 + 512 && kv.rope16_stride == kv.lat8_stride);
+}
+
+template <int KV, bool UNION>
+void launch_stage1(dim3 grid, hipStream_t stream, const Stage1Args& a) {
+  if (gathers_by_index(a.kv))
+    hipLaunchKernelGGL((decode_stage1_mfma<KV, UNION, true>), grid, dim3(kS1Threads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_stage1_mfma<KV, UNION, false>), grid, dim3(kS1Threads), 0, stream, a);
+}
+}  // namespace
+
 hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void* ws, hipStream_t stream,
                          int stages, const smla_page_map* map) {
   if (d.T == 0) return hipSuccess;
@@ -1523,9 +1365,9 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
     dim3 grid(plan.S * d.T, (d.H + 15) / 16);
     hipLaunchKernelGGL(decode_stage1_f32, grid, dim3(kThreads), 0, stream, a);
   } else if (d.kv.dtype == SMLA_BF16) {
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, false>), dim3(plan.grid), dim3(kS1Threads), 0, stream, a);
+    launch_stage1<SMLA_BF16, false>(dim3(plan.grid), stream, a);
   } else {
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, false>), dim3(plan.grid), dim3(kS1Threads), 0, stream, a);
+    launch_stage1<SMLA_FP8_E4M3, false>(dim3(plan.grid), stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !(stages & 2) || plan.fused) return e;   // fused: stage 1 has merged
@@ -1594,9 +1436,9 @@ hipError_t launch_union_decode(const smla_prefill_args& d, hipStream_t stream) {
   // 64 / H queries per workgroup, G * H / 64 workgroups per group
   const dim3 grid((unsigned)(((d.Q + d.G - 1) / d.G) * (d.G * d.H / kHeads)));
   if (d.kv.dtype == SMLA_BF16)
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_BF16, true>), grid, dim3(kS1Threads), 0, stream, a);
+    launch_stage1<SMLA_BF16, true>(grid, stream, a);
   else
-    hipLaunchKernelGGL((decode_stage1_mfma<SMLA_FP8_E4M3, true>), grid, dim3(kS1Threads), 0, stream, a);
+    launch_stage1<SMLA_FP8_E4M3, true>(grid, stream, a);
   return hipGetLastError();
 }
 
