@@ -49,13 +49,24 @@ __device__ __forceinline__ int token_len(const Stage1Args& a, int t) {
 constexpr int kS1Waves = 8;
 constexpr int kS1Threads = 64 * kS1Waves;
 #ifndef SMLA_PV_IN_A
-#define SMLA_PV_IN_A 4
+#define SMLA_PV_IN_A 2
 #endif
 constexpr int kPvA = SMLA_PV_IN_A;          // P V tiles of chunk ci computed with the scores of chunk ci + 1
+#ifndef SMLA_PV_PUB
+#define SMLA_PV_PUB 6
+#endif
+constexpr int kPvPub = SMLA_PV_PUB;         // P V tiles of chunk ci computed while chunk ci + 1's weights are formed
 #ifndef SMLA_PV_FP8
 #define SMLA_PV_FP8 4
 #endif
 constexpr int kPvF = SMLA_PV_FP8;           // fp8: P V tiles of chunk ci computed while chunk ci + 1 is converted
+
+// Two floats as nearest bf16 (ties to even), lo in the low half: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // The balanced plan of a dense paged decode of tv <= 64 virtual tokens (64-head blocks; virtual
 // token v is block v / T of token v % T), computed by one wave from the lengths alone, lane v for
@@ -360,11 +371,11 @@ __device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int64_t
 // Stage 1. The scores are computed transposed, S^T = K Q^T (chunk rows are the M dimension
 // of a 16x16x32 MFMA tile, heads the N dimension, K = 576), so that lane (g, c) holds head
 // c's scores for rows 4g .. 4g+3 of its half. The two partners swap their tiles through LDS,
-// after which each lane holds head c's eight scores for rows 4g + v and 16 + 4g + v: the
-// softmax statistics need only cross-lane moves inside the wave, and the eight weights are
-// the A operand of the P V product (16x16x32, K = the chunk's 32 rows taken in that order),
-// whose B operand the transposing LDS reads fetch in the same row order. The loop is
-// software pipelined: while it accumulates P V for chunk ci it computes the scores of
+// after which each lane holds head c's eight scores, for its own rows 16x + 4g + v and then
+// its partner's: the softmax statistics need only cross-lane moves inside the wave, and the
+// eight weights are the A operand of the P V product (16x16x32, K = the chunk's 32 rows taken
+// in that order), whose B operand the transposing LDS reads fetch in the same row order. The
+// loop is software pipelined: while it accumulates P V for chunk ci it computes the scores of
 // chunk ci + 1.
 
 template <int KV, bool UNION, bool BYIDX>
@@ -385,7 +396,10 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   __shared__ __attribute__((aligned(16))) int32_t slot_s[kMaxSplitRows];
   __shared__ int32_t page_s[kMaxSplitRows / 2 + 64];     // page ids of a split (page size >= 2)
   __shared__ __attribute__((aligned(16))) float scale_s[kFp8 ? kMaxSplitRows : 4];
-  __shared__ float sx[kS1Waves][4][64];                    // score tiles swapped between partners
+  __shared__ uint2 px[kS1Waves][64];                       // weights (bf16) swapped between partners
+  __shared__ float mx[kS1Waves][16];                       // the reference each wave's weights are relative to
+  __shared__ int fx[kS1Waves];                             // 1: that reference is the running max
+  __shared__ float lx[kS1Waves][16];                       // the partners' sums, at the end
   __shared__ int wcnt[kMaxSplitRows / kS1Threads][kS1Waves];   // union mode: kept entries per wave
 
   // t, s: the (virtual) token and split; rps rows per split, pbase the token's first partial,
@@ -660,97 +674,112 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
 
   const Offsets off(x, g, c);
   // P V tiles of chunk ci in iteration ci: fp8, tiles 0 .. kPv0 - 1 while chunk ci + 1 is
-  // converted, then (both) tiles kPv0 .. kPvS - 1 with the scores of chunk ci + 1, the rest
-  // with its softmax
+  // converted; then (both) tiles kPv0 .. kPvS - 1 with the scores of chunk ci + 1, tiles
+  // kPvS .. kPvP - 1 while its weights are formed and published, the rest after the exchange
   constexpr int kPv0 = kFp8 ? kPvF : 0;
   constexpr int kPvS = kFp8 ? kPvF : kPvA;
+  constexpr int kPvP = kPvS + kPvPub;
   static_assert(!kFp8 || kPv0 >= 3, "the conversion takes three steps");
+  static_assert(kPvPub >= 5 && 16 - kPvP >= 3, "the weights are formed in five steps and taken in three");
   f32x4 oacc[16];
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;        // head h0 + c; l_part: this lane's rows only
-  bf16x8 pa;                                    // softmax weights of the chunk being multiplied
   f32x4 sl, sr;
 
-  // Online softmax in base 2 for head h0 + c over chunk ci's 32 rows (both partners compute
-  // the same values). publish(ci) writes this wave's masked, scaled scores (rows 16x + 4g + v)
-  // to its exchange tile; after the barrier, piece(ci, k) for k = 0 .. 8 reads the partner's
-  // tile (then f[4j + v] is row 16j + 4g + v for both), updates the running max and sum, and
-  // leaves the weights that meet the rows' values in pa_next. The pieces run between the
-  // P V MFMAs of the previous chunk, so the matrix unit stays busy meanwhile; finish() then
-  // rescales O (after those MFMAs) when the running max moved. The max only moves when a
-  // score exceeds it by more than 2^8, so most chunks skip the rescale.
-  float sv[4], ex[4], f[8], mloc = 0.f, mn = 0.f, mn_safe = 0.f, alpha = 1.f, pv[8];
-  bool up = false;
-  float4 sc0 = make_float4(1.f, 1.f, 1.f, 1.f), sc1 = sc0;
-  bf16x8 pa_next;
-  auto publish = [&](int ci) {
-    const int4 lv = *(const int4*)(slot_s + ci * kChunk + 16 * x + 4 * g);
-    float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
-    if constexpr (kFp8) sc = *(const float4*)(scale_s + ci * kChunk + 16 * x + 4 * g);
-    const float raw[4] = {kFp8 ? sl[0] * sc.x + sr[0] : sl[0], kFp8 ? sl[1] * sc.y + sr[1] : sl[1],
-                          kFp8 ? sl[2] * sc.z + sr[2] : sl[2], kFp8 ? sl[3] * sc.w + sr[3] : sl[3]};
-    // a row counts for head h0 + c when its slot is valid and, in union mode, when it names
-    // the head's own member
-    const int mbit = SMLA_UNION_ROW_BITS + (umode ? (h0 + c) / uH : 0);
-    auto ok = [&](int e) { return e >= 0 && (!umode || ((e >> mbit) & 1)); };
-    sv[0] = ok(lv.x) ? raw[0] * a.scale_log2 : -INFINITY;
-    sv[1] = ok(lv.y) ? raw[1] * a.scale_log2 : -INFINITY;
-    sv[2] = ok(lv.z) ? raw[2] * a.scale_log2 : -INFINITY;
-    sv[3] = ok(lv.w) ? raw[3] * a.scale_log2 : -INFINITY;
-    // the partner read this wave's previous tile before it reached the barrier that this
-    // wave passed last, so the slot is free
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sx[w][v][lane] = sv[v];
-  };
-  auto piece = [&](int ci, int k) {
+  // Online softmax in base 2 for head h0 + c. Both partners hold the same running max m_run;
+  // each forms the weights of its own 16 rows of a chunk and the pair swaps them, so that each
+  // lane ends with head c's eight weights (its own rows 16x + 4g + v, then its partner's
+  // 16(1 - x) + 4g + v), the A operand of the P V product.
+  //   pub(ci, k), k = 0 .. 4, between P V MFMAs of chunk ci - 1: the masked, scaled scores of
+  //     the own rows; their weights exp2(s - m_run) when no score of the wave's heads passes
+  //     m_run by more than 2^8 (then every weight is at most 2^8), else relative to the head's
+  //     own-row max where that one passes it; the weights (times the row scale for fp8) as
+  //     bf16 to the exchange, with the reference they are relative to.
+  //   absb(k), k = 0 .. 2, after the barrier: the partner's weights and reference. When both
+  //     are relative to m_run (nearly every chunk once the first has set the max) the weights
+  //     are used as they are; otherwise both sides scale each half by 2^(ref - new max) from
+  //     the same bf16 values, so the partners still agree to the bit, and O and the sum are
+  //     rescaled (in finish, after the P V MFMAs of chunk ci - 1).
+  // Each lane's sum l_own covers its own rows; the partners add theirs at the end.
+  float m_run = -INFINITY, l_own = 0.f, l_next = 0.f, mn = -INFINITY, alpha = 1.f;
+  float sv[4], pown[4], psum = 0.f, m_use = 0.f, m_par = 0.f;
+  int4 lv = make_int4(-1, -1, -1, -1);
+  float4 sco = make_float4(1.f, 1.f, 1.f, 1.f);
+  uint2 pw = make_uint2(0u, 0u), ppw = make_uint2(0u, 0u);
+  int pfast = 1;
+  bool wfast = true, up = false;
+  bf16x8 pa, pa_next;
+  auto pub = [&](int ci, int k) {
     if (k == 0) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) ex[v] = sx[w ^ 4][v][lane];
-      if constexpr (kFp8) {
-        sc0 = *(const float4*)(scale_s + ci * kChunk + 4 * g);
-        sc1 = *(const float4*)(scale_s + ci * kChunk + 16 + 4 * g);
-      }
+      lv = *(const int4*)(slot_s + ci * kChunk + 16 * x + 4 * g);
+      if constexpr (kFp8) sco = *(const float4*)(scale_s + ci * kChunk + 16 * x + 4 * g);
+    } else if (k == 1) {
+      const float raw[4] = {kFp8 ? sl[0] * sco.x + sr[0] : sl[0], kFp8 ? sl[1] * sco.y + sr[1] : sl[1],
+                            kFp8 ? sl[2] * sco.z + sr[2] : sl[2], kFp8 ? sl[3] * sco.w + sr[3] : sl[3]};
+      // a row counts for head h0 + c when its slot is valid and, in union mode, when it names
+      // the head's own member
+      const int mbit = SMLA_UNION_ROW_BITS + (umode ? (h0 + c) / uH : 0);
+      auto ok = [&](int e) { return e >= 0 && (!umode || ((e >> mbit) & 1)); };
+      sv[0] = ok(lv.x) ? raw[0] * a.scale_log2 : -INFINITY;
+      sv[1] = ok(lv.y) ? raw[1] * a.scale_log2 : -INFINITY;
+      sv[2] = ok(lv.z) ? raw[2] * a.scale_log2 : -INFINITY;
+      sv[3] = ok(lv.w) ? raw[3] * a.scale_log2 : -INFINITY;
+      wfast = !__any(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) > m_run + 8.0f);
     } else if (k == 2) {
+      m_use = m_run;
+      if (!wfast) {
+        // (also the first rows, with m_run = -inf)
+        const float mo = max_rows(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+        if (mo > m_run + 8.0f) m_use = mo;
+      }
+      const float ms = m_use == -INFINITY ? 0.f : m_use;   // no finite score: every weight is 0
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        f[v] = x == 0 ? sv[v] : ex[v];
-        f[4 + v] = x == 0 ? ex[v] : sv[v];
+        pown[v] = __builtin_amdgcn_exp2f(sv[v] - ms);
+        pin(pown[v]);
       }
-      mloc = f[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mloc = fmaxf(mloc, f[i]);
     } else if (k == 3) {
-      mloc = max_rows(mloc);
+      psum = (pown[0] + pown[1]) + (pown[2] + pown[3]);
+      // the weight that meets row r's values is p * scale(r)
+      const float q0 = kFp8 ? pown[0] * sco.x : pown[0], q1 = kFp8 ? pown[1] * sco.y : pown[1];
+      const float q2 = kFp8 ? pown[2] * sco.z : pown[2], q3 = kFp8 ? pown[3] * sco.w : pown[3];
+      pw = make_uint2(cvt_bf16x2(q0, q1), cvt_bf16x2(q2, q3));
+      pin(pw.x); pin(pw.y);
     } else if (k == 4) {
-      // branch-free: with no finite score yet (mn = -inf) every f is -inf, and exp2 of
-      // f - 0 gives the zero weights; alpha is 1 when the max stays and 0 from -inf
-      up = mloc > m_run + 8.0f;
-      mn = up ? mloc : m_run;
-      mn_safe = mn == -INFINITY ? 0.f : mn;
-      alpha = __builtin_amdgcn_exp2f(m_run - mn_safe);
-    } else if (k == 5 || k == 6) {
-#pragma unroll
-      for (int i = 4 * (k - 5); i < 4 * (k - 4); ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(f[i] - mn_safe);
-        pin(pv[i]);
+      // the partner took this wave's previous weights before it reached the barrier that this
+      // wave passed last, so the slots are free
+      px[w][lane] = pw;
+      if (g == 0) mx[w][c] = m_use;
+      if (lane == 0) fx[w] = wfast ? 1 : 0;
+    }
+  };
+  auto scaled = [](uint32_t wd, float f) {
+    return cvt_bf16x2(bf16_to_f32(wd & 0xffffu) * f, bf16_to_f32(wd >> 16) * f);
+  };
+  auto absb = [&](int k) {
+    if (k == 0) {
+      ppw = px[w ^ 4][lane];
+      m_par = mx[w ^ 4][c];
+      pfast = fx[w ^ 4];
+    } else if (k == 2) {
+      uint2 a0 = pw, a1 = ppw;
+      if (wfast && __builtin_amdgcn_readfirstlane(pfast) != 0) {
+        mn = m_run;
+        up = false;
+        l_next = l_own + psum;
+      } else {
+        // the new running max of head h0 + c; each half's factor 2^(ref - mn) (0 for a half
+        // with no finite score yet), O's 2^(m_run - mn)
+        mn = fmaxf(m_use, m_par);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float fo = __builtin_amdgcn_exp2f(m_use - ms), fp = __builtin_amdgcn_exp2f(m_par - ms);
+        alpha = __builtin_amdgcn_exp2f(m_run - ms);
+        up = mn != m_run;
+        a0 = make_uint2(scaled(pw.x, fo), scaled(pw.y, fo));
+        a1 = make_uint2(scaled(ppw.x, fp), scaled(ppw.y, fp));
+        l_next = l_own * alpha + psum * fo;
       }
-    } else if (k == 7) {
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) psum += pv[i];
-      l_part = l_part * alpha + psum;
-      if constexpr (kFp8) {
-        // the weight that meets row r's values is p * scale(r)
-        pv[0] *= sc0.x; pv[1] *= sc0.y; pv[2] *= sc0.z; pv[3] *= sc0.w;
-        pv[4] *= sc1.x; pv[5] *= sc1.y; pv[6] *= sc1.z; pv[7] *= sc1.w;
-      }
-    } else if (k == 8) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pa_next[i] = (__bf16)pv[i];
-      uint4 pw = __builtin_bit_cast(uint4, pa_next);
-      pin(pw.x); pin(pw.y); pin(pw.z); pin(pw.w);
-      pa_next = __builtin_bit_cast(bf16x8, pw);
+      pa_next = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
     }
   };
   auto finish = [&]() {
@@ -765,6 +794,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
         for (int v = 0; v < 4; ++v) oacc[nt][v] *= ah[v];
     }
     m_run = mn;
+    l_own = l_next;
     pa = pa_next;
   };
 
@@ -935,15 +965,17 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
 
     // scores and weights of chunk 0
     chunk_step<true, false, kFp8>(rows_of(0), rows_of(0), off, qf, sl, sr, pa, oacc, no_hook);
-    publish(0);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) pub(0, k);
     lds_barrier();
 #pragma unroll
-    for (int k = 0; k <= 8; ++k) piece(0, k);
+    for (int k = 0; k < 3; ++k) absb(k);
     finish();
 
-    // iteration ci, in two phases between three barriers: the scores of chunk ci + 1 (phase
-    // A, with the gathers of a later chunk spread over its MFMAs), the exchange of score
-    // tiles, then O += P V over chunk ci with the softmax of chunk ci + 1 in between (phase C).
+    // iteration ci, in two phases between two barriers: the scores of chunk ci + 1 and its
+    // weights (phase A, with the gathers of a later chunk spread over its MFMAs and the
+    // weights formed between P V MFMAs of chunk ci), the exchange of weights, then the rest of
+    // O += P V over chunk ci with the partner's weights taken in between (phase C).
     // bf16: the barrier at the top publishes chunk ci + 1 and tells that every wave is done
     // with the ring slot of chunk ci - 1, which the iteration refills with chunk ci + kNBuf - 1.
     // fp8: the barrier at the top publishes chunk ci + 1 and frees the staging tile of chunk
@@ -976,11 +1008,10 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       };
       chunk_step<true, (kPvS > kPv0), kFp8, decltype((gathers)), kPv0, kPvS>(rows_of(ci + 1), rows_of(ci), off, qf, sl, sr,
                                                                             pa, oacc, gathers);
-      publish(ci + 1);
+      auto pubs = [&](int k) { pub(ci + 1, k); };
+      chunk_step<false, true, kFp8, decltype((pubs)), kPvS, kPvP>(rows_of(ci), rows_of(ci), off, qf, sl, sr, pa, oacc, pubs);
       lds_barrier();
-      auto pieces = [&](int k) { piece(ci + 1, k); };
-      chunk_step<false, true, kFp8, decltype((pieces)), kPvS, 16>(rows_of(ci), rows_of(ci), off, qf, sl, sr, pa, oacc,
-                                                                 pieces);
+      chunk_step<false, true, kFp8, decltype((absb)), kPvP, 16>(rows_of(ci), rows_of(ci), off, qf, sl, sr, pa, oacc, absb);
       finish();
     }
     chunk_step<false, true, kFp8>(rows_of(nchunks - 1), rows_of(nchunks - 1), off, qf, sl, sr, pa, oacc, no_hook);
@@ -988,7 +1019,13 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
 
   // ---- normalise. A token whose rows fit one split is finished here; the others leave
   // their partials for stage 2.
-  const float l = sum_rows(l_part);              // head h0 + c, all rows of the split
+  // head h0 + c, all rows of the split: this wave's rows, then the partner's added in the same
+  // order on both sides
+  const float lw = sum_rows(l_own);
+  if (g == 0) lx[w][c] = lw;
+  lds_barrier();
+  const float lpar = lx[w ^ 4][c];
+  const float l = x == 0 ? lw + lpar : lpar + lw;
   const float lse_c = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
   const float inv_c = l > 0.f ? 1.0f / l : 0.0f;
   float inv[4];

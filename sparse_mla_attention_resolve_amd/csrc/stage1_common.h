@@ -198,9 +198,10 @@ __device__ __forceinline__ void wait_chunks_w(bool hi, int chunks) {
 // for every chunk; fp8 chunks are dequantised into bf16 rows before the loop reads them).
 //   ka[m]: score operand A = K[chunk row 16x + c][dims 32ks + 8g .. +7]: unit 4ks + g sits at
 //          4(ks ^ (key >> 2)) + (g ^ (key & 3)): base m = ks & 1, plus 64 ks
-//   vo[m]: P V operand B = V[rows 4g .. 4g+3, then 16 + 4g .. +3][column c of tile 16x + nt],
-//          two transposed 16-bit reads (j = 0, 1); the group's lane c points at row
-//          16j + 4g + c/4, columns 16(16x + nt) + 4(c%4) .. +3: unit 32x + 2nt + (c%4)/2,
+//   vo[m]: P V operand B = V[the wave's own rows 16x + 4g .. +3, then its partner's rows
+//          16(1 - x) + 4g .. +3][column c of tile 16x + nt], two transposed 16-bit reads
+//          (j = 0, 1); the group's lane c points at row 16(j ^ x) + 4g + c/4, columns
+//          16(16x + nt) + 4(c%4) .. +3: unit 32x + 2nt + (c%4)/2,
 //          stored at 32x + 8(nt >> 2) + 2((nt & 3) ^ (key >> 1)) + (((c%4)/2) ^ (key & 1)):
 //          base vo[4j + (nt & 3)], plus 128 (nt >> 2)
 struct Offsets {
@@ -215,7 +216,7 @@ struct Offsets {
     const int b = (c & 3) >> 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int r = 16 * j + 4 * g + (c >> 2), k2 = swz_key<SMLA_BF16>(r);
+      const int r = 16 * (j ^ x) + 4 * g + (c >> 2), k2 = swz_key<SMLA_BF16>(r);
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         vo[4 * j + m] = r * kRowBytes + 512 * x + 32 * (m ^ (k2 >> 1)) + 16 * (b ^ (k2 & 1)) + 8 * (c & 1);
