@@ -62,8 +62,8 @@ def section(torch, name):
             torch.cuda.nvtx.range_pop()
 
 
-KERNEL_SOURCES = ["sparse_mla_attention_resolve_amd/csrc/decode.hip", "sparse_mla_attention_resolve_amd/csrc/smla_device.h",
-                  "sparse_mla_attention_resolve_amd/csrc/smla_internal.h"]
+KERNEL_SOURCES = ["sparse_mla_attention_resolve_amd/csrc/decode.hip", "sparse_mla_attention_resolve_amd/csrc/stage1_common.h",
+                  "sparse_mla_attention_resolve_amd/csrc/smla_device.h", "sparse_mla_attention_resolve_amd/csrc/smla_internal.h"]
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernels_hbm_traffic.md")
 
 
@@ -1069,7 +1069,7 @@ def main():
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = "sparse_mla_attention_resolve_amd/csrc/"
 ALL_KERNEL_SOURCES = [CSRC + f for f in ("decode.hip", "union.hip", "resolve.hip", "kv_write.hip", "prefill.hip",
-                                          "abi.hip", "smla_device.h", "smla_internal.h")] + ["include/smla.h"]
+                                          "abi.hip", "stage1_common.h", "smla_device.h", "smla_internal.h")] + ["include/smla.h"]
 # the commands whose output the summaries reduce (run from the repository root); the summary
 # documents quote them
 BENCH_TRACE = "python3 bench.py --steps 30 --warmup 5 --no-cpu-baseline"
@@ -1293,7 +1293,7 @@ def summarize_traffic(fd: str, wd: str) -> None:
          "copy y = x * 1 over 256 MiB of fp32: 262,144 KiB read and 262,144 KiB written, which calibrates each "
          "counter). From the repository root:", ""]
     L += _fmt_cmds("traffic", [fd, wd])
-    L += [f"Kernel source sha256 (decode.hip + smla_device.h + smla_internal.h): `{sha}`", "",
+    L += [f"Kernel source sha256 (decode.hip + stage1_common.h + smla_device.h + smla_internal.h): `{sha}`", "",
           f"Calibration: FETCH_SIZE reads {fe['copy']['FETCH_SIZE']:.1f} KiB for the copy's 262,144 KiB of reads "
           f"(scale {sf:.4f}); WRITE_SIZE reads {wr['copy']['WRITE_SIZE']:.1f} KiB for its 262,144 KiB of writes "
           f"(scale {sw:.4f}).", "",
@@ -1336,7 +1336,7 @@ def summarize_sq(da: str, db: str) -> None:
     L = ["# Shader-sequencer counters: bf16 and fp8 decode, grouped prefill (MI355X)", "",
          "Two counter passes (eight SQ counters each) over the same short bench run. From the repository root:", ""]
     L += _fmt_cmds("sq", [da, db])
-    L += [f"Kernel source sha256 (decode.hip + smla_device.h + smla_internal.h): `{sha}`", "",
+    L += [f"Kernel source sha256 (decode.hip + stage1_common.h + smla_device.h + smla_internal.h): `{sha}`", "",
           "Per-dispatch means: `decode bf16` = `decode_stage1_mfma<bf16>` on bf16 batch 32 (every form the bench runs); "
           "`decode fp8` = `decode_stage1_mfma<fp8>` on fp8 batch 64; `union (prefill)` = "
           "`decode_stage1_mfma<bf16, union>` on grouped prefill Q 8192 (G 2, 64 heads). Counter values are the device "
@@ -1391,13 +1391,13 @@ def summarize_profile(argv) -> None:
 
 def split_sweep_markdown(res) -> str:
     cols = sorted({S for v in res.values() for S in v["us"]})
-    sha = sources_sha256([CSRC + f for f in ("decode.hip", "smla_device.h", "smla_internal.h", "abi.hip")])
+    sha = sources_sha256([CSRC + f for f in ("decode.hip", "stage1_common.h", "smla_device.h", "smla_internal.h", "abi.hip")])
     L = ["# Decode step against the split count (MI355X, one GPU)", "",
          "Cold steps (1 GiB read before each, median) of `smla_sparse_decode` at top-k 2048, 64 heads, over a "
          "2^20-slot pool of random rows, for each batch size and cache format, at every split count from the fewest "
          "(a split holds at most 1,024 rows) to one 32-row chunk per split. From the repository root:", "",
          "```", "python3 bench.py --split-sweep > profiles/decode_split_sweep.md", "```", "",
-         f"Source sha256 (decode.hip + smla_device.h + smla_internal.h + abi.hip): `{sha}`", "",
+         f"Source sha256 (decode.hip + stage1_common.h + smla_device.h + smla_internal.h + abi.hip): `{sha}`", "",
          "`auto` is the split count the library picks when `num_splits` is 0. Step time in microseconds.", "",
          "| cache | T | auto S | auto us | best S | best us | " + " | ".join(f"S={S}" for S in cols) + " |",
          "|---" * (6 + len(cols)) + "|"]
@@ -1409,7 +1409,7 @@ def split_sweep_markdown(res) -> str:
 
 
 def overlap_sweep_markdown(res, steps) -> str:
-    sha = sources_sha256([CSRC + f for f in ("decode.hip", "union.hip", "smla_device.h", "smla_internal.h")])
+    sha = sources_sha256([CSRC + f for f in ("decode.hip", "union.hip", "stage1_common.h", "smla_device.h", "smla_internal.h")])
     L = ["# Grouped prefill against per-query decode, by list overlap (MI355X, one GPU)", "",
          "4,096 queries with lists of 2,048 slots over a 24,576-slot bf16 cache of random rows (the grouped-prefill "
          "configuration's pool). Queries come in groups of G with H = 128 / G heads; a fraction `overlap` of each list "
@@ -1418,7 +1418,7 @@ def overlap_sweep_markdown(res, steps) -> str:
          "- grouped: `smla_build_group_union` + `smla_grouped_prefill`;",
          "- alone: `smla_sparse_decode` over the same lists (page size 1), every query attending its own rows.", "",
          "From the repository root:", "", "```", "python3 bench.py --overlap-sweep > profiles/grouped_prefill_overlap_sweep.md",
-         "```", "", f"Source sha256 (decode.hip + union.hip + smla_device.h + smla_internal.h): `{sha}`", "",
+         "```", "", f"Source sha256 (decode.hip + union.hip + stage1_common.h + smla_device.h + smla_internal.h): `{sha}`", "",
          "| G | H | overlap | union rows / W | grouped us | alone us | speedup |", "|---|---|---|---|---|---|---|"]
     for (G, ov), v in res.items():
         L.append(f"| {G} | {128 // G} | {ov:.2f} | {v['union_per_list']:.2f} | {v['grouped_us']:.0f} | "
