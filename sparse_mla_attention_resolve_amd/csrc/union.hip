@@ -120,8 +120,18 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
     for (int i = 0; i < K; ++i) {
       const int32_t mj = entry(i);
       const int m = mj >> 16, j = mj & 0xffff;
-      const int q = min(g * G + min(max(m, 0), G - 1), Q - 1);
-      raw[i] = mj >= 0 ? slots[(int64_t)q * slots_stride + j] : -1;
+      // the group's member m, or its last query for a short last group. With 16 entries per
+      // thread the offsets from the group's first list are 32-bit (they span G * slots_stride
+      // < 2^31 entries): the 64-bit addresses of all 16 loads in flight spilled registers (97
+      // against 61 us for 8-query groups of 2,048 entries); with fewer entries the 64-bit form
+      // is faster
+      if constexpr (K >= 16) {
+        const int mq = min(min(max(m, 0), G - 1), Q - 1 - g * G);
+        raw[i] = mj >= 0 ? (slots + (int64_t)g * G * slots_stride)[(uint32_t)(mq * (int)slots_stride + j)] : -1;
+      } else {
+        const int q = min(g * G + min(max(m, 0), G - 1), Q - 1);
+        raw[i] = mj >= 0 ? slots[(int64_t)q * slots_stride + j] : -1;
+      }
     }
     // a vector load (a scalar one would be waited for at the next LDS barrier)
     const bool member = lane < G && g * G + lane < Q;
@@ -151,12 +161,14 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
       if (key[i] >= 0) atomicOr(&lds[(key[i] & 0xffffff) >> 5], 1u << (key[i] & 31));
     lds_barrier();
     // set bits per block, and their prefix inside the wave's range: round k covers blocks
-    // b_lo + 64k + lane (at most 8 rounds: 2^20 rows are 8,192 blocks over 16 waves); the
-    // rounds' reads all go out first and their scans are independent
+    // b_lo + 64k + lane (at most 8 rounds: 2^20 rows are 8,192 blocks over 16 waves; 2 for the
+    // lists of more than 8,192 entries, whose pools stay below 2^18 rows); the rounds' reads all
+    // go out first and their scans are independent
+    constexpr int kRounds = K >= 16 ? 2 : 8;
     const int b_lo = wv * per_wave, b_hi = min(b_lo + per_wave, nblocks);
-    int c[8], incl[8];
+    int c[kRounds], incl[kRounds];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < kRounds; ++k) {
       const int b = b_lo + 64 * k + lane;
       c[k] = 0;
       if (b < b_hi) {
@@ -166,7 +178,7 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
     }
     int run = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < kRounds; ++k) {
       incl[k] = wave_inclusive_sum(c[k]) + run;
       run = __builtin_amdgcn_readlane(incl[k], 63);
     }
@@ -179,7 +191,7 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
       total += wave_tot[k];
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < kRounds; ++k) {
       const int b = b_lo + 64 * k + lane;
       if (b < b_hi) pre[b] = (uint16_t)(off + incl[k] - c[k]);
     }
@@ -386,8 +398,12 @@ hipError_t launch_union(const int32_t* slots, int64_t slots_stride, const int32_
   const int n = G * W, nblocks = (int)((std::min<int64_t>(num_slots, kBitmapSlots) + 127) >> 7);
   const size_t lds = (size_t)(std::max(4 * nblocks, n) + ((n + 3) >> 2)) * 4 + (size_t)nblocks * 2;
   // the bit map, the member bytes and the block counts must fit one compute unit's LDS beside
-  // the kernel's own (a 2^20-row pool with 16,384 list entries per group does not: the sort)
-  if (num_slots <= (n > 8192 ? (1 << 18) - 1 : kBitmapSlots) && lds + 1024 <= 160u * 1024u) {
+  // the kernel's own (a 2^20-row pool with 16,384 list entries per group does not: the sort);
+  // lists of more than 8,192 entries (16 per thread) take pools below 2^18 rows, which their
+  // packed keys and two counting rounds assume; a group's list entries must sit within 2^31
+  // entries of its first (32-bit offsets)
+  if (num_slots <= (n > 8192 ? (1 << 18) - 1 : kBitmapSlots) && lds + 1024 <= 160u * 1024u &&
+      (int64_t)G * slots_stride < ((int64_t)1 << 31)) {
     // as many workgroups as fit the compute units at once (registers and LDS decide)
 #define SMLA_UNION_BITMAP(K)                                                                                        \
   do {                                                                                                              \

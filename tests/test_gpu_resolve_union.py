@@ -106,6 +106,23 @@ def test_union_golden():
         assert [int(e) for e in enc[0, :n]] == ents, line
 
 
+@pytest.mark.parametrize("G,ns", [(2, 5000), (8, 5000), (8, 262143), (4, 1 << 20)])
+def test_union_strided_lists(G, ns):
+    """Lists read from a column slice of a wider table (row stride W + 37), both builders."""
+    rng = np.random.default_rng(G * 131 + ns % 977)
+    Q, W = 13, 2048 if G != 4 else 1024
+    wide = np.full((Q, W + 37), 77, np.int32)
+    for q in range(Q):
+        wide[q, :W] = rng.choice(ns, size=W, replace=False)
+    wide[3, 100:200] = -1
+    valid = rng.integers(0, W + 1, size=Q).astype(np.int32)
+    t = _t(wide)[:, :W]
+    assert t.stride(0) == W + 37
+    enc, lens = smla.smla_build_group_union(t, _t(valid), G, ns)
+    enc_o, lens_o = oracle.group_union(wide[:, :W], valid, G, ns)
+    _compare_union(enc.cpu().numpy().view(np.uint32), lens.cpu().numpy(), enc_o, lens_o)
+
+
 @pytest.mark.parametrize("G", [2, 4, 8])
 @pytest.mark.parametrize("Q", [1, 7, 64])
 @pytest.mark.parametrize("ns", [5000, 262143, 262144, 1 << 20, (1 << 20) + 1, 3000000])
