@@ -370,13 +370,13 @@ __device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int64_t
 
 // Stage 1. The scores are computed transposed, S^T = K Q^T (chunk rows are the M dimension
 // of a 16x16x32 MFMA tile, heads the N dimension, K = 576), so that lane (g, c) holds head
-// c's scores for rows 4g .. 4g+3 of its half. The two partners swap their tiles through LDS,
-// after which each lane holds head c's eight scores, for its own rows 16x + 4g + v and then
-// its partner's: the softmax statistics need only cross-lane moves inside the wave, and the
-// eight weights are the A operand of the P V product (16x16x32, K = the chunk's 32 rows taken
-// in that order), whose B operand the transposing LDS reads fetch in the same row order. The
-// loop is software pipelined: while it accumulates P V for chunk ci it computes the scores of
-// chunk ci + 1.
+// c's scores for rows 4g .. 4g+3 of its half. Each wave turns them into weights and the two
+// partners swap those through LDS, after which each lane holds head c's eight weights, for its
+// own rows 16x + 4g + v and then its partner's: the softmax statistics need only cross-lane
+// moves inside the wave, and the eight weights are the A operand of the P V product (16x16x32,
+// K = the chunk's 32 rows taken in that order), whose B operand the transposing LDS reads
+// fetch in the same row order. The loop is software pipelined: while it accumulates P V for
+// chunk ci it computes the scores and weights of chunk ci + 1.
 
 template <int KV, bool UNION, bool BYIDX>
 __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a) {
@@ -1436,43 +1436,8 @@ hipError_t launch_decode(const smla_decode_args& d, const DecodePlan& plan, void
   return hipGetLastError();
 }
 
-hipError_t launch_union_decode(const smla_prefill_args& d, hipStream_t stream) {
-  if (d.Q == 0) return hipSuccess;
-  Stage1Args a = {};
-  a.q = (const uint16_t*)d.q;
-  a.q_tok_stride = d.q_tok_stride;
-  a.q_head_stride = d.q_head_stride;
-  a.kv = d.kv;
-  a.table = (const int32_t*)d.enc;
-  a.table_stride = d.enc_stride;
-  a.lens = d.lens;                             // [groups]: read at the token's group
-  a.max_len = d.enc_width;
-  a.table_width = d.enc_width;
-  a.log2_page = 0;
-  a.scale_log2 = d.scale * kLog2e;
-  a.rows_per_split = kMaxSplitRows;            // the segment size; one split per query
-  a.S = 1;
-  a.H = d.H;
-  a.T = d.Q;
-  a.part_o = nullptr;
-  a.part_lse = nullptr;
-  a.mapped = 0;
-  a.map_req = d.lens;                          // a valid array at the group index (unused)
-  a.out = d.out;
-  a.out_tok_stride = d.out_tok_stride;
-  a.out_head_stride = d.out_head_stride;
-  a.lse = d.lse;
-  a.lse_tok_stride = d.lse_tok_stride;
-  a.sync = nullptr;
-  a.wait_ticks = 0;
-  a.union_G = d.G;
-  a.hblocks = 1;
-  a.balanced = 0;
-  a.min_rows = kChunk;
-  a.cus = 0;
-  // 64 / H queries per workgroup, G * H / 64 workgroups per group
-  const dim3 grid((unsigned)(((d.Q + d.G - 1) / d.G) * (d.G * d.H / kHeads)));
-  if (d.kv.dtype == SMLA_BF16)
+hipError_t launch_stage1_union(const Stage1Args& a, dim3 grid, hipStream_t stream) {
+  if (a.kv.dtype == SMLA_BF16)
     launch_stage1<SMLA_BF16, true>(grid, stream, a);
   else
     launch_stage1<SMLA_FP8_E4M3, true>(grid, stream, a);

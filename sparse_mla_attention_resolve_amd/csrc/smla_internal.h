@@ -62,10 +62,6 @@ hipError_t launch_union(const int32_t* slots, int64_t slots_stride, const int32_
 
 hipError_t launch_prefill(const smla_prefill_args& a, hipStream_t stream);
 
-// Grouped prefill through the decode stage-1 kernel in union mode: G * H / 64 workgroups per
-// group, each serving 64 / H of its queries over the group's union.
-hipError_t launch_union_decode(const smla_prefill_args& a, hipStream_t stream);
-
 // Zero-fill bytes / 16 16-byte words at p (a kernel, so it may be captured in a graph).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 

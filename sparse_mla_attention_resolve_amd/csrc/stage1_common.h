@@ -1,6 +1,6 @@
-// Device pieces shared by the stage-1 kernels (the decode kernel and the grouped-prefill
-// kernel): their argument block, the LDS row layout of a gathered chunk, direct-to-LDS copies
-// and their waits, the per-lane MFMA operand offsets and the cross-row reductions.
+// The stage-1 kernel's pieces (decode, and grouped prefill in union mode): its argument block
+// and launch entry for the prefill path, the LDS row layout of a gathered chunk, direct-to-LDS
+// copies and their waits, the per-lane MFMA operand offsets and the cross-row reductions.
 #pragma once
 
 #include "smla_device.h"
@@ -8,10 +8,9 @@
 
 namespace smla {
 
-namespace {
-
 constexpr int kHeads = 64;                  // head slots of a stage-1 workgroup (four 16-row MFMA tiles)
 
+// The stage-1 kernel's argument block (decode, dense paged decode and grouped prefill).
 struct Stage1Args {
   const uint16_t* q;
   int64_t q_tok_stride, q_head_stride;
@@ -65,6 +64,12 @@ struct Stage1Args {
   // for a device of `cus` compute units
   int32_t balanced, min_rows, cus;
 };
+
+// Launches the stage-1 kernel in union mode (grouped prefill) over `grid` workgroups, for the
+// cache format of a.kv (decode.hip).
+hipError_t launch_stage1_union(const Stage1Args& a, dim3 grid, hipStream_t stream);
+
+namespace {
 
 // Shared-memory layout of one gathered row: the row's 16-byte units, unit u stored at
 // position u ^ key(row), a permutation inside each aligned block of 8 units, so that a 32-row
