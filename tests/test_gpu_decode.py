@@ -292,6 +292,37 @@ def test_topk_fused_masks(splits):
 
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_topk_requests_out_of_order(kv_dtype):
+    """Tokens whose requests are not their own indices (a decode batch usually holds one token
+    per request, in order): permuted and repeated requests through short page-table rows, the
+    fused path against resolve + decode and the oracle."""
+    rng = np.random.default_rng(41)
+    T, W, R, P, ptw, pages = 7, 512, 5, 16, 40, 300
+    num_slots = pages * P
+    page_table = np.stack([rng.permutation(pages)[:ptw] for _ in range(R)]).astype(np.int32)
+    seq_lens = np.array([600, 640, 333, 500, 17], np.int32)
+    tok_req = np.array([3, 0, 4, 1, 1, 2, 0], np.int32)
+    idx = np.stack([rng.choice(640, size=W, replace=False) for _ in range(T)]).astype(np.int32)
+    valid = np.array([512, 400, 512, 512, 100, 512, 512], np.int32)
+    q = wl.f32_to_bf16_bits(rng.standard_normal((T, 64, 576)).astype(np.float32) * 0.5)
+    live = np.arange(num_slots, dtype=np.int32)
+    vals = rng.standard_normal((num_slots, 576)).astype(np.float32) * (1.0 if kv_dtype == "fp8" else 0.5)
+    kv, pool = _pools(live, vals, num_slots, kv_dtype)
+    qt = gc.q_tensor(q, "bf16")
+    args = (_t(idx), _t(valid), _t(tok_req), _t(page_table), _t(seq_lens))
+    slots = smla.smla_resolve_slots(*args, P)
+    oslots = oracle.resolve_slots(idx, valid, tok_req, page_table, seq_lens, P)
+    assert np.array_equal(slots.cpu().numpy(), oslots)
+    for splits in (0, 1):
+        a = smla.smla_sparse_decode(qt, kv, slots, _t(valid), 1, 1 / 16, num_splits=splits)
+        b = smla.smla_sparse_decode_topk(qt, kv, *args, P, 1 / 16, num_splits=splits)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+        o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, oslots, valid, 1, 1 / 16)
+        atol = FP8_ATOL if kv_dtype == "fp8" else BF16_ATOL
+        _check(b[0], b[1], o_ref, l_ref, atol, BF16_RTOL, f"requests out of order {kv_dtype} splits={splits}")
+
+
 def test_topk_slots_past_int32():
     """Page ids whose slots pass the int32 range (page size 2^20; page id 4096 gives 2^32 + offset,
     which a 32-bit slot would wrap onto a slot inside the pool): smla_resolve_slots masks them
