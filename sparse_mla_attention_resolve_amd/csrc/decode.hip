@@ -454,17 +454,17 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   // ---- prologue. What the first gathers need goes out as early as it can:
   //   - at once (it needs only the kernel's arguments): the split's table entries
   //     table[t][e0 .. e0 + n_ent) (slots when the page size is 1, page ids otherwise) into
-  //     slot_s / page_s, and the scalar loads of the token's length and request (no branch:
-  //     map_req is lens when the table holds slots);
-  //   - once the request is known, for a page-mapped table: its context length (a scalar
-  //     load) and its page-table row, into ring slot 1 when the row fits there.
+  //     slot_s / page_s; for a page-mapped table, the guessed request's page-table row into
+  //     ring slot 1 when the row fits there; then the scalar loads of the token's length and
+  //     request and the guessed request's context length;
+  //   - once the request is known, if the guess was wrong: its context length and row.
   // All of it lands before the slots are built, so that building them touches LDS only (a
   // register that a global load may still be writing would make the compiler wait for
   // every copy in flight, since it does not see them). Decode issues q right behind it and
   // leaves q in flight meanwhile; union mode issues q first.
   const int lp = a.log2_page;
   const int r0 = s * rps;
-  const bool mapped = a.mapped != 0;
+  const bool mapped = !UNION && a.mapped != 0;          // union mode never maps
   constexpr bool umode = UNION;                         // a.union_G > 0
   // union mode: heads per query, queries per workgroup, workgroups per group, this
   // workgroup's group and first member; head hh of the workgroup is head hh % uH of query
@@ -484,9 +484,6 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   auto writes = [&](int hh) { return umode ? tok_of(hh) < a.T : hh < hv; };   // head slot hh has an output
   if (umode && tok_of(0) >= a.T) return;               // a short last group's missing members
   const int trow_id = umode ? grp : tr;                // the table row (union mode: the group's)
-  const int len_raw = a.lens[trow_id];
-  const int req_raw = a.map_req[trow_id];
-  const int len = len_raw < 0 ? 0 : (len_raw > a.max_len ? a.max_len : len_raw);
   const int32_t* trow = a.table + (int64_t)trow_id * a.table_stride;
   const int e0 = r0 >> lp;
   const int n_ent = lp == 0 ? min(rps, a.max_len - r0) : min((r0 + rps - 1) >> lp, a.table_width - 1) - e0 + 1;
@@ -497,6 +494,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   int32_t* const prow_lds = (int32_t*)kvbuf[1];
   const bool row_in_lds = a.map_pt_width <= kChunkBytes / 4;
   int32_t req = -1, seq = 0;
+  int len;                                     // the token's length, clamped to max_len
   // q, in the order the lanes read it back (head quarter hq: piece ks of lane (g, c) = head
   // 16hq + c, dims 32ks + 8g .. +7) into its staging (wave (hq, x) copies pieces 9x .. 9x+8
   // of quarter hq)
@@ -516,27 +514,50 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       const int e = k * 64 + lane;
       dma4(e < n_ent ? (const void*)(trow + e0 + e) : (const void*)kZeroRow, (char*)(ent + k * 64));
     }
+    // the page-table row of request r into ring slot 1
+    auto copy_ptrow = [&](int r) {
+      const int32_t* ptrow = a.map_pt + (int64_t)r * a.map_pt_stride;
+      for (int k = w; k * 64 < a.map_pt_width; k += kS1Waves) {
+        const int e = k * 64 + lane;
+        dma4(e < a.map_pt_width ? (const void*)(ptrow + e) : (const void*)kZeroRow, (char*)(prow_lds + k * 64));
+      }
+    };
+    // In a decode batch every request has one token and token t usually belongs to request
+    // t: that request's page-table row and context length go out at once, with the entries,
+    // instead of one round trip later behind the token's request id. A token of another
+    // request fetches its own once the guessed ones have landed.
+    const bool guess = mapped && trow_id < a.map_R;
+    if (guess && row_in_lds) copy_ptrow(trow_id);
+    // decode: q goes out right behind the entries (it depends on the token alone) and stays
+    // in flight while the slots are built: the waits below cover the copies issued before q
+    if constexpr (!UNION) copy_q();
+    // The token's length and request id are cold loads. They go out only now, behind the
+    // copies (the empty asm keeps the compiler from hoisting them), since a copy whose
+    // address needs a kernel argument would otherwise wait for them too: scalar loads
+    // complete out of order, so any wait for one waits for all. They are scalar loads
+    // through the constant address space (the arrays are read-only here): as vector loads
+    // behind the copies their first use would wait for every copy in flight.
+    using cint = const __attribute__((address_space(4))) int32_t;
+    int row = trow_id;
+    __asm__ volatile("" : "+s"(row));
+    int len_raw = ((cint*)a.lens)[row];
+    int req_raw = mapped ? ((cint*)a.map_req)[row] : -1;
+    int32_t seq_guess = guess ? ((cint*)a.map_seq)[row] : 0;
+    __asm__ volatile("" : "+s"(len_raw), "+s"(req_raw), "+s"(seq_guess));   // all three in flight together
+    len = len_raw < 0 ? 0 : (len_raw > a.max_len ? a.max_len : len_raw);
+    bool reissue = false;
     if (mapped) {
       if (req_raw >= 0 && req_raw < a.map_R) {
-        // a scalar load through the constant address space (the array is read-only here):
-        // as a vector load after the copies above it would make the compiler wait for all of
-        // them before seq is used
         req = req_raw;
-        seq = ((const __attribute__((address_space(4))) int32_t*)a.map_seq)[req];
+        seq = req == trow_id ? seq_guess : ((cint*)a.map_seq)[req];
       }
-      if (row_in_lds) {
-        const int32_t* ptrow = a.map_pt + (int64_t)(req >= 0 ? req : 0) * a.map_pt_stride;
-        for (int k = w; k * 64 < a.map_pt_width; k += kS1Waves) {
-          const int e = k * 64 + lane;
-          dma4(e < a.map_pt_width ? (const void*)(ptrow + e) : (const void*)kZeroRow, (char*)(prow_lds + k * 64));
-        }
-      }
+      reissue = row_in_lds && !(guess && req == trow_id) && req >= 0;
     }
-    if constexpr (!UNION) {
-      // decode: q goes out right behind the entries (it depends on the token alone) and stays
-      // in flight while the slots are built: the wait below covers the entries only, the
-      // copies issued before q
-      copy_q();
+    if (reissue) {
+      wait_vmcnt<0>();                          // the guessed row's copies land first: both write the same LDS
+      copy_ptrow(req);
+      wait_vmcnt<0>();
+    } else if constexpr (!UNION) {
       wait_vmcnt<kQLoads / 2>();
     } else {
       wait_vmcnt<0>();

@@ -295,14 +295,16 @@ def test_topk_fused_masks(splits):
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 def test_topk_requests_out_of_order(kv_dtype):
     """Tokens whose requests are not their own indices (a decode batch usually holds one token
-    per request, in order): permuted and repeated requests through short page-table rows, the
-    fused path against resolve + decode and the oracle."""
+    per request, in order, and stage 1 fetches request t's page-table row for token t before it
+    knows the request): permuted and repeated requests through short page-table rows, tokens 1
+    and 3 in their own index's request, tokens 5 and 6 past the last request index; the fused
+    path against resolve + decode and the oracle."""
     rng = np.random.default_rng(41)
     T, W, R, P, ptw, pages = 7, 512, 5, 16, 40, 300
     num_slots = pages * P
     page_table = np.stack([rng.permutation(pages)[:ptw] for _ in range(R)]).astype(np.int32)
     seq_lens = np.array([600, 640, 333, 500, 17], np.int32)
-    tok_req = np.array([3, 0, 4, 1, 1, 2, 0], np.int32)
+    tok_req = np.array([3, 1, 4, 3, 1, 2, 0], np.int32)
     idx = np.stack([rng.choice(640, size=W, replace=False) for _ in range(T)]).astype(np.int32)
     valid = np.array([512, 400, 512, 512, 100, 512, 512], np.int32)
     q = wl.f32_to_bf16_bits(rng.standard_normal((T, 64, 576)).astype(np.float32) * 0.5)
