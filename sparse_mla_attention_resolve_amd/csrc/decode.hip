@@ -303,7 +303,7 @@ __device__ __forceinline__ void merge_part(const Stage1Args& a, int64_t pbase, i
     uint32_t* o =
         (uint32_t*)((uint16_t*)a.out + (int64_t)tr * a.out_tok_stride + (int64_t)(hbase + hb + v) * a.out_head_stride + col);
 #pragma unroll
-    for (int n = 0; n < NP; ++n) o[128 * n] = pack_bf16x2(acc[n][v][0] * inv, acc[n][v][1] * inv);
+    for (int n = 0; n < NP; ++n) o[128 * n] = cvt_bf16x2(acc[n][v][0] * inv, acc[n][v][1] * inv);
     if (a.lse && (p & 1) == 0 && ntp == 0 && (lanep & 15) == 0)
       a.lse[(int64_t)tr * a.lse_tok_stride + hbase + hb + v] = ws[v] > 0.f ? (mx[v] + log2f(ws[v])) * kLn2 : -INFINITY;
   }
@@ -1060,7 +1060,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       uint16_t* ob = (uint16_t*)a.out + (int64_t)tok_of(hh) * a.out_tok_stride + (int64_t)head_of(hh) * a.out_head_stride +
                      256 * x + c;
 #pragma unroll
-      for (int nt = 0; nt < 16; ++nt) ob[16 * nt] = (uint16_t)f32_to_bf16_rne(oacc[nt][v] * inv[v]);
+      for (int nt = 0; nt < 16; ++nt) ob[16 * nt] = (uint16_t)cvt_bf16x2(oacc[nt][v] * inv[v], 0.f);
     }
     if (a.lse && x == 0 && g == 0 && writes(h0 + c))
       a.lse[(int64_t)tok_of(h0 + c) * a.lse_tok_stride + head_of(h0 + c)] = lse_c;
@@ -1077,8 +1077,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   uint64_t* po = (uint64_t*)((uint16_t*)a.part_o + part * (kHeads * kLatent)) + ((hq * 2 + x) * 16 * 64 + lane);
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) {
-    const uint64_t v = (uint64_t)pack_bf16x2(oacc[nt][0] * inv[0], oacc[nt][1] * inv[1]) |
-                       ((uint64_t)pack_bf16x2(oacc[nt][2] * inv[2], oacc[nt][3] * inv[3]) << 32);
+    const uint64_t v = (uint64_t)cvt_bf16x2(oacc[nt][0] * inv[0], oacc[nt][1] * inv[1]) |
+                       ((uint64_t)cvt_bf16x2(oacc[nt][2] * inv[2], oacc[nt][3] * inv[3]) << 32);
     __hip_atomic_store(po + nt * 64, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // (the LDS ring is idle from here on: its first slot holds the merge's LSE staging)
@@ -1230,8 +1230,8 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2(Stage2Args a) {
   } else {
     uint16_t* o = (uint16_t*)a.out + (int64_t)t * a.out_tok_stride + (int64_t)h * a.out_head_stride + c0;
     uint2 v;
-    v.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-    v.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    v.x = cvt_bf16x2(acc.x * inv, acc.y * inv);
+    v.y = cvt_bf16x2(acc.z * inv, acc.w * inv);
     *(uint2*)o = v;
   }
   if (a.lse && (threadIdx.x & 127) == 0)
@@ -1337,7 +1337,7 @@ __global__ void __launch_bounds__(kS2Threads) decode_stage2_packed(Stage2Args a)
     const int h = kHeads * hbk + hbase + v;
     const float inv = wsum[v] > 0.f ? 1.0f / wsum[v] : 0.f;
     uint16_t* o = (uint16_t*)a.out + (int64_t)tr * a.out_tok_stride + (int64_t)h * a.out_head_stride + col0;
-    *(uint2*)o = make_uint2(pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv), pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv));
+    *(uint2*)o = make_uint2(cvt_bf16x2(acc[v][0] * inv, acc[v][1] * inv), cvt_bf16x2(acc[v][2] * inv, acc[v][3] * inv));
     if (a.lse && nt == 0 && x == 0 && cq == 0)
       a.lse[(int64_t)tr * a.lse_tok_stride + h] = wsum[v] > 0.f ? mx[v] + logf(wsum[v]) : -INFINITY;
   }
