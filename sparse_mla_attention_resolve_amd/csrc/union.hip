@@ -4,9 +4,9 @@
 //
 // Two builders with the same result (the ascending union, each row once with the OR of its
 // members' bits):
-//   - pools of up to kBitmapSlots (2^20) rows (below 2^18 when a group lists more than 8,192
-//     entries), when the map fits LDS: a bit per pool row in LDS, counted per block to place
-//     each row; persistent workgroups build one group after another;
+//   - pools of up to kBitmapSlots (2^20) rows, when the map fits LDS: a bit per pool row in LDS
+//     (a window of 2^18 rows at a time when a group lists more than 8,192 entries), counted per
+//     block to place each row; persistent workgroups build one group after another;
 //   - larger pools, one workgroup per group: every listed (row, member) pair becomes the key
 //     row * 8 + member (padding, negative rows and rows past the pool become 0xffffffff), the
 //     keys are sorted by a bitonic network held in registers, each run of one row is folded
@@ -73,7 +73,8 @@ __device__ __forceinline__ int block_exclusive_sum(int x, int32_t* wave_tot, int
 }
 
 // Pools of at most kBitmapSlots rows: a bit per pool row in LDS, in blocks of 128 rows (four
-// words). The group's listed rows set their bits (an atomic OR each). Each wave counts the set
+// words), one window of the pool at a time (the whole pool; windows of 2^18 rows for lists of
+// more than 8,192 entries, whose map must leave room for their other LDS). The group's listed rows set their bits (an atomic OR each). Each wave counts the set
 // bits of a contiguous range of blocks, 64 blocks at a time (one 16-byte read per lane, so a
 // wave's reads cover every bank once) with a prefix inside the wave, and one block-wide sum of
 // the waves' totals turns the counts into the number of union rows before each block. A row's
@@ -81,7 +82,7 @@ __device__ __forceinline__ int block_exclusive_sum(int x, int32_t* wave_tot, int
 // block (one 16-byte read). Each listed entry ORs its member's bit into its place's byte, the
 // union's rows are written over the bit map in place order, and one coalesced pass writes the
 // entries. Cost per group: the map's size (cleared and counted once) plus a few LDS reads per
-// listed entry; no sort.
+// listed entry; no sort. A window's union rows follow the previous windows' in the output.
 // A workgroup builds groups blockIdx.x, + gridDim.x, ... (as many workgroups as fit the compute
 // units at once): the next group's list entries are loaded while the current one is built.
 constexpr int kBitmapSlots = 1 << 20;
@@ -97,12 +98,13 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
   __shared__ int32_t wave_tot[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = G * W;                                 // list entries of a group
-  const int nblocks = (num_slots + 127) >> 7;          // 128-row blocks
-  const int per_wave = (nblocks + kWaves - 1) / kWaves;   // blocks counted by each wave
-  const int area = max(4 * nblocks, n);
-  uint4* const bm = (uint4*)lds;                       // the bit map (a block per uint4), then the union's rows
+  const int nblocks = (num_slots + 127) >> 7;          // 128-row blocks of the pool
+  constexpr int kWinLog2 = K >= 16 ? 11 : 13;          // blocks per window: 2^18 or 2^20 rows
+  const int wblocks = min(nblocks, 1 << kWinLog2);     // blocks of the largest window
+  const int area = max(4 * wblocks, n);
+  uint4* const bm = (uint4*)lds;                       // the window's bit map (a block per uint4), then its union rows
   uint32_t* const ubits = lds + area;                  // byte r: member bits of union entry r
-  uint16_t* const pre = (uint16_t*)(ubits + ((n + 3) >> 2));   // union rows before each block
+  uint16_t* const pre = (uint16_t*)(ubits + ((n + 3) >> 2));   // the window's union rows before each block
   // entry e = i * P + tid of the members' lists laid end to end: member m = e / W and position
   // j = e - m W, the same for every group (as m << 16 | j, or -1 past the lists)
   const float rw = 1.0f / (float)W;
@@ -153,19 +155,27 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
       key[i] = mj >= 0 && j < lim && raw[i] >= 0 && raw[i] < num_slots ? raw[i] | (m << 24) : -1;
     }
     if (kAhead && g + (int)gridDim.x < groups) load(g + gridDim.x);   // lands while this group is built
-    for (int b = tid; b < nblocks; b += P) bm[b] = make_uint4(0u, 0u, 0u, 0u);
     for (int w = tid; w < ((n + 3) >> 2); w += P) ubits[w] = 0u;
+    int base = 0;                                      // union rows of the windows before
+    // (one window, known at compile time, for lists of up to 8,192 entries)
+    const int nwin = K >= 16 ? (nblocks + (1 << kWinLog2) - 1) >> kWinLog2 : 1;
+    for (int wi = 0; wi < nwin; ++wi) {
+    // window wi: pool rows 128 b0 .., its keys' rows relative to it
+    const int b0 = wi << kWinLog2;
+    const int nbw = min(nblocks - b0, 1 << kWinLog2);
+    const int per_wave = (nbw + kWaves - 1) / kWaves;  // blocks counted by each wave
+    for (int b = tid; b < nbw; b += P) bm[b] = make_uint4(0u, 0u, 0u, 0u);
     lds_barrier();
+    auto in_win = [&](int32_t k) { return K >= 16 ? k >= 0 && ((k & 0xffffff) >> (kWinLog2 + 7)) == wi : k >= 0; };
 #pragma unroll
     for (int i = 0; i < K; ++i)
-      if (key[i] >= 0) atomicOr(&lds[(key[i] & 0xffffff) >> 5], 1u << (key[i] & 31));
+      if (in_win(key[i])) atomicOr(&lds[((key[i] & 0xffffff) - 128 * b0) >> 5], 1u << (key[i] & 31));
     lds_barrier();
     // set bits per block, and their prefix inside the wave's range: round k covers blocks
-    // b_lo + 64k + lane (at most 8 rounds: 2^20 rows are 8,192 blocks over 16 waves; 2 for the
-    // lists of more than 8,192 entries, whose pools stay below 2^18 rows); the rounds' reads all
-    // go out first and their scans are independent
-    constexpr int kRounds = K >= 16 ? 2 : 8;
-    const int b_lo = wv * per_wave, b_hi = min(b_lo + per_wave, nblocks);
+    // b_lo + 64k + lane (at most 8 rounds: a window of 2^20 rows is 8,192 blocks over 16 waves;
+    // 2 for 2^18); the rounds' reads all go out first and their scans are independent
+    constexpr int kRounds = 1 << (kWinLog2 - 10);
+    const int b_lo = wv * per_wave, b_hi = min(b_lo + per_wave, nbw);
     int c[kRounds], incl[kRounds];
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
@@ -196,21 +206,23 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
       if (b < b_hi) pre[b] = (uint16_t)(off + incl[k] - c[k]);
     }
     lds_barrier();
-    // each listed entry's place in the union (its block's count, plus the set bits before it in
-    // the block), and its member's bit there
-    // (with 16 entries per thread the place replaces the member in the key, row | place << 18,
-    // which holds for pools of fewer than 2^18 rows: the row's 18 bits are never all ones, so a
+    // each listed entry's place in the union (the windows before, its block's count, plus the
+    // set bits before it in the block), and its member's bit there
+    // (with 16 entries per thread the place replaces the member in the key, window row | place
+    // << 18, which holds in windows of 2^18 rows: the row's 18 bits are never all ones, so a
     // packed key is never -1; fewer entries keep the places apart)
     constexpr bool kPack = K >= 16;
     int place[kPack ? 1 : K];
+    bool mine[kPack ? K : 1];                          // packed keys: this window's
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       if constexpr (!kPack) place[i] = -1;
-      if (key[i] >= 0) {
-        const int r = key[i] & 0xffffff, b = r >> 7, wi = (r >> 5) & 3;
+      if constexpr (kPack) mine[i] = in_win(key[i]);
+      if (kPack ? mine[i] : in_win(key[i])) {
+        const int r = (key[i] & 0xffffff) - 128 * b0, b = r >> 7, wi = (r >> 5) & 3;
         const uint4 x = bm[b];
         const uint32_t below = (1u << (r & 31)) - 1u;
-        int pl = pre[b];
+        int pl = base + pre[b];
         pl += wi > 0 ? __popc(x.x) : __popc(x.x & below);
         pl += wi > 1 ? __popc(x.y) : (wi == 1 ? __popc(x.y & below) : 0);
         pl += wi > 2 ? __popc(x.z) : (wi == 2 ? __popc(x.z & below) : 0);
@@ -220,21 +232,26 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
         else place[i] = pl;
       }
     }
-    lds_barrier();                                   // the bit map is read: it takes the rows
+    lds_barrier();                                   // the bit map is read: it takes the window's rows
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       if constexpr (kPack) {
-        if (key[i] != -1) lds[(uint32_t)key[i] >> 18] = (uint32_t)key[i] & 0x3ffffu;
+        if (mine[i]) {
+          lds[((uint32_t)key[i] >> 18) - base] = (uint32_t)key[i] & 0x3ffffu;
+          key[i] = -1;                               // placed: no later window takes it
+        }
       } else {
-        if (place[i] >= 0) lds[place[i]] = (uint32_t)(key[i] & 0xffffff);
+        if (place[i] >= 0) lds[place[i] - base] = (uint32_t)((key[i] & 0xffffff) - 128 * b0);
       }
     }
     lds_barrier();
-    uint32_t* out = enc + (int64_t)g * enc_stride;
+    uint32_t* out = enc + (int64_t)g * enc_stride + base;
     for (int r = tid; r < total; r += P)
-      out[r] = lds[r] | (((ubits[r >> 2] >> (8 * (r & 3))) & 0xffu) << SMLA_UNION_ROW_BITS);
-    if (tid == 0) lens[g] = total;
-    lds_barrier();                                   // before the next group clears the map
+      out[r] = (lds[r] + 128 * b0) | (((ubits[(base + r) >> 2] >> (8 * ((base + r) & 3))) & 0xffu) << SMLA_UNION_ROW_BITS);
+    base += total;
+    lds_barrier();                                   // before the next window or group clears the map
+    }
+    if (tid == 0) lens[g] = base;
   }
 }
 
@@ -396,14 +413,14 @@ hipError_t launch_union(const int32_t* slots, int64_t slots_stride, const int32_
   if (Q == 0) return hipSuccess;
   const int groups = (Q + G - 1) / G;
   const int n = G * W, nblocks = (int)((std::min<int64_t>(num_slots, kBitmapSlots) + 127) >> 7);
-  const size_t lds = (size_t)(std::max(4 * nblocks, n) + ((n + 3) >> 2)) * 4 + (size_t)nblocks * 2;
-  // the bit map, the member bytes and the block counts must fit one compute unit's LDS beside
-  // the kernel's own (a 2^20-row pool with 16,384 list entries per group does not: the sort);
-  // lists of more than 8,192 entries (16 per thread) take pools below 2^18 rows, which their
-  // packed keys and two counting rounds assume; a group's list entries must sit within 2^31
-  // entries of its first (32-bit offsets)
-  if (num_slots <= (n > 8192 ? (1 << 18) - 1 : kBitmapSlots) && lds + 1024 <= 160u * 1024u &&
-      (int64_t)G * slots_stride < ((int64_t)1 << 31)) {
+  // lists of more than 8,192 entries (16 per thread) map windows of 2^18 rows, which their
+  // packed keys and two counting rounds assume; the others the whole pool
+  const int wblocks = std::min(nblocks, n > 8192 ? 1 << 11 : 1 << 13);
+  const size_t lds = (size_t)(std::max(4 * wblocks, n) + ((n + 3) >> 2)) * 4 + (size_t)wblocks * 2;
+  // the window's bit map, the member bytes and the block counts must fit one compute unit's
+  // LDS beside the kernel's own; a group's list entries must sit within 2^31 entries of its
+  // first (32-bit offsets)
+  if (num_slots <= kBitmapSlots && lds + 1024 <= 160u * 1024u && (int64_t)G * slots_stride < ((int64_t)1 << 31)) {
     // as many workgroups as fit the compute units at once (registers and LDS decide)
 #define SMLA_UNION_BITMAP(K)                                                                                        \
   do {                                                                                                              \

@@ -128,7 +128,7 @@ def test_union_strided_lists(G, ns):
 @pytest.mark.parametrize("ns", [5000, 262143, 262144, 1 << 20, (1 << 20) + 1, 3000000])
 def test_union_random(G, Q, ns):
     # pools of up to 2^20 rows take the bit-map kernel (with 16,384 entries per group, G = 8 here,
-    # only below 2^18 rows), larger ones the sorting kernel
+    # in windows of 2^18 rows), larger ones the sorting kernel
     W = 1024 if G == 4 else 2048
     slots, valid = wl.random_slot_lists(1000 + G * 10 + Q, Q, W, ns, overlap=0.6, G=G, pad_frac=0.3)
     rng = np.random.default_rng(Q)
@@ -145,6 +145,27 @@ def test_union_random(G, Q, ns):
     enc_g2, lens_g2 = _union_gpu(slots, None, G, ns)
     enc_o2, lens_o2 = oracle.group_union(slots, np.full(Q, W), G, ns)
     _compare_union(enc_g2, lens_g2, enc_o2, lens_o2)
+
+
+@pytest.mark.parametrize("ns", [262145, 600000, 1 << 20])
+def test_union_windows(ns):
+    """Groups of 8 lists of 2,048 entries map the pool in windows of 2^18 rows: rows on both
+    sides of every window edge, the pool's first and last rows and a short last window, each
+    listed by some members only, against the oracle."""
+    rng = np.random.default_rng(ns % 1009)
+    Q, W, G = 16, 2048, 8
+    edges = [r for k in range(1, 4) for r in ((k << 18) - 1, k << 18) if r < ns] + [0, ns - 1]
+    slots = np.stack([rng.choice(ns, size=W, replace=False) for _ in range(Q)]).astype(np.int32)
+    for q in range(Q):
+        pick = [e for i, e in enumerate(edges) if (q + i) % 3 != 0]          # some members only
+        row = slots[q][~np.isin(slots[q], edges)][: W - len(pick)]
+        slots[q] = np.concatenate([np.array(pick, np.int32), row])
+        rng.shuffle(slots[q])
+    valid = np.full(Q, W, np.int32)
+    valid[5] = 1000
+    enc_g, lens_g = _union_gpu(slots, valid, G, ns)
+    enc_o, lens_o = oracle.group_union(slots, valid, G, ns)
+    _compare_union(enc_g, lens_g, enc_o, lens_o)
 
 
 def test_union_24bit_rows():
