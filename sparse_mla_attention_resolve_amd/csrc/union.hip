@@ -74,15 +74,16 @@ __device__ __forceinline__ int block_exclusive_sum(int x, int32_t* wave_tot, int
 
 // Pools of at most kBitmapSlots rows: a bit per pool row in LDS, in blocks of 128 rows (four
 // words), one window of the pool at a time (the whole pool; windows of 2^18 rows for lists of
-// more than 8,192 entries, whose map must leave room for their other LDS). The group's listed rows set their bits (an atomic OR each). Each wave counts the set
-// bits of a contiguous range of blocks, 64 blocks at a time (one 16-byte read per lane, so a
-// wave's reads cover every bank once) with a prefix inside the wave, and one block-wide sum of
-// the waves' totals turns the counts into the number of union rows before each block. A row's
-// place in the ascending union is then its block's count plus the set bits before it in the
-// block (one 16-byte read). Each listed entry ORs its member's bit into its place's byte, the
-// union's rows are written over the bit map in place order, and one coalesced pass writes the
-// entries. Cost per group: the map's size (cleared and counted once) plus a few LDS reads per
-// listed entry; no sort. A window's union rows follow the previous windows' in the output.
+// more than 8,192 entries, whose map must leave room for their other LDS). The group's listed
+// rows set their bits (an atomic OR each). Each wave counts the set bits of a contiguous range
+// of blocks, 64 blocks at a time (one 16-byte read per lane, so a wave's reads cover every bank
+// once) with a prefix inside the wave, and one block-wide sum of the waves' totals turns the
+// counts into the number of union rows before each block. A row's place in the ascending union
+// is then its block's count plus the set bits before it in the block (one 16-byte read). Each
+// listed entry ORs its member's bit into its place's byte, the union's rows are written over
+// the bit map in place order, and one coalesced pass writes the entries; a window's union rows
+// follow the previous windows'. Cost per group: the map's size (cleared and counted once per
+// window) plus a few LDS reads per listed entry; no sort.
 // A workgroup builds groups blockIdx.x, + gridDim.x, ... (as many workgroups as fit the compute
 // units at once): the next group's list entries are loaded while the current one is built.
 constexpr int kBitmapSlots = 1 << 20;
@@ -160,96 +161,98 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(
     // (one window, known at compile time, for lists of up to 8,192 entries)
     const int nwin = K >= 16 ? (nblocks + (1 << kWinLog2) - 1) >> kWinLog2 : 1;
     for (int wi = 0; wi < nwin; ++wi) {
-    // window wi: pool rows 128 b0 .., its keys' rows relative to it
-    const int b0 = wi << kWinLog2;
-    const int nbw = min(nblocks - b0, 1 << kWinLog2);
-    const int per_wave = (nbw + kWaves - 1) / kWaves;  // blocks counted by each wave
-    for (int b = tid; b < nbw; b += P) bm[b] = make_uint4(0u, 0u, 0u, 0u);
-    lds_barrier();
-    auto in_win = [&](int32_t k) { return K >= 16 ? k >= 0 && ((k & 0xffffff) >> (kWinLog2 + 7)) == wi : k >= 0; };
+      // window wi: pool rows 128 b0 .., its keys' rows relative to it
+      const int b0 = wi << kWinLog2;
+      const int nbw = min(nblocks - b0, 1 << kWinLog2);
+      const int per_wave = (nbw + kWaves - 1) / kWaves;  // blocks counted by each wave
+      for (int b = tid; b < nbw; b += P) bm[b] = make_uint4(0u, 0u, 0u, 0u);
+      lds_barrier();
+      // a key of this window (every valid key with a single window)
+      auto in_win = [&](int32_t k) { return K >= 16 ? k >= 0 && ((k & 0xffffff) >> (kWinLog2 + 7)) == wi : k >= 0; };
 #pragma unroll
-    for (int i = 0; i < K; ++i)
-      if (in_win(key[i])) atomicOr(&lds[((key[i] & 0xffffff) - 128 * b0) >> 5], 1u << (key[i] & 31));
-    lds_barrier();
-    // set bits per block, and their prefix inside the wave's range: round k covers blocks
-    // b_lo + 64k + lane (at most 8 rounds: a window of 2^20 rows is 8,192 blocks over 16 waves;
-    // 2 for 2^18); the rounds' reads all go out first and their scans are independent
-    constexpr int kRounds = 1 << (kWinLog2 - 10);
-    const int b_lo = wv * per_wave, b_hi = min(b_lo + per_wave, nbw);
-    int c[kRounds], incl[kRounds];
+      for (int i = 0; i < K; ++i)
+        if (in_win(key[i])) atomicOr(&lds[((key[i] & 0xffffff) - 128 * b0) >> 5], 1u << (key[i] & 31));
+      lds_barrier();
+      // set bits per block, and their prefix inside the wave's range: round k covers blocks
+      // b_lo + 64k + lane (at most 8 rounds: a window of 2^20 rows is 8,192 blocks over 16 waves;
+      // 2 for 2^18); the rounds' reads all go out first and their scans are independent
+      constexpr int kRounds = 1 << (kWinLog2 - 10);
+      const int b_lo = wv * per_wave, b_hi = min(b_lo + per_wave, nbw);
+      int c[kRounds], incl[kRounds];
 #pragma unroll
-    for (int k = 0; k < kRounds; ++k) {
-      const int b = b_lo + 64 * k + lane;
-      c[k] = 0;
-      if (b < b_hi) {
-        const uint4 x = bm[b];
-        c[k] = __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
-      }
-    }
-    int run = 0;
-#pragma unroll
-    for (int k = 0; k < kRounds; ++k) {
-      incl[k] = wave_inclusive_sum(c[k]) + run;
-      run = __builtin_amdgcn_readlane(incl[k], 63);
-    }
-    if (lane == 0) wave_tot[wv] = run;
-    lds_barrier();
-    int off = 0, total = 0;
-#pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
-      off += k < wv ? wave_tot[k] : 0;
-      total += wave_tot[k];
-    }
-#pragma unroll
-    for (int k = 0; k < kRounds; ++k) {
-      const int b = b_lo + 64 * k + lane;
-      if (b < b_hi) pre[b] = (uint16_t)(off + incl[k] - c[k]);
-    }
-    lds_barrier();
-    // each listed entry's place in the union (the windows before, its block's count, plus the
-    // set bits before it in the block), and its member's bit there
-    // (with 16 entries per thread the place replaces the member in the key, window row | place
-    // << 18, which holds in windows of 2^18 rows: the row's 18 bits are never all ones, so a
-    // packed key is never -1; fewer entries keep the places apart)
-    constexpr bool kPack = K >= 16;
-    int place[kPack ? 1 : K];
-    bool mine[kPack ? K : 1];                          // packed keys: this window's
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-      if constexpr (!kPack) place[i] = -1;
-      if constexpr (kPack) mine[i] = in_win(key[i]);
-      if (kPack ? mine[i] : in_win(key[i])) {
-        const int r = (key[i] & 0xffffff) - 128 * b0, b = r >> 7, wi = (r >> 5) & 3;
-        const uint4 x = bm[b];
-        const uint32_t below = (1u << (r & 31)) - 1u;
-        int pl = base + pre[b];
-        pl += wi > 0 ? __popc(x.x) : __popc(x.x & below);
-        pl += wi > 1 ? __popc(x.y) : (wi == 1 ? __popc(x.y & below) : 0);
-        pl += wi > 2 ? __popc(x.z) : (wi == 2 ? __popc(x.z & below) : 0);
-        pl += wi == 3 ? __popc(x.w & below) : 0;
-        atomicOr(&ubits[pl >> 2], (1u << (key[i] >> 24)) << (8 * (pl & 3)));
-        if constexpr (kPack) key[i] = r | (pl << 18);
-        else place[i] = pl;
-      }
-    }
-    lds_barrier();                                   // the bit map is read: it takes the window's rows
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-      if constexpr (kPack) {
-        if (mine[i]) {
-          lds[((uint32_t)key[i] >> 18) - base] = (uint32_t)key[i] & 0x3ffffu;
-          key[i] = -1;                               // placed: no later window takes it
+      for (int k = 0; k < kRounds; ++k) {
+        const int b = b_lo + 64 * k + lane;
+        c[k] = 0;
+        if (b < b_hi) {
+          const uint4 x = bm[b];
+          c[k] = __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
         }
-      } else {
-        if (place[i] >= 0) lds[place[i] - base] = (uint32_t)((key[i] & 0xffffff) - 128 * b0);
       }
-    }
-    lds_barrier();
-    uint32_t* out = enc + (int64_t)g * enc_stride + base;
-    for (int r = tid; r < total; r += P)
-      out[r] = (lds[r] + 128 * b0) | (((ubits[(base + r) >> 2] >> (8 * ((base + r) & 3))) & 0xffu) << SMLA_UNION_ROW_BITS);
-    base += total;
-    lds_barrier();                                   // before the next window or group clears the map
+      int run = 0;
+#pragma unroll
+      for (int k = 0; k < kRounds; ++k) {
+        incl[k] = wave_inclusive_sum(c[k]) + run;
+        run = __builtin_amdgcn_readlane(incl[k], 63);
+      }
+      if (lane == 0) wave_tot[wv] = run;
+      lds_barrier();
+      int off = 0, total = 0;
+#pragma unroll
+      for (int k = 0; k < kWaves; ++k) {
+        off += k < wv ? wave_tot[k] : 0;
+        total += wave_tot[k];
+      }
+#pragma unroll
+      for (int k = 0; k < kRounds; ++k) {
+        const int b = b_lo + 64 * k + lane;
+        if (b < b_hi) pre[b] = (uint16_t)(off + incl[k] - c[k]);
+      }
+      lds_barrier();
+      // each listed entry's place in the union (the windows before, its block's count, plus the
+      // set bits before it in the block), and its member's bit there
+      // (with 16 entries per thread the place replaces the member in the key, window row | place
+      // << 18, which holds in windows of 2^18 rows: the row's 18 bits are never all ones, so a
+      // packed key is never -1; fewer entries keep the places apart)
+      constexpr bool kPack = K >= 16;
+      int place[kPack ? 1 : K];
+      bool mine[kPack ? K : 1];                          // packed keys: this window's
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        if constexpr (!kPack) place[i] = -1;
+        if constexpr (kPack) mine[i] = in_win(key[i]);
+        if (kPack ? mine[i] : in_win(key[i])) {
+          const int r = (key[i] & 0xffffff) - 128 * b0, b = r >> 7, wq = (r >> 5) & 3;
+          const uint4 x = bm[b];
+          const uint32_t below = (1u << (r & 31)) - 1u;
+          int pl = base + pre[b];
+          pl += wq > 0 ? __popc(x.x) : __popc(x.x & below);
+          pl += wq > 1 ? __popc(x.y) : (wq == 1 ? __popc(x.y & below) : 0);
+          pl += wq > 2 ? __popc(x.z) : (wq == 2 ? __popc(x.z & below) : 0);
+          pl += wq == 3 ? __popc(x.w & below) : 0;
+          atomicOr(&ubits[pl >> 2], (1u << (key[i] >> 24)) << (8 * (pl & 3)));
+          if constexpr (kPack) key[i] = r | (pl << 18);
+          else place[i] = pl;
+        }
+      }
+      lds_barrier();                                   // the bit map is read: it takes the window's rows
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        if constexpr (kPack) {
+          if (mine[i]) {
+            lds[((uint32_t)key[i] >> 18) - base] = (uint32_t)key[i] & 0x3ffffu;
+            key[i] = -1;                               // placed: no later window takes it
+          }
+        } else {
+          if (place[i] >= 0) lds[place[i] - base] = (uint32_t)((key[i] & 0xffffff) - 128 * b0);
+        }
+      }
+      lds_barrier();
+      uint32_t* out = enc + (int64_t)g * enc_stride + base;
+      for (int r = tid; r < total; r += P)
+        out[r] = (lds[r] + 128 * b0) |
+                 (((ubits[(base + r) >> 2] >> (8 * ((base + r) & 3))) & 0xffu) << SMLA_UNION_ROW_BITS);
+      base += total;
+      lds_barrier();                                   // before the next window or group clears the map
     }
     if (tid == 0) lens[g] = base;
   }
