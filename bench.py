@@ -1118,7 +1118,7 @@ def sources_sha256(files) -> str:
 
 _KV_NAMES = {"1": "bf16", "2": "fp8"}
 _KERNEL_RULES = [
-    (re.compile(r"decode_stage1_mfma<(\d+), (true|false)(?:, (?:true|false))?>"),
+    (re.compile(r"decode_stage1_mfma<(\d+), (true|false)(?:, (?:true|false))*>"),
      lambda m: f"decode_stage1_mfma<{_KV_NAMES.get(m.group(1), m.group(1))}{', union' if m.group(2) == 'true' else ''}>"),
     (re.compile(r"decode_stage1_f32\b"), lambda m: "decode_stage1_f32"),
     (re.compile(r"decode_stage2_packed\b"), lambda m: "decode_stage2_packed"),

@@ -200,15 +200,11 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   plan->cus = device_cus();
   // A dense paged decode (page size > 1: contexts of any length) of at most 64 tokens lets the
   // workgroups size the splits from the actual lengths (no host copy of them), so that short
-  // and long contexts share the compute units evenly. The grid bounds the splits any lengths
-  // can produce: at most one workgroup per compute unit while the rows per split stay under
-  // the cap, else ceil(max_len / kMaxSplitRows) per token, plus one per token.
+  // and long contexts share the compute units evenly: at most one split per compute unit,
+  // a long split walking its rows in segments of kMaxSplitRows. The grid is one workgroup per
+  // compute unit.
   plan->balanced = bf16 && a->page_size > 1 && a->num_splits == 0 && tv <= 64 && tv < plan->cus;
-  int64_t items = tv * plan->S;
-  if (plan->balanced) {
-    const int64_t capped = tv * ((max_len + smla::kMaxSplitRows - 1) / smla::kMaxSplitRows) + tv;
-    items = capped > plan->cus ? capped : plan->cus;
-  }
+  const int64_t items = plan->balanced ? (int64_t)plan->cus : tv * plan->S;
   plan->grid = (int32_t)items;
   // the bf16 path keeps its partial outputs in bf16, the fp32 path in fp32
   plan->part_o_bytes = (size_t)items * hslots * SMLA_LATENT * (bf16 ? 2 : 4);
@@ -217,11 +213,8 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   // the head of the workspace; a workgroup waits for its block's other splits (at most
   // 10 us) only when the whole grid is resident at once
   plan->sync_bytes = bf16 ? smla::kSyncBytes : 0;
-  // A balanced plan whose grid may exceed the device merges in stage 2 instead: its splits
-  // cannot all run at once, and the last arrival of a token with tens of splits would merge
-  // them all by itself.
-  plan->fused = bf16 && tv <= smla::kSyncTokens && !(plan->balanced && items > plan->cus);
-  plan->wait_ticks = tv * plan->S <= plan->cus || (plan->balanced && items <= plan->cus) ? wall_ticks(10) : 0;
+  plan->fused = bf16 && tv <= smla::kSyncTokens;
+  plan->wait_ticks = tv * plan->S <= plan->cus || plan->balanced ? wall_ticks(10) : 0;
   plan->ws_bytes = plan->sync_bytes + (plan->part_o_bytes + plan->part_lse_bytes + 255) / 256 * 256;
   return SMLA_OK;
 }

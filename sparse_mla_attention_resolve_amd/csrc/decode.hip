@@ -70,13 +70,30 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 
 // The balanced plan of a dense paged decode of tv <= 64 virtual tokens (64-head blocks; virtual
 // token v is block v / T of token v % T), computed by one wave from the lengths alone, lane v for
-// token v: rows per split r from the launch's total rows, so that every token's splits fit the
-// compute units at once (at least min_rows, at most kMaxSplitRows, whole chunks); token v gets
-// n = max(1, ceil(len_v / r)) splits, numbered consecutively in token order from base. Stage 1
-// and stage 2 compute the same plan. Returns the total number of splits (wave-uniform).
+// token v: token v gets n_v = max(1, ceil(len_v / r)) splits of at most r rows, numbered
+// consecutively in token order from base. r (whole chunks, at least min_rows) is
+// ceil(total / (cus - tv)), at which the splits always fit the compute units (sum n_v <=
+// total / r + tv); when that is more than one segment of kMaxSplitRows rows, r is instead the
+// fewest rows whose splits fit: a binary search down to ceil(total / cus), since the count only
+// falls as r grows. (Below a segment, more splits than that would add more merge work than
+// balance; above it, the rounding of ceil(len_v / r) can leave a quarter of the units idle.)
+// A split longer than kMaxSplitRows rows is walked in segments of that many. Stage 1 and
+// stage 2 compute the same plan. Returns the total number of splits (wave-uniform).
 struct BalancedPlan {
   int r, base, n, total;
 };
+// the sum over the wave's 64 lanes (all active), in every lane: DPP moves, no LDS
+__device__ __forceinline__ int wave_sum_i(int x) { return __builtin_amdgcn_readlane(wave_inclusive_sum(x), 63); }
+// ceil(a / b) for a >= 0, b >= 8 and a + b <= 2^25: the fp32 reciprocal estimate (relative
+// error ~2^-22) puts the truncated quotient within one of the true one, which one step each way
+// corrects
+__device__ __forceinline__ int ceil_div_small(int a, int b) {
+  const int num = a + b - 1;
+  int q = (int)((float)num * __builtin_amdgcn_rcpf((float)b));
+  q -= q * b > num ? 1 : 0;
+  q += (q + 1) * b <= num ? 1 : 0;
+  return q;
+}
 __device__ __forceinline__ BalancedPlan balanced_plan(const int32_t* lens, int T, int hblocks, int max_len, int cus,
                                                       int min_rows, int v) {
   const int tv = T * hblocks;
@@ -85,21 +102,20 @@ __device__ __forceinline__ BalancedPlan balanced_plan(const int32_t* lens, int T
     const int l = lens[v % T];
     ln = l < 0 ? 0 : (l > max_len ? max_len : l);
   }
-  int tot = ln;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
-  const int room = cus - tv;                               // splits beyond one per token
-  int r = (tot + room - 1) / room;
-  r = (r + kChunk - 1) / kChunk * kChunk;
-  r = r < min_rows ? min_rows : (r > kMaxSplitRows ? kMaxSplitRows : r);
-  const int n = v < tv ? max(1, (ln + r - 1) / r) : 0;
-  int incl = n;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (v >= o) incl += y;
+  const int tot = wave_sum_i(ln);
+  auto splits_of = [&](int r) { return v < tv ? max(1, ceil_div_small(ln, r)) : 0; };
+  const int cmin = (min_rows + kChunk - 1) / kChunk;       // in chunks
+  int hi = max(cmin, ceil_div_small(tot, (cus - tv) * kChunk));
+  int lo = hi * kChunk <= kMaxSplitRows ? hi : max(cmin, ceil_div_small(tot, cus * kChunk));
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (wave_sum_i(splits_of(mid * kChunk)) <= cus) hi = mid;
+    else lo = mid + 1;
   }
-  return BalancedPlan{r, incl - n, n, __shfl(incl, 63, 64)};
+  const int r = hi * kChunk;
+  const int n = splits_of(r);
+  const int incl = wave_inclusive_sum(n);
+  return BalancedPlan{r, incl - n, n, __builtin_amdgcn_readlane(incl, 63)};
 }
 
 // Workgroup id -> (token, split). Workgroups are dispatched to the 8 XCDs round robin;
@@ -378,7 +394,9 @@ __device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int64_t
 // fetch in the same row order. The loop is software pipelined: while it accumulates P V for
 // chunk ci it computes the scores and weights of chunk ci + 1.
 
-template <int KV, bool UNION, bool BYIDX>
+// SEGS (decode): a split may be longer than one segment of kMaxSplitRows rows, which only the
+// balanced plan makes; the other decode launches keep the segment loop out of the code.
+template <int KV, bool UNION, bool BYIDX, bool SEGS>
 __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a) {
   using L = Lay<KV>;
   constexpr int kRowBytes = L::kUnits * 16;
@@ -406,13 +424,13 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   // smax the cap on a token's splits
   int t, s, rps = a.rows_per_split, smax = a.S, wait_ticks = a.wait_ticks;
   int64_t pbase;
-  if (!UNION && a.balanced) {
+  if constexpr (!UNION && SEGS) {                         // launched for a balanced plan (a.balanced)
     // Splits planned from the lengths (a dense paged decode of at most 64 tokens, whose
     // contexts may differ widely): rows per split from the launch's total rows, so that every
-    // token's splits fit the compute units at once (at least min_rows, at most kMaxSplitRows,
-    // whole chunks); token v gets ceil(len_v / rows) splits, at least one (which writes an
-    // empty token's output); workgroup b takes the b-th split in token order, or leaves past
-    // the last. Wave 0 plans, lane v for token v.
+    // token's splits fit the compute units at once (at least min_rows, whole chunks, in
+    // segments of kMaxSplitRows rows); token v gets ceil(len_v / rows) splits, at least one
+    // (which writes an empty token's output); workgroup b takes the b-th split in token order,
+    // or leaves past the last. Wave 0 plans, lane v for token v.
     __shared__ int bplan[5];
     if (threadIdx.x < 64) {
       const int v = threadIdx.x, b = blockIdx.x;
@@ -486,7 +504,10 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int trow_id = umode ? grp : tr;                // the table row (union mode: the group's)
   const int32_t* trow = a.table + (int64_t)trow_id * a.table_stride;
   const int e0 = r0 >> lp;
-  const int n_ent = lp == 0 ? min(rps, a.max_len - r0) : min((r0 + rps - 1) >> lp, a.table_width - 1) - e0 + 1;
+  // the first segment's entries (only a balanced plan makes splits of more than one segment:
+  // their later page ids are copied segment by segment)
+  const int rps1 = min(rps, kMaxSplitRows);
+  const int n_ent = lp == 0 ? min(rps1, a.max_len - r0) : min((r0 + rps1 - 1) >> lp, a.table_width - 1) - e0 + 1;
   // q's staging: bf16, ring slots 2 ..; fp8, the two staging tiles
   static_assert(kFp8 ? 2 * kStgBytes >= 4 * kQLoads * 1024 : (kNBuf - 2) * kChunkBytes >= 4 * kQLoads * 1024,
                 "q must fit its staging");
@@ -819,24 +840,34 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     pa = pa_next;
   };
 
-  // The rows come in segments whose slots are built in LDS: decode walks one (the split's
-  // rows); the union mode walks its group's union in pieces of kMaxSplitRows entries, each
-  // compacted to the entries whose bit names its query. O and the running max and sum carry
-  // over from one segment to the next.
-  const int nseg = umode ? (len + kMaxSplitRows - 1) / kMaxSplitRows : 1;
+  // The rows come in segments of at most kMaxSplitRows whose slots are built in LDS: decode
+  // walks its split's rows (one segment, except a long split of a balanced plan); the union
+  // mode walks its group's union, each piece compacted to the entries whose bit names its
+  // query. O and the running max and sum carry over from one segment to the next.
+  const int nseg = umode ? (len + kMaxSplitRows - 1) / kMaxSplitRows : SEGS ? (r1 - r0 + kMaxSplitRows - 1) / kMaxSplitRows : 1;
   for (int seg = 0; seg < nseg; ++seg) {
-    const int sb = r0 + seg * kMaxSplitRows;       // first entry of the segment
+    const int sb = r0 + seg * kMaxSplitRows;       // first entry (row) of the segment
     if (seg > 0) {
       lds_barrier();                               // every wave is done with the slots and the ring
-      const int n_seg = min(kMaxSplitRows, a.max_len - sb);
-      for (int k = w; k * 64 < n_seg; k += kS1Waves) {
-        const int e = k * 64 + lane;
-        dma4(e < n_seg ? (const void*)(trow + sb + e) : (const void*)kZeroRow, (char*)(slot_s + k * 64));
+      if (umode || lp == 0) {
+        const int n_seg = min(kMaxSplitRows, a.max_len - sb);
+        for (int k = w; k * 64 < n_seg; k += kS1Waves) {
+          const int e = k * 64 + lane;
+          dma4(e < n_seg ? (const void*)(trow + sb + e) : (const void*)kZeroRow, (char*)(slot_s + k * 64));
+        }
+      } else {
+        // the page ids of the segment's rows
+        const int e0s = sb >> lp;
+        const int n_pg = min((min(sb + kMaxSplitRows, r1) - 1) >> lp, a.table_width - 1) - e0s + 1;
+        for (int k = w; k * 64 < n_pg; k += kS1Waves) {
+          const int e = k * 64 + lane;
+          dma4(e < n_pg ? (const void*)(trow + e0s + e) : (const void*)kZeroRow, (char*)(page_s + k * 64));
+        }
       }
       wait_vmcnt<0>();
       lds_barrier();
     }
-    const int nraw = umode ? min(kMaxSplitRows, len - sb) : r1 - r0;
+    const int nraw = min(kMaxSplitRows, (umode ? len : r1) - sb);
     const int nch_raw = (nraw + kChunk - 1) / kChunk;
     int nrows = nraw;
 
@@ -922,8 +953,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
           if (lp == 0) {
             sl = slot_s[i];
           } else {
-            const int p = r0 + i;
-            const int32_t pg = page_s[(p >> lp) - e0];
+            const int p = sb + i;
+            const int32_t pg = page_s[(p >> lp) - (sb >> lp)];
             sl = pg < 0 ? -1 : ((int64_t)pg << lp) + (p & ((1 << lp) - 1));
           }
           if (sl >= a.kv.num_slots) sl = -1;
@@ -950,12 +981,12 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
 
     if constexpr (kFp8) {
       // the ring's chunks go out; once chunk 0 (and q and the scales, issued before it) has
-      // landed, decode moves q to registers, and chunk 0 is converted into staging tile 0,
-      // whose ring slot then takes chunk kNBuf
+      // landed, decode moves q to registers (in its first segment), and chunk 0 is converted
+      // into staging tile 0, whose ring slot then takes chunk kNBuf
       for (int ci = 0; ci < kNBuf && ci < nchunks; ++ci) issue(ci);
       wait_chunks_w<kNBuf - 1, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 1, nchunks - 1));
       lds_barrier();
-      if constexpr (!UNION) {
+      if (!UNION && seg == 0) {
 #pragma unroll
         for (int ks = 0; ks < kQLoads; ++ks) qf[ks] = as_bf16x8(*(const uint4*)(qlds + ks * 1024 + lane * 16));
         lds_barrier();
@@ -965,8 +996,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       lds_barrier();
       if (kNBuf < nchunks) issue(kNBuf);
     } else {
-      if constexpr (!UNION) {
-        // decode (one segment): chunks 0 and 1 go out; once q (issued in the prologue) has
+      if (!UNION && seg == 0) {
+        // decode, first segment: chunks 0 and 1 go out; once q (issued in the prologue) has
         // landed every wave moves its quarter to registers, and the slots it held take the
         // next chunks
         for (int ci = 0; ci < 2 && ci < nchunks; ++ci) issue(ci);
@@ -1358,10 +1389,18 @@ bool gathers_by_index(const smla_kv& kv) {
 
 template <int KV, bool UNION>
 void launch_stage1(dim3 grid, hipStream_t stream, const Stage1Args& a) {
-  if (gathers_by_index(a.kv))
-    hipLaunchKernelGGL((decode_stage1_mfma<KV, UNION, true>), grid, dim3(kS1Threads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_stage1_mfma<KV, UNION, false>), grid, dim3(kS1Threads), 0, stream, a);
+  const bool byidx = gathers_by_index(a.kv);
+  if (UNION || !a.balanced) {
+    if (byidx)
+      hipLaunchKernelGGL((decode_stage1_mfma<KV, UNION, true, false>), grid, dim3(kS1Threads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_stage1_mfma<KV, UNION, false, false>), grid, dim3(kS1Threads), 0, stream, a);
+  } else if constexpr (!UNION) {
+    if (byidx)
+      hipLaunchKernelGGL((decode_stage1_mfma<KV, false, true, true>), grid, dim3(kS1Threads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_stage1_mfma<KV, false, false, true>), grid, dim3(kS1Threads), 0, stream, a);
+  }
 }
 }  // namespace
 

@@ -114,4 +114,21 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
   return sign | (code > 0x7eu ? 0x7eu : code);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no LDS): shifts by 1,
+// 2, 4 and 8 lanes inside each row of 16, then the last lane of row 0 added to rows 1 and 3,
+// and the last lane of row 1 (by then the sum of rows 0 and 1) added to rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x = dpp_add<0x111, 0xf>(x);                          // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);                          // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);                          // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);                          // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);                          // row_bcast:15 into rows 1, 3
+  x = dpp_add<0x143, 0xc>(x);                          // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 }  // namespace smla

@@ -514,3 +514,19 @@ def test_dense_paged_planned_one_long_context():
     out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(pt), _t(ctx), 64, 1 / 16)
     o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, pt, ctx, 64, 1 / 16)
     _check(out, lse, o_ref, l_ref, BF16_ATOL, BF16_RTOL, "dense planned 64K")
+
+
+def test_dense_paged_planned_long_splits():
+    """Eight contexts of 40K-64K (and one of 100): the balanced plan keeps one workgroup per
+    compute unit, so each split holds more rows than one 1,024-row segment and walks them
+    segment by segment (page ids copied per segment), with O, max and sum carried across;
+    sampled tokens against the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(29)
+    ctx = [int(x) for x in rng.integers(40000, 65537, 8)] + [100]
+    assert sum(ctx) > 1024 * cus                      # rows per split above one segment
+    q, pt, ctx, kv, pool = _dense_case(29, ctx, 64)
+    out, lse = smla.smla_sparse_decode(gc.q_tensor(q, "bf16"), kv, _t(pt), _t(ctx), 64, 1 / 16)
+    sample = [0, 5, 8]
+    o_ref, l_ref = oracle.sparse_decode(q[sample], "bf16", pool, pt[sample], ctx[sample], 64, 1 / 16)
+    _check(out[sample], lse[sample], o_ref, l_ref, BF16_ATOL, BF16_RTOL, "dense planned long splits")
