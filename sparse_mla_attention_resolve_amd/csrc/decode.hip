@@ -411,9 +411,11 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   // fp8: each chunk's rows converted to bf16 rows (the layout of a bf16 chunk), two chunks
   constexpr int kStgBytes = kChunk * Lay<SMLA_BF16>::kUnits * 16;
   __shared__ __attribute__((aligned(16))) char stg[kFp8 ? 2 : 1][kFp8 ? kStgBytes : 16];
-  __shared__ __attribute__((aligned(16))) int32_t slot_s[kMaxSplitRows];
+  // SEGS: two blocks of kMaxSplitRows slots, the next block built while the current one runs
+  constexpr int kSlotRows = SEGS ? 2 * kMaxSplitRows : kMaxSplitRows;
+  __shared__ __attribute__((aligned(16))) int32_t slot_s[kSlotRows];
   __shared__ int32_t page_s[kMaxSplitRows / 2 + 64];     // page ids of a split (page size >= 2)
-  __shared__ __attribute__((aligned(16))) float scale_s[kFp8 ? kMaxSplitRows : 4];
+  __shared__ __attribute__((aligned(16))) float scale_s[kFp8 ? kSlotRows : 4];
   __shared__ uint2 px[kS1Waves][64];                       // weights (bf16) swapped between partners
   __shared__ float mx[kS1Waves][16];                       // the reference each wave's weights are relative to
   __shared__ int fx[kS1Waves];                             // 1: that reference is the running max
@@ -641,9 +643,12 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   struct Copies {
     int32_t slot[kLoadsHi];                     // -1: masked row, copied from the zero row
   };
+  // chunk ci's slots: chunk ci of the segment; SEGS, the chunk's block is ci / 32 and sits in
+  // half (ci / 32) % 2 of slot_s
+  auto cidx = [](int ci) { return SEGS ? ci & (2 * kMaxSplitRows / kChunk - 1) : ci; };
   auto src_of = [&](int ci) {
     Copies cp;
-    const int32_t* srow = slot_s + ci * kChunk;
+    const int32_t* srow = slot_s + cidx(ci) * kChunk;
 #pragma unroll
     for (int k = 0; k < kLoadsHi; ++k) cp.slot[k] = (k < kLoadsLo || hi) ? srow[lpos[k] & 0xff] : -1;
     return cp;
@@ -753,8 +758,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   bf16x8 pa, pa_next;
   auto pub = [&](int ci, int k) {
     if (k == 0) {
-      lv = *(const int4*)(slot_s + ci * kChunk + 16 * x + 4 * g);
-      if constexpr (kFp8) sco = *(const float4*)(scale_s + ci * kChunk + 16 * x + 4 * g);
+      lv = *(const int4*)(slot_s + cidx(ci) * kChunk + 16 * x + 4 * g);
+      if constexpr (kFp8) sco = *(const float4*)(scale_s + cidx(ci) * kChunk + 16 * x + 4 * g);
     } else if (k == 1) {
       const float raw[4] = {kFp8 ? sl[0] * sco.x + sr[0] : sl[0], kFp8 ? sl[1] * sco.y + sr[1] : sl[1],
                             kFp8 ? sl[2] * sco.z + sr[2] : sl[2], kFp8 ? sl[3] * sco.w + sr[3] : sl[3]};
@@ -840,34 +845,62 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     pa = pa_next;
   };
 
-  // The rows come in segments of at most kMaxSplitRows whose slots are built in LDS: decode
-  // walks its split's rows (one segment, except a long split of a balanced plan); the union
-  // mode walks its group's union, each piece compacted to the entries whose bit names its
-  // query. O and the running max and sum carry over from one segment to the next.
-  const int nseg = umode ? (len + kMaxSplitRows - 1) / kMaxSplitRows : SEGS ? (r1 - r0 + kMaxSplitRows - 1) / kMaxSplitRows : 1;
+  // The rows come in segments whose slots are built in LDS. Decode walks one, its split's rows;
+  // a split of the segmented form (SEGS, longer than kMaxSplitRows rows) builds its slots a
+  // block of kMaxSplitRows rows at a time, the next block while the current one is gathered
+  // (page ids and fp8 scales copied ahead), so its ring runs on without a break. The union mode
+  // walks its group's union in pieces of kMaxSplitRows entries, each compacted to the entries
+  // whose bit names its query; O and the running max and sum carry over from one piece to the
+  // next.
+  const int nseg = umode ? (len + kMaxSplitRows - 1) / kMaxSplitRows : 1;
+  // SEGS: the page ids of block bk (rows r0 + kMaxSplitRows bk ..) into page_s; its slots into
+  // half bk % 2 of slot_s (-1 past the split); its fp8 row scales into the same half of scale_s
+  const int nblk = (r1 - r0 + kMaxSplitRows - 1) / kMaxSplitRows;
+  auto copy_pages = [&](int bk) {
+    const int sbn = r0 + bk * kMaxSplitRows;
+    const int e0s = sbn >> lp;
+    const int n_pg = min((min(sbn + kMaxSplitRows, r1) - 1) >> lp, a.table_width - 1) - e0s + 1;
+    for (int k = w; k * 64 < n_pg; k += kS1Waves) {
+      const int e = k * 64 + lane;
+      dma4(e < n_pg ? (const void*)(trow + e0s + e) : (const void*)kZeroRow, (char*)(page_s + k * 64));
+    }
+  };
+  auto build_block = [&](int bk) {
+    const int sbn = r0 + bk * kMaxSplitRows;
+    int32_t* const dst = slot_s + (bk & 1) * kMaxSplitRows;
+    for (int i = tid; i < kMaxSplitRows; i += kS1Threads) {
+      const int p = sbn + i;
+      int64_t sl = -1;
+      if (p < r1) {
+        const int32_t pg = page_s[(p >> lp) - (sbn >> lp)];
+        sl = pg < 0 ? -1 : ((int64_t)pg << lp) + (p & ((1 << lp) - 1));
+        if (sl >= a.kv.num_slots) sl = -1;
+      }
+      dst[i] = sl < 0 ? -1 : (int32_t)sl;
+    }
+  };
+  auto copy_scales = [&](int bk, int rows) {
+    const int h = (bk & 1) * kMaxSplitRows;
+    for (int k = w; k * 64 < rows; k += kS1Waves) {
+      const int32_t e = slot_s[h + k * 64 + lane];
+      const int32_t sl = umode && e >= 0 ? e & ((1 << SMLA_UNION_ROW_BITS) - 1) : e;
+      dma4(sl >= 0 && k * 64 + lane < rows ? (const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride : (const char*)kZeroRow,
+           (char*)(scale_s + h + k * 64));
+    }
+  };
   for (int seg = 0; seg < nseg; ++seg) {
     const int sb = r0 + seg * kMaxSplitRows;       // first entry (row) of the segment
     if (seg > 0) {
       lds_barrier();                               // every wave is done with the slots and the ring
-      if (umode || lp == 0) {
-        const int n_seg = min(kMaxSplitRows, a.max_len - sb);
-        for (int k = w; k * 64 < n_seg; k += kS1Waves) {
-          const int e = k * 64 + lane;
-          dma4(e < n_seg ? (const void*)(trow + sb + e) : (const void*)kZeroRow, (char*)(slot_s + k * 64));
-        }
-      } else {
-        // the page ids of the segment's rows
-        const int e0s = sb >> lp;
-        const int n_pg = min((min(sb + kMaxSplitRows, r1) - 1) >> lp, a.table_width - 1) - e0s + 1;
-        for (int k = w; k * 64 < n_pg; k += kS1Waves) {
-          const int e = k * 64 + lane;
-          dma4(e < n_pg ? (const void*)(trow + e0s + e) : (const void*)kZeroRow, (char*)(page_s + k * 64));
-        }
+      const int n_seg = min(kMaxSplitRows, a.max_len - sb);
+      for (int k = w; k * 64 < n_seg; k += kS1Waves) {
+        const int e = k * 64 + lane;
+        dma4(e < n_seg ? (const void*)(trow + sb + e) : (const void*)kZeroRow, (char*)(slot_s + k * 64));
       }
       wait_vmcnt<0>();
       lds_barrier();
     }
-    const int nraw = min(kMaxSplitRows, (umode ? len : r1) - sb);
+    const int nraw = umode ? min(kMaxSplitRows, len - sb) : r1 - r0;
     const int nch_raw = (nraw + kChunk - 1) / kChunk;
     int nrows = nraw;
 
@@ -946,6 +979,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
         if (ok[k] && page >= 0) sl = ((int64_t)page << mlp) + (pos[k] & ((1 << mlp) - 1));
         slot_s[i] = (sl < 0 || sl >= a.kv.num_slots) ? -1 : (int32_t)sl;
       }
+    } else if (SEGS) {
+      build_block(0);                              // (a balanced plan: page size > 1)
     } else {
       for (int i = tid; i < nch_raw * kChunk; i += kS1Threads) {
         int64_t sl = -1;
@@ -953,8 +988,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
           if (lp == 0) {
             sl = slot_s[i];
           } else {
-            const int p = sb + i;
-            const int32_t pg = page_s[(p >> lp) - (sb >> lp)];
+            const int p = r0 + i;
+            const int32_t pg = page_s[(p >> lp) - e0];
             sl = pg < 0 ? -1 : ((int64_t)pg << lp) + (p & ((1 << lp) - 1));
           }
           if (sl >= a.kv.num_slots) sl = -1;
@@ -963,6 +998,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       }
     }
     lds_barrier();
+    if (SEGS && nblk > 1) copy_pages(1);           // page_s is read: block 1's page ids go out
     const int nchunks = (nrows + kChunk - 1) / kChunk;
     if constexpr (kFp8) {
       // the segment's row scales, copied once before its first rows: one 4-byte copy per row
@@ -970,13 +1006,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       // loop held each chunk's row gathers up behind it (the fp8 loop took 2.3 instead of 1.3 us
       // per chunk), so the scales go out here, ahead of q and the first chunks, and land before
       // them.
-      for (int k = w; k * 64 < nchunks * kChunk; k += kS1Waves) {
-        const int32_t e = slot_s[k * 64 + lane];
-        const int32_t sl = umode && e >= 0 ? e & ((1 << SMLA_UNION_ROW_BITS) - 1) : e;
-        dma4(sl >= 0 && k * 64 + lane < nchunks * kChunk ? (const char*)a.kv.scale + (int64_t)sl * a.kv.scale_stride
-                                                          : (const char*)kZeroRow,
-             (char*)(scale_s + k * 64));
-      }
+      copy_scales(0, min(nchunks * kChunk, kMaxSplitRows));
     }
 
     if constexpr (kFp8) {
@@ -1049,6 +1079,19 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
       } else {
         wait_chunks_w<kNBuf - 3, kLoadsHi, kLoadsLo>(hi, min(kNBuf - 3, nchunks - 2 - ci));
         lds_barrier();
+      }
+      if constexpr (SEGS) {
+        // the next block, four chunks into this one: its slots from its page ids (copied a block
+        // ago, so older than the copies just waited for); one iteration later, once every
+        // thread has built them (barriers between), the block after's page ids and, fp8, the
+        // next block's row scales. The next block's gathers start ~30 chunks on, at the end of
+        // this block; its half of slot_s last served the block before, finished by then.
+        const int bk = ci >> 5;
+        if ((ci & 31) == 4 && bk + 1 < nblk) build_block(bk + 1);
+        if ((ci & 31) == 5 && bk + 1 < nblk) {
+          if (bk + 2 < nblk) copy_pages(bk + 2);
+          if constexpr (kFp8) copy_scales(bk + 1, kMaxSplitRows);
+        }
       }
       // a copy instruction can wait for room in the compute unit's memory queue: one at a
       // time among the MFMAs, the matrix unit keeps busy meanwhile
