@@ -77,8 +77,9 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 // fewest rows whose splits fit: a binary search down to ceil(total / cus), since the count only
 // falls as r grows. (Below a segment, more splits than that would add more merge work than
 // balance; above it, the rounding of ceil(len_v / r) can leave a quarter of the units idle.)
-// A split longer than kMaxSplitRows rows is walked in segments of that many. Stage 1 and
-// stage 2 compute the same plan. Returns the total number of splits (wave-uniform).
+// A split longer than kMaxSplitRows rows builds its slots a block of that many at a time
+// (SEGS). Stage 1 and stage 2 compute the same plan. Returns the total number of splits
+// (wave-uniform).
 struct BalancedPlan {
   int r, base, n, total;
 };
@@ -394,8 +395,9 @@ __device__ __forceinline__ void merge_splits(const Stage1Args& a, int t, int64_t
 // fetch in the same row order. The loop is software pipelined: while it accumulates P V for
 // chunk ci it computes the scores and weights of chunk ci + 1.
 
-// SEGS (decode): a split may be longer than one segment of kMaxSplitRows rows, which only the
-// balanced plan makes; the other decode launches keep the segment loop out of the code.
+// SEGS (decode): a split may be longer than one block of kMaxSplitRows rows, which only the
+// balanced plan makes; the other decode launches keep the plan and the block pipeline out of
+// their code.
 template <int KV, bool UNION, bool BYIDX, bool SEGS>
 __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a) {
   using L = Lay<KV>;
@@ -430,7 +432,7 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
     // Splits planned from the lengths (a dense paged decode of at most 64 tokens, whose
     // contexts may differ widely): rows per split from the launch's total rows, so that every
     // token's splits fit the compute units at once (at least min_rows, whole chunks, in
-    // segments of kMaxSplitRows rows); token v gets ceil(len_v / rows) splits, at least one
+    // blocks of kMaxSplitRows rows); token v gets ceil(len_v / rows) splits, at least one
     // (which writes an empty token's output); workgroup b takes the b-th split in token order,
     // or leaves past the last. Wave 0 plans, lane v for token v.
     __shared__ int bplan[5];
@@ -506,8 +508,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   const int trow_id = umode ? grp : tr;                // the table row (union mode: the group's)
   const int32_t* trow = a.table + (int64_t)trow_id * a.table_stride;
   const int e0 = r0 >> lp;
-  // the first segment's entries (only a balanced plan makes splits of more than one segment:
-  // their later page ids are copied segment by segment)
+  // the first block's entries (only a balanced plan makes splits of more than one block of
+  // kMaxSplitRows rows: their later page ids are copied block by block)
   const int rps1 = min(rps, kMaxSplitRows);
   const int n_ent = lp == 0 ? min(rps1, a.max_len - r0) : min((r0 + rps1 - 1) >> lp, a.table_width - 1) - e0 + 1;
   // q's staging: bf16, ring slots 2 ..; fp8, the two staging tiles
@@ -643,8 +645,8 @@ __global__ void __launch_bounds__(kS1Threads, 1) decode_stage1_mfma(Stage1Args a
   struct Copies {
     int32_t slot[kLoadsHi];                     // -1: masked row, copied from the zero row
   };
-  // chunk ci's slots: chunk ci of the segment; SEGS, the chunk's block is ci / 32 and sits in
-  // half (ci / 32) % 2 of slot_s
+  // chunk ci's slots: chunk ci of the segment; SEGS, the chunk's block is ci / 32, whose slots
+  // sit in half (ci / 32) % 2 of slot_s
   auto cidx = [](int ci) { return SEGS ? ci & (2 * kMaxSplitRows / kChunk - 1) : ci; };
   auto src_of = [&](int ci) {
     Copies cp;
