@@ -2,6 +2,8 @@
 // Changed Everything, "The Message" (the write into the pool that precedes decode
 // attention, and the fp8 cache the Triton path refused) and "Why This Message Was
 // Written" (the fp8_e4m3 cache dtype).
+#include <type_traits>
+
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -54,7 +56,20 @@ __global__ void __launch_bounds__(64) kv_write_kernel(
   } else {
     float amax = 0.0f;
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(lat[i]));
-    for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    // the row's maximum: a max-scan over the wave with DPP lane moves (row shifts by 1, 2, 4, 8,
+    // then rows 0 and 2 into 1 and 3, then row 1 into 2 and 3), lane 63's value in every lane
+    // (lanes shifted in from outside a row contribute +0, and every amax is >= +0)
+    auto dmax = [](float x, auto ctrl, auto rows) {
+      return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                                  decltype(rows)::value, 0xf, false)));
+    };
+    amax = dmax(amax, std::integral_constant<int, 0x111>(), std::integral_constant<int, 0xf>());
+    amax = dmax(amax, std::integral_constant<int, 0x112>(), std::integral_constant<int, 0xf>());
+    amax = dmax(amax, std::integral_constant<int, 0x114>(), std::integral_constant<int, 0xf>());
+    amax = dmax(amax, std::integral_constant<int, 0x118>(), std::integral_constant<int, 0xf>());
+    amax = dmax(amax, std::integral_constant<int, 0x142>(), std::integral_constant<int, 0xa>());
+    amax = dmax(amax, std::integral_constant<int, 0x143>(), std::integral_constant<int, 0xc>());
+    amax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(amax), 63));
     const float scale = amax / 448.0f;              // IEEE division, rounded to nearest
     uint32_t lo = 0, hi = 0;
     if (scale != 0.0f) {
