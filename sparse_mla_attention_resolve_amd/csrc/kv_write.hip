@@ -55,7 +55,11 @@ __global__ void __launch_bounds__(64) kv_write_kernel(
     d[kLatent + lane] = (uint16_t)f32_to_bf16_rne(rope);
   } else {
     float amax = 0.0f;
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(lat[i]));
+    bool nan_in = false;
+    for (int i = 0; i < 8; ++i) {
+      amax = fmaxf(amax, fabsf(lat[i]));
+      nan_in |= lat[i] != lat[i];
+    }
     // the row's maximum: a max-scan over the wave with DPP lane moves (row shifts by 1, 2, 4, 8,
     // then rows 0 and 2 into 1 and 3, then row 1 into 2 and 3), lane 63's value in every lane
     // (lanes shifted in from outside a row contribute +0, and every amax is >= +0)
@@ -70,6 +74,9 @@ __global__ void __launch_bounds__(64) kv_write_kernel(
     amax = dmax(amax, std::integral_constant<int, 0x142>(), std::integral_constant<int, 0xa>());
     amax = dmax(amax, std::integral_constant<int, 0x143>(), std::integral_constant<int, 0xc>());
     amax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(amax), 63));
+    // fmaxf passes over a NaN; the maximum of a row that holds one is NaN, so its scale is
+    // NaN and every latent code of the row is the NaN code
+    if (__builtin_amdgcn_ballot_w64(nan_in) != 0) amax = __builtin_nanf("");
     const float scale = amax / 448.0f;              // IEEE division, rounded to nearest
     uint32_t lo = 0, hi = 0;
     if (scale != 0.0f) {

@@ -111,3 +111,39 @@ def test_kv_write_fp8_rounding_edges():
     s = kv.storage.cpu().numpy()[smap]
     assert np.all(want["scale"] == np.float32(1.0))
     assert np.array_equal(s[:, :512], want["lat8"])
+
+
+def test_kv_write_fp8_nonfinite_rows():
+    """Rows holding a NaN or an infinity. The maximum over a latent row that holds a NaN is
+    NaN, so its scale is NaN and all 512 codes are the NaN code; a NaN in the rotary part
+    leaves the scale alone. A latent infinity gives an infinite scale: finite values encode
+    to signed zeros and the infinity itself to the NaN code (inf / inf). Codes equal the
+    oracle's bit for bit; scales equal it bit for bit where finite, and are NaN together."""
+    rng = np.random.default_rng(7)
+    src = rng.standard_normal((8, 576)).astype(np.float32)
+    src[0, 0] = np.nan
+    src[1, 511] = np.nan
+    src[2, 300] = -np.nan
+    src[3, 520] = np.nan          # rotary column only
+    src[4, 17] = np.inf
+    src[5, 400] = -np.inf
+    src[6, :512] = 0.0            # all-zero latent: scale 0, codes 0
+    smap = np.arange(8, dtype=np.int32) * 3 + 2
+    ns = 8 * 3 + 2
+    kv = smla.KvCache.empty(smla.SMLA_FP8_E4M3, ns)
+    smla.smla_kv_write(torch.from_numpy(src).cuda(), torch.from_numpy(smap).cuda(), kv)
+    pool = oracle.Pool(ns, "fp8")
+    oracle.kv_write(pool, src, "f32", smap)
+    want = pool.stored(smap)
+    got_codes = kv.lat8()[torch.from_numpy(smap).long()].cpu().numpy()
+    got_scale = kv.scale()[torch.from_numpy(smap).long()].cpu().numpy()
+    assert np.array_equal(got_codes, want["lat8"])
+    assert np.array_equal(np.isnan(got_scale), np.isnan(want["scale"]))
+    fin = ~np.isnan(want["scale"])
+    assert np.array_equal(got_scale[fin].view(np.uint32), want["scale"][fin].view(np.uint32))
+    assert np.isnan(want["scale"][:3]).all() and (want["lat8"][:3] == 0x7F).all()
+    assert np.isfinite(want["scale"][3]) and np.isinf(want["scale"][4:6]).all()
+    got_rope = kv.rope16()[torch.from_numpy(smap).long()].cpu().numpy().view(np.uint16)
+    rnan = np.isnan(src[:, 512:])
+    assert np.array_equal(got_rope[~rnan], want["rope16"][~rnan])
+    assert ((got_rope[rnan] & 0x7FFF) > 0x7F80).all()
