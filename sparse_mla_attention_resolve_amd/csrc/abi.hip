@@ -114,9 +114,11 @@ int32_t wall_ticks(int32_t us) {
 // token, at least enough for the per-split row limit.
 // Splits per token when the caller leaves it open: one workgroup per compute unit (CUs / T),
 // but no split shorter than min_rows, and none longer than kMaxSplitRows. The floor comes from
-// a sweep of split counts for batches 1 .. 128 at top-k 2048: below 128 rows (bf16 cache) or
-// 64 rows (fp8 cache) a split's fixed cost (first gathers, partial store, merge) outweighs
-// the compute units it adds; at batch 1 the floor takes the step from 28.6 to 23.2 us (bf16).
+// a sweep of split counts for batches 1 .. 128 at top-k 2048: below 128 rows a split's fixed
+// cost (first gathers, partial store, merge) outweighs the compute units it adds; at batch 1
+// the floor takes the step from 28.6 to 23.2 us (bf16). An fp8 cache's 64-row splits still pay
+// while the grid they make is small (batch 1 and 2: 0.2-0.5 us), not beyond (batch 8: 25.4-26
+// against 23.4-23.6 us at 128 rows), so check_decode lowers its floor to 64 rows only there.
 void plan_splits(int32_t T, int32_t max_len, int32_t requested, int32_t min_rows, int32_t* S_out, int32_t* R_out) {
   const int32_t chunk = smla::kChunk;
   const int32_t max_chunks = (max_len + chunk - 1) / chunk;
@@ -194,7 +196,8 @@ smla_status check_decode(const smla_decode_args* a, smla::DecodePlan* plan, bool
   const int64_t tv = (int64_t)a->T * plan->hblocks;
   CHECK(tv <= (1 << 24), SMLA_ERR_RANGE, "%s: T * ceil(H / 64) must be <= 2^24", fn);
   const int64_t hslots = bf16 ? 64 : a->H;
-  const int32_t min_rows = !bf16 ? smla::kChunk : a->kv.dtype == SMLA_FP8_E4M3 ? 64 : 128;
+  int32_t min_rows = !bf16 ? smla::kChunk : 128;
+  if (bf16 && a->kv.dtype == SMLA_FP8_E4M3 && tv * ((max_len + 63) / 64) <= device_cus() / 4) min_rows = 64;
   plan_splits((int32_t)tv, (int32_t)max_len, a->num_splits, min_rows, &plan->S, &plan->rows_per_split);
   plan->min_rows = min_rows;
   plan->cus = device_cus();

@@ -141,6 +141,12 @@ def test_decode_split_plan_follows_shapes():
     assert splits(T=1, table_width=256, table_stride=256) <= 8
     assert splits(num_splits=5) == 5
     assert splits(num_splits=200, table_width=64, table_stride=64) == 2      # at most one split per 32 rows
+    # fp8 cache, top-k 2048, 256 compute units: 64-row splits while the grid stays within 64
+    # workgroups (batch 1 and 2), 128-row splits beyond (batch 4 and 8), then CUs / T
+    fp8 = dict(kv_dtype=S.SMLA_FP8_E4M3, kv_rows=None, kv_row_stride=0, kv_lat8=FAKE, kv_lat8_stride=656,
+               kv_rope16=FAKE + 512, kv_rope16_stride=656, kv_scale=FAKE + 640, kv_scale_stride=656)
+    assert [splits(T=t, **fp8) for t in (1, 2, 4, 8, 16, 64)] == [32, 32, 16, 16, 16, 4]
+    assert [splits(T=t) for t in (1, 2, 4, 8, 16, 64)] == [16, 16, 16, 16, 16, 4]
 
 
 def test_union_checks():
