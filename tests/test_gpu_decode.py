@@ -78,6 +78,21 @@ def test_decode_small_sparse(kv_dtype, splits):
     assert torch.all(out[torch.from_numpy(empty)] == 0)
 
 
+@pytest.mark.parametrize("T,want_splits", [(1, 32), (2, 32), (4, 16)])
+def test_decode_fp8_small_batch_plan(T, want_splits):
+    """An fp8 cache at top-k 2048 under the automatic plan: 64-row splits at batch 1 and 2,
+    128-row splits at batch 4 (the plan's floor), each against the oracle. Lengths cover a
+    full list, a ragged tail and a list shorter than one split."""
+    lens = [2048, 1000, 50, 2047][:T]
+    q, table, lens, live, vals = _random_case(40 + T, T, 2048, lens, 30000, kv_dtype="fp8")
+    kv, pool = _pools(live, vals, 30000, "fp8")
+    qt = gc.q_tensor(q, "bf16")
+    assert smla.smla_sparse_decode_splits(qt, kv, _t(table), _t(lens), 1, 1 / 16) == want_splits
+    out, lse = smla.smla_sparse_decode(qt, kv, _t(table), _t(lens), 1, 1 / 16)
+    o_ref, l_ref = oracle.sparse_decode(q, "bf16", pool, table, lens, 1, 1 / 16)
+    _check(out, lse, o_ref, l_ref, FP8_ATOL, BF16_RTOL, f"fp8 T={T} auto splits")
+
+
 @pytest.mark.parametrize("P", [16, 64])
 def test_decode_small_dense_paged(P):
     lens = [1, 63, 64, 65, 1000, 4000]
